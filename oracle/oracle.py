@@ -1,0 +1,123 @@
+"""Python face of the fp64 CPU oracle (``oracle_attn.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product path never imports this
+module, and this module never imports the product package.
+
+``attn_fwd`` computes exact softmax attention forward in float64 from the
+definition (see the header of ``oracle_attn.c`` for the formula and the
+passages of the pages it follows).  Every function's parity status is
+"pinned": ``tests/test_oracle_pins.py`` ties it to brute force, closed forms
+and invariants that do not go through this code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle_attn.c")
+LIB = os.path.join(HERE, "liboracle_attn.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C, -O2, pthreads)."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build(force=True)
+        lib = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        lib.oracle_attn_fwd.restype = ctypes.c_int
+        lib.oracle_attn_fwd.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_double, P, P,
+                                        ctypes.c_int, ctypes.c_int, P, ctypes.c_int64, P, P, P,
+                                        ctypes.c_int]
+        lib.oracle_default_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    return int(_load().oracle_default_threads())
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def attn_fwd(q, k, v, cu_seqlens, causal: bool, scale: float, row_ptr=None, col_idx=None,
+             block: int = 128, rows=None, nthreads: int = 0, with_psum: bool = False):
+    """Exact attention forward.
+
+    q:  float64 [T, Hq, D] (all tokens) or [len(rows), Hq, D] when ``rows`` is given
+    k, v: float64 [T, Hkv, D];  cu_seqlens: int [n+1]
+    row_ptr/col_idx: optional block list (single sequence only), ``block`` rows per block
+    rows: optional packed token ids to compute
+    Returns (O [n_q, Hq, D], LSE [n_q, Hq]) or (O, LSE, sum_j P) with ``with_psum``.
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    n_seqs = len(cu) - 1
+    t = int(cu[-1])
+    hq, d = q.shape[1], q.shape[2]
+    hkv = k.shape[1]
+    if k.shape != (t, hkv, d) or v.shape != (t, hkv, d):
+        raise ValueError(f"k/v shape {k.shape}/{v.shape} != {(t, hkv, d)}")
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n_q = t if rows_a is None else len(rows_a)
+    if q.shape[0] != n_q:
+        raise ValueError(f"q has {q.shape[0]} rows, expected {n_q}")
+    rp = None if row_ptr is None else np.ascontiguousarray(row_ptr, dtype=np.int32)
+    ci = None if col_idx is None else np.ascontiguousarray(col_idx, dtype=np.int32)
+    if rp is not None and ci is not None and len(ci) == 0:
+        ci = np.zeros(1, dtype=np.int32)  # keep a valid pointer for an empty list
+    out = np.zeros((n_q, hq, d), dtype=np.float64)
+    lse = np.zeros((n_q, hq), dtype=np.float64)
+    psum = np.zeros((n_q, hq), dtype=np.float64) if with_psum else None
+    rc = _load().oracle_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu), n_seqs, hq, hkv, d, int(bool(causal)),
+        float(scale), _ptr(rp), _ptr(ci), 0 if rp is None else len(rp) - 1, int(block),
+        _ptr(rows_a), 0 if rows_a is None else len(rows_a), _ptr(out), _ptr(lse), _ptr(psum),
+        int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_fwd failed with code {rc}")
+    if with_psum:
+        return out, lse, psum
+    return out, lse
+
+
+def run_workload(w, rows=None, nthreads: int = 0, with_psum: bool = False):
+    """Oracle on an ``attn_workloads.Workload`` (bf16 inputs widened exactly to float64).
+
+    Returns outputs in packed order: O [n_q, Hq, D], LSE [n_q, Hq] where n_q is
+    every token or ``len(rows)`` (token ids in packed order).
+    """
+    from attn_workloads import bf16_bits_to_f32  # input module only (no attention arithmetic)
+
+    q, k, v = w.packed_views()
+    kf = bf16_bits_to_f32(k).astype(np.float64)
+    vf = bf16_bits_to_f32(v).astype(np.float64)
+    if rows is None:
+        qf = bf16_bits_to_f32(q).astype(np.float64)
+    else:
+        qf = bf16_bits_to_f32(q[np.asarray(rows, dtype=np.int64)]).astype(np.float64)
+    return attn_fwd(qf, kf, vf, w.cu_seqlens_or_fixed(), w.causal, w.scale, w.row_ptr, w.col_idx,
+                    128, rows, nthreads, with_psum)
