@@ -1,0 +1,157 @@
+"""Fused softmax-attention forward for AMD Instinct MI355X (gfx950).
+
+The work happens in ``libattn_fwd.so`` (hand-written HIP, C ABI declared in
+``include/attn_fwd.h``).  This module only marshals torch tensors into the C
+descriptors: every step of the computation runs in the library's kernels.
+There is no fallback: if the library is missing, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn_fwd.so")
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = -1
+ATTN_ERR_UNSUPPORTED = -2
+ATTN_ERR_LAUNCH = -3
+
+
+class AttnTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("stride_batch", ctypes.c_int64), ("stride_seq", ctypes.c_int64),
+                ("stride_head", ctypes.c_int64)]
+
+
+class AttnBlockList(ctypes.Structure):
+    _fields_ = [("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
+                ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("num_q_blocks", ctypes.c_int32)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"attn_fwd failed: {msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m attention_forward_flashattention_amd.build`")
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        T = ctypes.POINTER(AttnTensor)
+        BL = ctypes.POINTER(AttnBlockList)
+        lib.attn_fwd.restype = ctypes.c_int
+        lib.attn_fwd.argtypes = [T, T, T, P, ctypes.c_int, ctypes.c_float, BL, T, P, P]
+        lib.attn_fwd_validate.restype = ctypes.c_int
+        lib.attn_fwd_validate.argtypes = [T, T, T, P, ctypes.c_int, ctypes.c_float, BL, T]
+        lib.attn_status_str.restype = ctypes.c_char_p
+        lib.attn_status_str.argtypes = [ctypes.c_int]
+        lib.attn_version.restype = ctypes.c_int
+        lib.attn_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return load_library().attn_status_str(int(status)).decode()
+
+
+def describe(t, batch: int, seqlen: int, packed: bool) -> AttnTensor:
+    """C descriptor of a [B, S, H, D] (or packed [T, H, D]) tensor; strides in elements."""
+    if packed:
+        _, h, d = t.shape
+        sb, ss, sh, sd = 0, t.stride(0), t.stride(1), t.stride(2)
+    else:
+        _, _, h, d = t.shape
+        sb, ss, sh, sd = t.stride(0), t.stride(1), t.stride(2), t.stride(3)
+    if sd != 1 and d > 1:
+        raise ValueError("head_dim must be contiguous")
+    return AttnTensor(t.data_ptr(), batch, seqlen, h, d, sb, ss, sh)
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def attn_fwd(q, k, v, cu_seqlens=None, causal: bool = False, scale: Optional[float] = None,
+             block_list: Optional[Tuple] = None, out=None, lse=None, max_seqlen: Optional[int] = None,
+             return_lse: bool = True, stream=None):
+    """O = softmax(scale * Q K^T + mask) V and the natural-log LSE per row.
+
+    q: bf16 [B, S, Hq, D] (or packed [T, Hq, D] with ``cu_seqlens`` int32 [B+1])
+    k, v: bf16 [B, S, Hkv, D] (or packed [T, Hkv, D])
+    block_list: optional (row_ptr, col_idx) int32 device tensors, 128x128 blocks
+    out: optional bf16 output like q;  lse: optional fp32 [B, Hq, S] (packed [Hq, T])
+    max_seqlen: packed form only, an upper bound on every sequence length
+    Returns (out, lse) (lse None when ``return_lse`` is false and none is given).
+    """
+    import torch
+
+    lib = load_library()
+    packed = cu_seqlens is not None
+    if packed:
+        if q.dim() != 3:
+            raise ValueError("packed q must be [T, H, D]")
+        batch = int(cu_seqlens.numel()) - 1
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with cu_seqlens")
+        seqlen = int(max_seqlen)
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+            raise ValueError("cu_seqlens must be an int32 device tensor")
+    else:
+        if q.dim() != 4:
+            raise ValueError("q must be [B, S, H, D]")
+        batch, seqlen = int(q.shape[0]), int(q.shape[1])
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError(f"{name} must be a bfloat16 device tensor")
+    d = int(q.shape[-1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    hq = int(q.shape[-2])
+    if lse is None and return_lse:
+        if packed:
+            lse = torch.empty((hq, int(q.shape[0])), dtype=torch.float32, device=q.device)
+        else:
+            lse = torch.empty((batch, hq, seqlen), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor")
+    dq = describe(q, batch, seqlen, packed)
+    dk = describe(k, batch, seqlen, packed)
+    dv = describe(v, batch, seqlen, packed)
+    do = describe(out, batch, seqlen, packed)
+    bl = None
+    if block_list is not None:
+        row_ptr, col_idx = block_list
+        for t in (row_ptr, col_idx):
+            if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("block list tensors must be contiguous int32 device tensors")
+        bl = AttnBlockList(row_ptr.data_ptr(), col_idx.data_ptr() if col_idx.numel() else row_ptr.data_ptr(),
+                           128, 128, int(row_ptr.numel()) - 1)
+    st = lib.attn_fwd(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                      ctypes.c_void_p(cu_seqlens.data_ptr()) if packed else None,
+                      int(bool(causal)), float(scale), ctypes.byref(bl) if bl is not None else None,
+                      ctypes.byref(do), ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
+                      ctypes.c_void_p(_stream_handle(stream)))
+    if st != ATTN_OK:
+        raise AttnError(st, status_str(st))
+    return out, lse

@@ -1,0 +1,481 @@
+// attn_fwd.hip — fused softmax-attention forward for AMD Instinct MI355X (gfx950).
+//
+// One workgroup computes a tile of BM = 128 query rows of one (sequence, query
+// head).  Four wave64s each own 32 of those rows and keep them in registers for
+// the whole kernel.  KV tiles of BN = 64 keys are streamed through LDS; for
+// each tile a wave computes the transposed score tile S^T = K Q^T with
+// 32x32x16 bf16 MFMAs, so that every lane holds the scores of ONE query row
+// (the softmax row statistics then need one exchange between the two lane
+// halves instead of a 32-lane reduction), runs the online softmax in base 2
+// with scale*log2(e) folded into one FMA, and accumulates O^T = V^T P^T with
+// the same MFMA, P staying in registers.  V^T operands come straight from the
+// row-major V tile with the gfx950 LDS transpose read (ds_read_b64_tr_b16).
+//
+// The computation is the softmax attention that FlashAttention-style kernels
+// evaluate tile by tile in on-chip memory (AdaSplash-2 explainer, technical
+// summary section 1); block skipping follows the ordered per-query-block KV
+// list of the CoSA explainer (lay summary): unlisted blocks are never loaded.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_fwd.h"
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) short short4_t;
+typedef __attribute__((ext_vector_type(16))) float floatx16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int uint4_t;
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+constexpr int kBM = 128;      // query rows per workgroup
+constexpr int kBN = 64;       // keys per KV tile
+constexpr int kWaves = 4;     // wave64s per workgroup; each owns 32 query rows
+constexpr int kThreads = 64 * kWaves;
+constexpr int kListBlock = 128;  // block-list granularity (rows and keys)
+constexpr float kLn2 = 0.69314718055994530942f;
+
+struct Params {
+  const uint16_t *q, *k, *v;
+  uint16_t *o;
+  float *lse;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  const int32_t *cu;       // packed sequences, or null
+  const int32_t *row_ptr;  // block list, or null
+  const int32_t *col_idx;
+  int batch, seqlen, hq, group;
+  int n_tiles;   // query tiles per (sequence, head) = ceil(seqlen / BM)
+  int n_units;   // batch * hq
+  int xcd_remap; // 1 when n_units % 8 == 0
+  float c;       // scale * log2(e)
+};
+
+// ---------------------------------------------------------------------------
+// LDS layouts.  Rows of D bf16 values, 16-byte chunks XOR-swizzled by row so
+// that 16 consecutive rows read at the same logical chunk land in 16
+// different 4-bank groups (K and Q, read as MFMA A/B operands), and 32-byte
+// units swizzled so that 4 consecutive rows read at the same logical unit are
+// conflict-free (V, read with the transpose instruction).
+// ---------------------------------------------------------------------------
+template <int D>
+struct Lds {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;                       // 16 B chunks per row
+  static constexpr int kRowsPerWin = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
+  // byte offset of 16 B chunk `c` of row `r` (K / Q layout)
+  __device__ static __forceinline__ int kq(int r, int c) {
+    return r * kRowBytes + ((c ^ ((r / kRowsPerWin) % kChunks)) << 4);
+  }
+  static constexpr int kUnits = D / 16;                       // 32 B units per row
+  // byte offset of byte `b` (0..31) of 32 B unit `u` of row `r` (V layout)
+  __device__ static __forceinline__ int vv(int r, int u, int b) {
+    return r * kRowBytes + ((u ^ ((r / kRowsPerWin) % kUnits)) << 5) + b;
+  }
+};
+
+__device__ __forceinline__ uint4_t ld_global16(const uint16_t *p) {
+  return *reinterpret_cast<const uint4_t *>(p);
+}
+
+__device__ __forceinline__ float wave_half_swap(float x) {
+  return __shfl_xor(x, 32);
+}
+
+// Decode the workgroup id into (query tile, sequence, head).  Workgroups are
+// dealt round-robin over the 8 XCDs; when the (sequence, head) units divide
+// evenly, each XCD gets a contiguous range of units so that the query heads
+// that share a KV head (and all tiles of a head) share that XCD's L2.
+// Causal and block-list tiles are issued heaviest first.
+__device__ __forceinline__ void decode_tile(const Params &p, bool heavy_first, int &tile,
+                                            int &unit) {
+  const int w = blockIdx.x;
+  int rank;
+  if (p.xcd_remap) {
+    const int upx = p.n_units >> 3;
+    const int local = w >> 3;
+    rank = local / upx;
+    unit = (w & 7) * upx + local % upx;
+  } else {
+    rank = w / p.n_units;
+    unit = w % p.n_units;
+  }
+  tile = heavy_first ? p.n_tiles - 1 - rank : rank;
+}
+
+template <int D, bool CAUSAL, bool LIST>
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p) {
+  using L = Lds<D>;
+  constexpr int kDc = D / 16;   // MFMA k-steps over the head dimension
+  constexpr int kDt = D / 32;   // 32-row output tiles over the head dimension
+  constexpr int kKt = kBN / 32; // 32-key score tiles per KV tile
+  constexpr int kTileBytes = kBN * D * 2;
+  constexpr int kQBytes = kBM * D * 2;
+  constexpr int kSmem = kQBytes > 2 * kTileBytes ? kQBytes : 2 * kTileBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  char *sK = smem;
+  char *sV = smem + kTileBytes;
+
+  int tile, unit;
+  decode_tile(p, CAUSAL || LIST, tile, unit);
+  const int b = unit / p.hq;
+  const int h = unit % p.hq;
+  const int kvh = h / p.group;
+
+  int64_t tok0 = 0;
+  int len = p.seqlen;
+  if (p.cu) {
+    tok0 = p.cu[b];
+    len = p.cu[b + 1] - p.cu[b];
+  }
+  const int q0 = tile * kBM;
+  if (q0 >= len) return;
+
+  const uint16_t *qg = p.q + (p.cu ? tok0 * p.q_ss : (int64_t)b * p.q_sb) + (int64_t)h * p.q_sh;
+  const uint16_t *kg = p.k + (p.cu ? tok0 * p.k_ss : (int64_t)b * p.k_sb) + (int64_t)kvh * p.k_sh;
+  const uint16_t *vg = p.v + (p.cu ? tok0 * p.v_ss : (int64_t)b * p.v_sb) + (int64_t)kvh * p.v_sh;
+  uint16_t *og = p.o + (p.cu ? tok0 * p.o_ss : (int64_t)b * p.o_sb) + (int64_t)h * p.o_sh;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;  // lane half
+
+  // ---- Q tile: global -> LDS (coalesced 16 B chunks) -> registers (MFMA B operand)
+  {
+    constexpr int kChunksTotal = kBM * L::kChunks;
+    for (int id = tid; id < kChunksTotal; id += kThreads) {
+      const int r = id / L::kChunks, c = id % L::kChunks;
+      uint4_t x = {0u, 0u, 0u, 0u};
+      if (q0 + r < len) x = ld_global16(qg + (int64_t)(q0 + r) * p.q_ss + c * 8);
+      *reinterpret_cast<uint4_t *>(smem + L::kq(r, c)) = x;
+    }
+  }
+  __syncthreads();
+  bf16x8_t qreg[kDc];
+  {
+    const int r = wave * 32 + l32;
+#pragma unroll
+    for (int dc = 0; dc < kDc; ++dc)
+      qreg[dc] = *reinterpret_cast<const bf16x8_t *>(smem + L::kq(r, dc * 2 + hi));
+  }
+  __syncthreads();
+
+  // ---- KV iteration space
+  int n_iter;
+  int e0 = 0;
+  const int n_kvblk = (len + kListBlock - 1) / kListBlock;
+  if (LIST) {
+    e0 = p.row_ptr[tile];
+    n_iter = (p.row_ptr[tile + 1] - e0) * (kListBlock / kBN);
+  } else {
+    const int kv_end = CAUSAL ? min(len, q0 + kBM) : len;
+    n_iter = (kv_end + kBN - 1) / kBN;
+  }
+  // kv start of iteration `it`, or -1 to skip it (block-list ids out of range
+  // or, under causal masking, wholly above this query tile)
+  auto kv_start = [&](int it) -> int {
+    if (!LIST) return it * kBN;
+    const int cb = p.col_idx[e0 + it / (kListBlock / kBN)];
+    if (cb < 0 || cb >= n_kvblk) return -1;
+    if (CAUSAL && cb * kListBlock > q0 + kBM - 1) return -1;
+    return cb * kListBlock + (it % (kListBlock / kBN)) * kBN;
+  };
+
+  // register staging of the next KV tile
+  constexpr int kTileChunks = kBN * L::kChunks;
+  constexpr int kPerThread = kTileChunks / kThreads;
+  static_assert(kTileChunks % kThreads == 0, "tile chunks must divide evenly");
+  uint4_t kst[kPerThread], vst[kPerThread];
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int id = tid + i * kThreads;
+      const int r = id / L::kChunks, c = id % L::kChunks;
+      uint4_t xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
+      if (kv0 >= 0 && kv0 + r < len) {
+        xk = ld_global16(kg + (int64_t)(kv0 + r) * p.k_ss + c * 8);
+        xv = ld_global16(vg + (int64_t)(kv0 + r) * p.v_ss + c * 8);
+      }
+      kst[i] = xk;
+      vst[i] = xv;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int id = tid + i * kThreads;
+      const int r = id / L::kChunks, c = id % L::kChunks;
+      *reinterpret_cast<uint4_t *>(sK + L::kq(r, c)) = kst[i];
+      *reinterpret_cast<uint4_t *>(sV + L::vv(r, c >> 1, (c & 1) << 4)) = vst[i];
+    }
+  };
+
+  floatx16_t oacc[kDt];
+#pragma unroll
+  for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+  float m_run = -INFINITY;  // running max of scale*log2(e)*s over this lane's row
+  float l_run = 0.f;        // running sum over this lane's half of the keys
+
+  const int qrow = q0 + wave * 32 + l32;  // this lane's query row (sequence position)
+  const int wq_last = q0 + wave * 32 + 31;
+
+  int kv_next = n_iter > 0 ? kv_start(0) : -1;
+  if (n_iter > 0) load_tile(kv_next);
+
+  for (int it = 0; it < n_iter; ++it) {
+    const int kv0 = kv_next;
+    __syncthreads();  // previous tile fully consumed
+    store_tile();
+    __syncthreads();
+    if (it + 1 < n_iter) {
+      kv_next = kv_start(it + 1);
+      load_tile(kv_next);
+    }
+    if (kv0 < 0) continue;
+    if (CAUSAL && kv0 > wq_last) continue;  // whole tile above this wave's rows
+
+    // ---- S^T = K Q^T : kKt tiles of 32 keys x 32 query rows
+    floatx16_t s[kKt];
+#pragma unroll
+    for (int kt = 0; kt < kKt; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+#pragma unroll
+      for (int dc = 0; dc < kDc; ++dc) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(sK + L::kq(kt * 32 + l32, dc * 2 + hi));
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], s[kt], 0, 0, 0);
+      }
+    }
+
+    // ---- mask (causal diagonal and sequence tail only)
+    const bool need_mask = (kv0 + kBN > len) || (CAUSAL && kv0 + kBN - 1 > q0 + wave * 32);
+    if (need_mask) {
+#pragma unroll
+      for (int kt = 0; kt < kKt; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + kt * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+          const bool bad = key >= len || (CAUSAL && key > qrow);
+          if (bad) s[kt][i] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax (base 2, scale folded into c)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < kKt; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+    mx = fmaxf(mx, wave_half_swap(mx));
+    const float m_new = fmaxf(m_run, mx * p.c);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    float rs = 0.f;
+    bf16x8_t pb[kKt][2];
+#pragma unroll
+    for (int kt = 0; kt < kKt; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], p.c, -m_use));
+        rs += pv;
+        pb[kt][i >> 3][i & 7] = (__bf16)pv;
+      }
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+
+    // ---- O^T += V^T P^T.  MFMA k index (8 per lane half) maps to keys
+    // 16c + 8(e/4) + 4*hi + (e%4) of a 32-key tile, matching where the score
+    // layout left P; V^T operands are read with the LDS transpose.
+    const int j16 = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt) {
+      const int d0 = dt * 32 + ((l32 >> 4) << 4);  // 16 head-dim columns of this lane group
+      const int u = d0 >> 4;                       // 32 B unit
+#pragma unroll
+      for (int kt = 0; kt < kKt; ++kt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int key0 = kt * 32 + 16 * c + 4 * hi + (j16 >> 2);
+          const int boff = (j16 & 3) * 8;
+          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_short4_t *)(sV + L::vv(key0, u, boff)));
+          const short4_t hi8 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_short4_t *)(sV + L::vv(key0 + 8, u, boff)));
+          bf16x8_t a;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] = __builtin_bit_cast(__bf16, lo[e]);
+            a[e + 4] = __builtin_bit_cast(__bf16, hi8[e]);
+          }
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][c], oacc[dt], 0, 0, 0);
+        }
+    }
+  }
+
+  // ---- epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log
+  const float l_tot = l_run + wave_half_swap(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < len) {
+    uint16_t *orow = og + (int64_t)qrow * p.o_ss;
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = dt * 32 + g4 * 8 + hi * 4;
+        __bf16 o4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[dt][g4 * 4 + e] * inv);
+        uint2 w;
+        w.x = (uint32_t)__builtin_bit_cast(uint16_t, o4[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o4[1]) << 16);
+        w.y = (uint32_t)__builtin_bit_cast(uint16_t, o4[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, o4[3]) << 16);
+        *reinterpret_cast<uint2 *>(orow + d) = w;
+      }
+    if (p.lse && hi == 0) {
+      const float v = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      int64_t idx;
+      if (p.cu) {
+        const int64_t total = p.cu[p.batch];
+        idx = (int64_t)h * total + tok0 + qrow;
+      } else {
+        idx = ((int64_t)b * p.hq + h) * p.seqlen + qrow;
+      }
+      p.lse[idx] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+bool stride_ok(int64_t s) { return ((s * 2) % 16) == 0; }
+
+int validate(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+             const int32_t *cu_seqlens, int causal, float scale, const attn_block_list_t *bl,
+             const attn_tensor_t *out) {
+  if (!q || !k || !v || !out) return ATTN_ERR_INVALID_ARG;
+  const attn_tensor_t *all[4] = {q, k, v, out};
+  for (const attn_tensor_t *t : all) {
+    if (t->batch < 0 || t->seqlen < 0 || t->heads < 1 || t->head_dim < 1)
+      return ATTN_ERR_INVALID_ARG;
+  }
+  if (k->batch != q->batch || v->batch != q->batch || out->batch != q->batch)
+    return ATTN_ERR_INVALID_ARG;
+  if (k->seqlen != q->seqlen || v->seqlen != q->seqlen || out->seqlen != q->seqlen)
+    return ATTN_ERR_INVALID_ARG;
+  if (k->head_dim != q->head_dim || v->head_dim != q->head_dim || out->head_dim != q->head_dim)
+    return ATTN_ERR_INVALID_ARG;
+  if (k->heads != v->heads || out->heads != q->heads || q->heads % k->heads != 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (bl) {
+    if (!bl->row_ptr || !bl->col_idx) return ATTN_ERR_INVALID_ARG;
+    if (bl->block_q != kListBlock || bl->block_k != kListBlock) return ATTN_ERR_UNSUPPORTED;
+    if (cu_seqlens || q->batch > 1) return ATTN_ERR_UNSUPPORTED;
+    if (bl->num_q_blocks != (q->seqlen + kListBlock - 1) / kListBlock) return ATTN_ERR_INVALID_ARG;
+  }
+  const bool empty = q->batch == 0 || q->seqlen == 0;
+  if (!empty) {
+    for (const attn_tensor_t *t : all)
+      if (!t->data) return ATTN_ERR_INVALID_ARG;
+  }
+  const int d = q->head_dim;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+  if (!(scale > 0.f)) return ATTN_ERR_UNSUPPORTED;
+  for (const attn_tensor_t *t : all) {
+    if (!aligned16(t->data)) return ATTN_ERR_UNSUPPORTED;
+    if (!stride_ok(t->stride_seq) || !stride_ok(t->stride_head)) return ATTN_ERR_UNSUPPORTED;
+    if (!cu_seqlens && !stride_ok(t->stride_batch)) return ATTN_ERR_UNSUPPORTED;
+  }
+  if (!empty) {
+    const int64_t tiles = (q->seqlen + kBM - 1) / kBM;
+    if (tiles * (int64_t)q->batch * q->heads > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  }
+  return ATTN_OK;
+}
+
+template <int D, bool CAUSAL, bool LIST>
+int launch(const Params &p, int64_t n_blocks, hipStream_t stream) {
+  void *args[] = {const_cast<Params *>(&p)};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<D, CAUSAL, LIST>),
+                                 dim3((unsigned)n_blocks), dim3(kThreads), args, 0, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+template <int D>
+int launch_d(const Params &p, bool causal, bool list, int64_t n, hipStream_t s) {
+  if (list) return causal ? launch<D, true, true>(p, n, s) : launch<D, false, true>(p, n, s);
+  return causal ? launch<D, true, false>(p, n, s) : launch<D, false, false>(p, n, s);
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_validate(const attn_tensor_t *q, const attn_tensor_t *k,
+                                 const attn_tensor_t *v, const int32_t *cu_seqlens, int causal,
+                                 float scale, const attn_block_list_t *block_list,
+                                 const attn_tensor_t *out) {
+  return validate(q, k, v, cu_seqlens, causal, scale, block_list, out);
+}
+
+extern "C" int attn_fwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                        const int32_t *cu_seqlens, int causal, float scale,
+                        const attn_block_list_t *block_list, attn_tensor_t *out, float *lse,
+                        void *stream) {
+  const int st = validate(q, k, v, cu_seqlens, causal, scale, block_list, out);
+  if (st != ATTN_OK) return st;
+  if (q->batch == 0 || q->seqlen == 0) return ATTN_OK;
+
+  Params p;
+  p.q = static_cast<const uint16_t *>(q->data);
+  p.k = static_cast<const uint16_t *>(k->data);
+  p.v = static_cast<const uint16_t *>(v->data);
+  p.o = static_cast<uint16_t *>(out->data);
+  p.lse = lse;
+  p.q_sb = q->stride_batch; p.q_ss = q->stride_seq; p.q_sh = q->stride_head;
+  p.k_sb = k->stride_batch; p.k_ss = k->stride_seq; p.k_sh = k->stride_head;
+  p.v_sb = v->stride_batch; p.v_ss = v->stride_seq; p.v_sh = v->stride_head;
+  p.o_sb = out->stride_batch; p.o_ss = out->stride_seq; p.o_sh = out->stride_head;
+  p.cu = cu_seqlens;
+  p.row_ptr = block_list ? block_list->row_ptr : nullptr;
+  p.col_idx = block_list ? block_list->col_idx : nullptr;
+  p.batch = q->batch;
+  p.seqlen = q->seqlen;
+  p.hq = q->heads;
+  p.group = q->heads / k->heads;
+  p.n_tiles = (q->seqlen + kBM - 1) / kBM;
+  p.n_units = q->batch * q->heads;
+  p.xcd_remap = (p.n_units % 8) == 0 ? 1 : 0;
+  p.c = scale * 1.44269504088896340736f;
+  const int64_t n = (int64_t)p.n_tiles * p.n_units;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool list = block_list != nullptr;
+  switch (q->head_dim) {
+    case 64: return launch_d<64>(p, causal, list, n, s);
+    case 128: return launch_d<128>(p, causal, list, n, s);
+    default: return launch_d<256>(p, causal, list, n, s);
+  }
+}
+
+extern "C" const char *attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported argument combination";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int attn_version(void) { return 100; }

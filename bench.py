@@ -1,0 +1,181 @@
+"""Benchmark: fused attention forward on one MI355X.
+
+A step is one forward pass (one ``attn_fwd`` launch) over the dense causal
+multi-head workload B=4, H=16, S=2048, D=128 (bf16, inputs resident in HBM).
+Prints ONE JSON line with causal-adjusted TFLOP/s, the roofline fraction of
+the kernel against the bf16 dense MFMA peak, and the fp64 CPU oracle timed on
+a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload mha]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import attn_workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA peak
+METRIC = "attention fwd TFLOPS (bf16, causal-adjusted) and % of MFMA bf16 peak, 1 GPU"
+KERNEL_SRC = os.path.join(ROOT, "attention_forward_flashattention_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_mha.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they match this kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_src_sha256_16") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w: W.Workload, budget_s: float = 12.0):
+    """fp64 oracle on a bounded random sample of query rows (all heads).
+
+    The sample's time is scaled by (pairs of the whole workload) / (pairs of the
+    sample) to a full-run estimate, and reported in the metric's unit: the
+    workload's causal-adjusted FLOPs divided by that estimate.
+    """
+    import oracle
+
+    threads = min(oracle.default_threads(), 16)
+    rng = np.random.default_rng(1234)
+    t_all = w.batch * w.seqlen
+
+    def pairs(rows):
+        pos = rows % w.seqlen
+        return float(np.sum(pos + 1)) if w.causal else float(len(rows) * w.seqlen)
+
+    total_pairs = pairs(np.arange(t_all))
+    n, spent, sample_pairs, used = 64, 0.0, 0.0, 0
+    while True:
+        rows = np.sort(rng.choice(t_all, size=n, replace=False))
+        t0 = time.perf_counter()
+        oracle.run_workload(w, rows=rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        spent += dt
+        sample_pairs += pairs(rows)
+        used += n
+        if spent >= budget_s or used >= t_all:
+            break
+        n = int(min(4096, t_all, max(n, n * (budget_s - spent) / max(dt, 1e-3))))
+    full_s = spent * total_pairs / sample_pairs
+    return {"value": W.counted_flops(w) / full_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{used} random query rows (with repeats across draws) x {w.hq} heads of the same "
+                      f"workload, {spent:.1f} s of fp64 oracle time scaled by pair count to a full-run "
+                      f"estimate of {full_s:.0f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mha", choices=list(W.CONFIG_NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention forward here is a "
+              "single-GPU kernel and no multi-GPU path is built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_forward_flashattention_amd as attn
+    from tests import _parity as P
+
+    w = W.make(args.workload)
+    flops = W.counted_flops(w)
+    q, k, v, cu, bl = P.to_device(w)
+    out = torch.empty_like(q)
+    if cu is None:
+        lse = torch.empty((w.batch, w.hq, w.seqlen), dtype=torch.float32, device=q.device)
+    else:
+        lse = torch.empty((w.hq, q.shape[0]), dtype=torch.float32, device=q.device)
+
+    def step():
+        attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale, block_list=bl, out=out,
+                      lse=lse, max_seqlen=w.seqlen if cu is not None else None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-launch kernel durations (events on the launch stream, which is torch's current stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start_all = torch.cuda.Event(enable_timing=True)
+    end_all = torch.cuda.Event(enable_timing=True)
+    start_all.record()
+    for e0, e1 in evs:
+        e0.record()
+        step()
+        e1.record()
+    end_all.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start_all.elapsed_time(end_all)
+    per_launch = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = float(np.mean(per_launch))
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    log(f"workload {w.name}: {flops / 1e9:.2f} GFLOP/launch, {ms_per_step * 1e3:.1f} us/step "
+        f"(median launch {np.median(per_launch) * 1e3:.1f} us, min {min(per_launch) * 1e3:.1f} us), "
+        f"wall {wall * 1e3 / args.steps:.1f} us/step, {tflops:.1f} TFLOP/s = "
+        f"{100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
+
+    cpu = None
+    if not args.no_cpu_baseline and not w.packed and w.row_ptr is None:
+        cpu = cpu_baseline(w)
+        log(f"cpu oracle: {cpu}")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: i.i.d. N(0,1) inputs rounded to bf16, seeded",
+        "config": {"workload": f"{w.name}: dense causal MHA B={w.batch} H={w.hq} S={w.seqlen} D={w.d}"
+                   if w.name == "mha" else w.name,
+                   "batch": w.batch, "seq_len": w.seqlen, "heads_q": w.hq, "heads_kv": w.hkv,
+                   "head_dim": w.d, "causal": w.causal, "flops_per_step": flops,
+                   "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

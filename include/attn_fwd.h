@@ -1,0 +1,136 @@
+/*
+ * attn_fwd.h — C ABI of the fused softmax-attention forward library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation
+ * -------------
+ * For every sequence b, query head h and query position i, with g = Hq/Hkv
+ * query heads per key/value head and kv head c = floor(h / g):
+ *
+ *   A(i)  = { j : 0 <= j < L_b, (causal == 0 || j <= i),
+ *                 (no block list || floor(j/128) is listed for floor(i/128)) }
+ *   O[b,i,h,:] = sum_{j in A(i)} softmax_j(scale * q.k_j) * v[b,j,c,:]
+ *   lse[b,h,i] = ln sum_{j in A(i)} exp(scale * q.k_j)      (natural log)
+ *   A(i) empty:  O = 0, lse = -inf.
+ *
+ * This is the softmax attention that FlashAttention-style kernels compute
+ * without materialising the score matrix: the AdaSplash-2 explainer
+ * (technical summary, section 1) describes those kernels as fusing the
+ * softmax attention steps in on-chip memory, with the closed-form
+ * log-sum-exp normaliser.  The optional block list is the ordered priority
+ * list of KV blocks that the CoSA explainer (lay summary) has a proxy hand to
+ * an ordered-skipping kernel; unlisted blocks are never loaded, as the
+ * AdaSplash-2 explainer (section 2, sparsity-aware execution) does for
+ * empty blocks.  The list order is only a visiting order.
+ *
+ * Conventions
+ * -----------
+ * - All tensor and index pointers are DEVICE pointers owned by the caller.
+ *   The library allocates nothing, keeps no state between calls, and is
+ *   safe to call from several host threads at once.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream).  The library never reads device memory on the host and never
+ *   synchronises.  Errors inside a kernel surface at the caller's next
+ *   synchronisation.
+ * - q, k, v, out are bfloat16; lse is float32; scale is float32;
+ *   accumulation is float32 and O is rounded to nearest even.
+ * - head_dim is contiguous (stride 1); all strides are in ELEMENTS.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A bfloat16 tensor of logical shape [batch, seqlen, heads, head_dim].
+ * Fixed-length batches: element (b, s, h, d) lives at
+ *     data + b*stride_batch + s*stride_seq + h*stride_head + d.
+ * Packed variable-length batches (cu_seqlens != NULL): batch = number of
+ * sequences, seqlen = an upper bound on every sequence length (the
+ * max_seqlen), stride_batch is ignored, and token t of the packed [T, H, D]
+ * tensor lives at data + t*stride_seq + h*stride_head + d. */
+typedef struct attn_tensor {
+  void *data;
+  int32_t batch, seqlen, heads, head_dim;
+  int64_t stride_batch, stride_seq, stride_head;
+} attn_tensor_t;
+
+/* Ordered per-query-block list of KV blocks (CSR).
+ * row_ptr: device int32 [num_q_blocks + 1], non-decreasing, row_ptr[0] = 0.
+ * col_idx: device int32 [row_ptr[num_q_blocks]], the KV block ids of query
+ *          block r in visiting order at col_idx[row_ptr[r] .. row_ptr[r+1]).
+ * Ids outside [0, ceil(seqlen/block_k)) are skipped.  Each id may appear at
+ * most once per row (a repeated id is a caller error: it is visited twice).
+ * Under causal masking, ids above the query block contribute nothing. */
+typedef struct attn_block_list {
+  const int32_t *row_ptr;
+  const int32_t *col_idx;
+  int32_t block_q, block_k; /* both must be 128 */
+  int32_t num_q_blocks;     /* must equal ceil(seqlen / 128) */
+} attn_block_list_t;
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1, /* arguments contradict each other or are null */
+  ATTN_ERR_UNSUPPORTED = -2, /* valid, but not implemented by this library   */
+  ATTN_ERR_LAUNCH = -3       /* the HIP kernel launch itself failed          */
+};
+
+/*
+ * attn_fwd — fused attention forward.
+ *
+ *   q          [B, S, Hq, D]  (or packed [T, Hq, D] with cu_seqlens)
+ *   k, v       [B, S, Hkv, D] (or packed [T, Hkv, D]); Hq % Hkv == 0,
+ *              k and v have equal heads; q/k/v/out share batch, seqlen
+ *              and head_dim
+ *   cu_seqlens device int32 [B + 1] prefix sums of packed sequence lengths,
+ *              or NULL for fixed-length batches
+ *   causal     0 or 1 (key j visible to query i iff j <= i, positions counted
+ *              from the start of each sequence)
+ *   scale      multiplies q.k; finite and > 0
+ *   block_list NULL for dense attention, else see attn_block_list_t
+ *              (requires B == 1 and cu_seqlens == NULL)
+ *   out        [B, S, Hq, D] bfloat16 (or packed [T, Hq, D]), written only
+ *              at valid positions
+ *   lse        NULL, or float32 [B, Hq, S] contiguous (packed: [Hq, T] with
+ *              T = cu_seqlens[B]); natural log, includes scale
+ *   stream     hipStream_t to enqueue on
+ *
+ * Returns ATTN_OK, or:
+ *   ATTN_ERR_INVALID_ARG  null descriptor or data pointer, negative sizes,
+ *                         Hq % Hkv != 0, mismatched batch/seqlen/head_dim,
+ *                         k/v head mismatch, out heads != Hq, causal not 0/1,
+ *                         non-finite scale, bad block-list descriptor
+ *   ATTN_ERR_UNSUPPORTED  head_dim not in {64, 128, 256}; scale <= 0; data
+ *                         pointer or any stride*2 not a multiple of 16 bytes;
+ *                         block sizes other than 128; a block list combined
+ *                         with cu_seqlens or batch > 1; a launch grid beyond
+ *                         2^31 - 1 workgroups
+ *   ATTN_ERR_LAUNCH       the kernel launch failed
+ * An empty problem (batch == 0 or seqlen == 0) returns ATTN_OK and launches
+ * nothing.
+ */
+int attn_fwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+             const int32_t *cu_seqlens, int causal, float scale,
+             const attn_block_list_t *block_list, attn_tensor_t *out, float *lse, void *stream);
+
+/* The argument checks of attn_fwd alone: pure host code, no HIP call, no
+ * device access.  Returns what attn_fwd would return before launching. */
+int attn_fwd_validate(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                      const int32_t *cu_seqlens, int causal, float scale,
+                      const attn_block_list_t *block_list, const attn_tensor_t *out);
+
+/* Static description of a status code (never NULL). */
+const char *attn_status_str(int status);
+
+/* Library ABI version: major*10000 + minor*100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

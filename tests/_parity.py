@@ -1,0 +1,104 @@
+"""Helpers shared by the GPU parity tests and the smoke check.
+
+Runs a workload through the HIP library (via the Python binding, which calls
+the C ABI) and compares it with the fp64 oracle on the same seeded inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import attn_workloads as W
+
+# Tolerances for bf16 inputs/outputs with fp32 accumulation.
+O_MAX_ABS = 2e-2
+O_MEAN_ABS = 2e-3
+LSE_MAX_ABS = 1e-3
+O_REL_RMS = 1e-2   # ||O - O_ref||_2 / ||O_ref||_2, catches errors the loose max-abs bound can hide
+
+
+def to_device(w: W.Workload, layout: str = "bshd"):
+    """Device tensors for a workload: q, k, v (bf16), cu_seqlens, block list."""
+    import torch
+
+    dev = torch.device("cuda:0")
+
+    def t(a):
+        x = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        if layout == "bhsd" and x.dim() == 4:
+            # same logical [B,S,H,D] tensor held in [B,H,S,D] memory order
+            x = x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        return x
+
+    q, k, v = t(w.q), t(w.k), t(w.v)
+    cu = None if w.cu_seqlens is None else torch.from_numpy(w.cu_seqlens.astype(np.int32)).to(dev)
+    bl = None
+    if w.row_ptr is not None:
+        bl = (torch.from_numpy(w.row_ptr.astype(np.int32)).to(dev),
+              torch.from_numpy(w.col_idx.astype(np.int32)).to(dev))
+    return q, k, v, cu, bl
+
+
+def run_gpu(w: W.Workload, layout: str = "bshd", tensors=None):
+    """GPU output in packed order: O float64 [T, Hq, D], LSE float64 [T, Hq]."""
+    import torch
+    import attention_forward_flashattention_amd as attn
+
+    q, k, v, cu, bl = tensors if tensors is not None else to_device(w, layout)
+    out, lse = attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale, block_list=bl,
+                             max_seqlen=w.seqlen if cu is not None else None)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy().astype(np.float64)
+    if cu is None:
+        o = o.reshape(w.batch * w.seqlen, w.hq, w.d)
+        l = l.transpose(0, 2, 1).reshape(w.batch * w.seqlen, w.hq)   # [B,H,S] -> tokens
+    else:
+        l = l.T                                                      # [H,T] -> [T,H]
+    return o, l
+
+
+def sample_tokens(w: W.Workload, per_seq: int = 48, seed: int = 0) -> np.ndarray:
+    """Packed token ids: tile edges and ends of every sequence plus random rows."""
+    rng = np.random.default_rng(seed)
+    cu = w.cu_seqlens_or_fixed().astype(np.int64)
+    out = []
+    for b in range(len(cu) - 1):
+        n = int(cu[b + 1] - cu[b])
+        if n == 0:
+            continue
+        fixed = {0, 1, 63, 64, 127, 128, 129, 255, 256, n - 129, n - 128, n - 65, n - 64, n - 2, n - 1}
+        fixed = {p for p in fixed if 0 <= p < n}
+        rest = rng.choice(n, size=min(n, per_seq), replace=False)
+        out.extend(int(cu[b]) + p for p in sorted(fixed | set(int(x) for x in rest)))
+    return np.array(sorted(set(out)), dtype=np.int64)
+
+
+def compare(o_gpu, l_gpu, o_ref, l_ref, label=""):
+    """Check the tolerances; returns a dict of error statistics."""
+    assert np.all(np.isfinite(o_gpu)), f"{label}: non-finite O"
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(l_gpu), fin), f"{label}: LSE finiteness differs"
+    assert np.all(l_gpu[~fin] == l_ref[~fin]), f"{label}: empty rows must give -inf"
+    err = np.abs(o_gpu - o_ref)
+    stats = {
+        "o_max_abs": float(err.max()) if err.size else 0.0,
+        "o_mean_abs": float(err.mean()) if err.size else 0.0,
+        "lse_max_abs": float(np.abs(l_gpu[fin] - l_ref[fin]).max()) if fin.any() else 0.0,
+        "o_rel_rms": float(np.linalg.norm(o_gpu - o_ref) / max(np.linalg.norm(o_ref), 1e-30)),
+    }
+    assert stats["o_max_abs"] <= O_MAX_ABS, (label, stats)
+    assert stats["o_mean_abs"] <= O_MEAN_ABS, (label, stats)
+    assert stats["lse_max_abs"] <= LSE_MAX_ABS, (label, stats)
+    assert stats["o_rel_rms"] <= O_REL_RMS, (label, stats)
+    return stats
+
+
+def check_workload(w: W.Workload, rows=None, layout: str = "bshd", nthreads: int = 0):
+    """GPU vs oracle on all rows (rows=None) or on the given packed token ids."""
+    import oracle
+
+    o, l = run_gpu(w, layout)
+    o_ref, l_ref = oracle.run_workload(w, rows=rows, nthreads=nthreads)
+    if rows is not None:
+        o, l = o[rows], l[rows]
+    return compare(o, l, o_ref, l_ref, w.name)

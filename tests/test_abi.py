@@ -1,0 +1,120 @@
+"""The C-ABI library: loads, exports what include/attn_fwd.h declares, and
+rejects bad arguments with the documented status codes (host-only checks; no
+kernel is launched, so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import attention_forward_flashattention_amd as attn
+from attention_forward_flashattention_amd import AttnBlockList, AttnTensor
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["attn_fwd", "attn_fwd_validate", "attn_status_str", "attn_version"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = attn.load_library()
+    out = subprocess.run(["nm", "-D", "--defined-only", attn.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert lib.attn_version() == 100
+    assert attn.status_str(0) == "ok" and attn.status_str(-3) == "kernel launch failed"
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation only reads the descriptors
+
+
+def desc(b=2, s=256, h=8, d=128, data=FAKE, layout="bshd"):
+    if layout == "bshd":
+        return AttnTensor(data, b, s, h, d, s * h * d, h * d, d)
+    return AttnTensor(data, b, s, h, d, h * s * d, d, s * d)
+
+
+def validate(q, k, v, cu=None, causal=1, scale=0.125, bl=None, out=None):
+    lib = attn.load_library()
+    out = out if out is not None else q
+    return lib.attn_fwd_validate(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), cu, causal, scale,
+                                 ctypes.byref(bl) if bl is not None else None, ctypes.byref(out))
+
+
+def test_valid_arguments_pass():
+    assert validate(desc(), desc(h=2), desc(h=2)) == 0
+    assert validate(desc(layout="bhsd"), desc(h=8, layout="bhsd"), desc(h=8, layout="bhsd")) == 0
+    for d in (64, 128, 256):
+        assert validate(desc(d=d), desc(d=d, h=4), desc(d=d, h=4)) == 0
+
+
+@pytest.mark.parametrize("mut,code", [
+    (lambda q, k, v: setattr(k, "heads", 3), -1),             # Hq % Hkv != 0
+    (lambda q, k, v: setattr(v, "heads", 4), -1),             # k/v head mismatch
+    (lambda q, k, v: setattr(k, "seqlen", 255), -1),          # seqlen mismatch
+    (lambda q, k, v: setattr(v, "batch", 1), -1),             # batch mismatch
+    (lambda q, k, v: setattr(k, "head_dim", 64), -1),         # head_dim mismatch
+    (lambda q, k, v: setattr(q, "data", None), -1),           # null data
+    (lambda q, k, v: [setattr(t, "head_dim", 96) for t in (q, k, v)], -2),  # unsupported D (out too)
+    (lambda q, k, v: setattr(q, "data", FAKE + 8), -2),       # misaligned pointer
+    (lambda q, k, v: setattr(k, "stride_seq", 2 * 128 + 4), -2),  # stride*2 not multiple of 16
+    (lambda q, k, v: setattr(q, "batch", -1), -1),
+])
+def test_invalid_arguments(mut, code):
+    q, k, v = desc(), desc(h=2), desc(h=2)
+    o = desc()
+    mut(q, k, v)
+    o.head_dim = q.head_dim if q.head_dim == 96 else o.head_dim
+    assert validate(q, k, v, out=o) == code
+
+
+def test_scalar_arguments():
+    q, k, v = desc(), desc(h=2), desc(h=2)
+    assert validate(q, k, v, causal=2) == -1
+    assert validate(q, k, v, scale=float("nan")) == -1
+    assert validate(q, k, v, scale=float("inf")) == -1
+    assert validate(q, k, v, scale=0.0) == -2
+    assert validate(q, k, v, scale=-0.5) == -2
+    assert validate(q, k, v, out=desc(h=4)) == -1  # out heads != Hq
+
+
+def test_block_list_arguments():
+    q, k, v = desc(b=1, s=1000), desc(b=1, s=1000, h=2), desc(b=1, s=1000, h=2)
+    ok = AttnBlockList(FAKE, FAKE, 128, 128, 8)
+    assert validate(q, k, v, bl=ok) == 0
+    assert validate(q, k, v, bl=AttnBlockList(FAKE, FAKE, 64, 128, 8)) == -2
+    assert validate(q, k, v, bl=AttnBlockList(FAKE, FAKE, 128, 128, 7)) == -1
+    assert validate(q, k, v, bl=AttnBlockList(None, FAKE, 128, 128, 8)) == -1
+    q2, k2, v2 = desc(b=2, s=1000), desc(b=2, s=1000, h=2), desc(b=2, s=1000, h=2)
+    assert validate(q2, k2, v2, bl=ok) == -2          # batch > 1 with a list
+    assert validate(q, k, v, cu=ctypes.c_void_p(FAKE), bl=ok) == -2   # packed with a list
+
+
+def test_empty_problem_is_ok_without_data():
+    q, k, v = desc(b=0, data=None), desc(b=0, h=2, data=None), desc(b=0, h=2, data=None)
+    assert validate(q, k, v, out=desc(b=0, data=None)) == 0
+
+
+def test_attn_fwd_returns_validation_errors_without_launching():
+    lib = attn.load_library()
+    q, k, v = desc(), desc(h=3), desc(h=3)
+    st = lib.attn_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), None, 1, 0.1, None,
+                      ctypes.byref(desc()), None, None)
+    assert st == -1
+    # an empty problem returns OK and launches nothing
+    e = desc(b=0, data=None)
+    st = lib.attn_fwd(ctypes.byref(e), ctypes.byref(e), ctypes.byref(e), None, 1, 0.1, None,
+                      ctypes.byref(e), None, None)
+    assert st == 0
