@@ -27,6 +27,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) short short4_t;
 typedef __attribute__((ext_vector_type(16))) float floatx16_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int uint4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int uint2_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
 constexpr int kBM = 128;      // query rows per workgroup
@@ -312,12 +313,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p) {
               (lds_short4_t *)(sV + L::vv(key0, u, boff)));
           const short4_t hi8 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_short4_t *)(sV + L::vv(key0 + 8, u, boff)));
-          bf16x8_t a;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a[e] = __builtin_bit_cast(__bf16, lo[e]);
-            a[e + 4] = __builtin_bit_cast(__bf16, hi8[e]);
-          }
+          // whole-register reinterpretation (no per-element shuffles)
+          const uint2_t lo2 = __builtin_bit_cast(uint2_t, lo);
+          const uint2_t hi2 = __builtin_bit_cast(uint2_t, hi8);
+          const uint4_t packed = {lo2.x, lo2.y, hi2.x, hi2.y};
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, packed);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][c], oacc[dt], 0, 0, 0);
         }
     }
