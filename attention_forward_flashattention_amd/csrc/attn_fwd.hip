@@ -29,13 +29,17 @@ typedef __attribute__((ext_vector_type(16))) float floatx16_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int uint4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned int uint2_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBM = 128;      // query rows per workgroup
-constexpr int kBN = 64;       // keys per KV tile
 constexpr int kWaves = 4;     // wave64s per workgroup; each owns 32 query rows
 constexpr int kThreads = 64 * kWaves;
 constexpr int kListBlock = 128;  // block-list granularity (rows and keys)
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLazy = 8.f;  // log2 headroom before the running max is raised
+// s_waitcnt immediate that waits for vmcnt == 0 and leaves the other counters
+// free (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
+constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 
 struct Params {
   const uint16_t *q, *k, *v;
@@ -67,23 +71,47 @@ struct Lds {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = D / 8;                       // 16 B chunks per row
   static constexpr int kRowsPerWin = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
+  __device__ static __forceinline__ int kswz(int r) { return (r / kRowsPerWin) % kChunks; }
   // byte offset of 16 B chunk `c` of row `r` (K / Q layout)
   __device__ static __forceinline__ int kq(int r, int c) {
-    return r * kRowBytes + ((c ^ ((r / kRowsPerWin) % kChunks)) << 4);
+    return r * kRowBytes + ((c ^ kswz(r)) << 4);
   }
   static constexpr int kUnits = D / 16;                       // 32 B units per row
+  __device__ static __forceinline__ int vswz(int r) { return (r / kRowsPerWin) % kUnits; }
   // byte offset of byte `b` (0..31) of 32 B unit `u` of row `r` (V layout)
   __device__ static __forceinline__ int vv(int r, int u, int b) {
-    return r * kRowBytes + ((u ^ ((r / kRowsPerWin) % kUnits)) << 5) + b;
+    return r * kRowBytes + ((u ^ vswz(r)) << 5) + b;
   }
+};
+
+// Keys per KV tile: 64, or 32 at head_dim 256 to bound registers and LDS.
+template <int D>
+struct KvTile {
+  static constexpr int kBN = D == 256 ? 32 : 64;
 };
 
 __device__ __forceinline__ uint4_t ld_global16(const uint16_t *p) {
   return *reinterpret_cast<const uint4_t *>(p);
 }
 
-__device__ __forceinline__ float wave_half_swap(float x) {
-  return __shfl_xor(x, 32);
+// Exchange between the two lane halves: after v_permlane32_swap, `a` holds
+// lanes 0-31 of x in both halves and `b` lanes 32-63 of x in both halves, so
+// a (op) b is the pairwise result for lanes l and l^32 in every lane.  (Inline
+// assembly: the compiler builtin returns the same register for both results.)
+__device__ __forceinline__ void half_pair(float x, float &a, float &b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float half_max(float x) {
+  float a, b;
+  half_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  float a, b;
+  half_pair(x, a, b);
+  return a + b;
 }
 
 // Decode the workgroup id into (query tile, sequence, head).  Workgroups are
@@ -108,17 +136,19 @@ __device__ __forceinline__ void decode_tile(const Params &p, bool heavy_first, i
 }
 
 template <int D, bool CAUSAL, bool LIST>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_fwd_kernel(Params p) {
   using L = Lds<D>;
+  constexpr int kBN = KvTile<D>::kBN;
   constexpr int kDc = D / 16;   // MFMA k-steps over the head dimension
   constexpr int kDt = D / 32;   // 32-row output tiles over the head dimension
   constexpr int kKt = kBN / 32; // 32-key score tiles per KV tile
   constexpr int kTileBytes = kBN * D * 2;
+  constexpr int kBufBytes = 2 * kTileBytes;  // one K tile then one V tile
   constexpr int kQBytes = kBM * D * 2;
-  constexpr int kSmem = kQBytes > 2 * kTileBytes ? kQBytes : 2 * kTileBytes;
-  __shared__ __attribute__((aligned(16))) char smem[kSmem];
-  char *sK = smem;
-  char *sV = smem + kTileBytes;
+  constexpr int kSmem = kQBytes > 2 * kBufBytes ? kQBytes : 2 * kBufBytes;
+  constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 1 KB per wave-wide 16 B load
+  static_assert(kLoadsPerWave * 1024 * kWaves == kTileBytes, "tile must split evenly over waves");
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
 
   int tile, unit;
   decode_tile(p, CAUSAL || LIST, tile, unit);
@@ -142,9 +172,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;  // lane half
+  const int j16 = lane & 15;
 
   // ---- Q tile: global -> LDS (coalesced 16 B chunks) -> registers (MFMA B operand)
   {
@@ -187,32 +218,23 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p) {
     return cb * kListBlock + (it % (kListBlock / kBN)) * kBN;
   };
 
-  // register staging of the next KV tile
-  constexpr int kTileChunks = kBN * L::kChunks;
-  constexpr int kPerThread = kTileChunks / kThreads;
-  static_assert(kTileChunks % kThreads == 0, "tile chunks must divide evenly");
-  uint4_t kst[kPerThread], vst[kPerThread];
-  auto load_tile = [&](int kv0) {
+  // Direct global -> LDS loads of one KV tile into buffer `buf`.  Each wave-wide
+  // load writes 64 consecutive 16 B LDS slots; each lane fetches the global
+  // chunk that the swizzled layout places in its slot.  Rows past the end of
+  // the sequence re-read the last row (finite data; those keys are masked).
+  auto issue_tile = [&](int kv0, int buf) {
+    char *kb = smem + buf * kBufBytes;
+    char *vb = kb + kTileBytes;
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int id = tid + i * kThreads;
-      const int r = id / L::kChunks, c = id % L::kChunks;
-      uint4_t xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-      if (kv0 >= 0 && kv0 + r < len) {
-        xk = ld_global16(kg + (int64_t)(kv0 + r) * p.k_ss + c * 8);
-        xv = ld_global16(vg + (int64_t)(kv0 + r) * p.v_ss + c * 8);
-      }
-      kst[i] = xk;
-      vst[i] = xv;
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int id = tid + i * kThreads;
-      const int r = id / L::kChunks, c = id % L::kChunks;
-      *reinterpret_cast<uint4_t *>(sK + L::kq(r, c)) = kst[i];
-      *reinterpret_cast<uint4_t *>(sV + L::vv(r, c >> 1, (c & 1) << 4)) = vst[i];
+    for (int n = 0; n < kLoadsPerWave; ++n) {
+      const int slot0 = (wave * kLoadsPerWave + n) * 64;
+      const int slot = slot0 + lane;
+      const int r = slot / L::kChunks, pc = slot % L::kChunks;
+      const int64_t row = min(kv0 + r, len - 1);
+      const int ck = pc ^ L::kswz(r);
+      const int cv = (((pc >> 1) ^ L::vswz(r)) << 1) | (pc & 1);
+      __builtin_amdgcn_global_load_lds(kg + row * p.k_ss + ck * 8, (lds_void_t *)(kb + slot0 * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vg + row * p.v_ss + cv * 8, (lds_void_t *)(vb + slot0 * 16), 16, 0, 0);
     }
   };
 
@@ -221,26 +243,34 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p) {
   for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
-  float m_run = -INFINITY;  // running max of scale*log2(e)*s over this lane's row
-  float l_run = 0.f;        // running sum over this lane's half of the keys
+  // Running max of c*s for this lane's row (c = scale*log2 e).  It is raised
+  // lazily: only when a tile's max exceeds it by more than kLazy, so P values
+  // stay below 2^kLazy and most tiles skip the rescale of O.
+  float m_run = -INFINITY;
+  float l_run = 0.f;  // running sum over this lane's half of the keys
 
   const int qrow = q0 + wave * 32 + l32;  // this lane's query row (sequence position)
   const int wq_last = q0 + wave * 32 + 31;
 
-  int kv_next = n_iter > 0 ? kv_start(0) : -1;
-  if (n_iter > 0) load_tile(kv_next);
+  int kv_cur = n_iter > 0 ? kv_start(0) : -1;
+  if (kv_cur >= 0) issue_tile(kv_cur, 0);
 
   for (int it = 0; it < n_iter; ++it) {
-    const int kv0 = kv_next;
-    __syncthreads();  // previous tile fully consumed
-    store_tile();
+    // tile `it` has landed (every wave waited for its own loads); every wave is
+    // done reading the other buffer
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+    int kv_nxt = -1;
     if (it + 1 < n_iter) {
-      kv_next = kv_start(it + 1);
-      load_tile(kv_next);
+      kv_nxt = kv_start(it + 1);
+      if (kv_nxt >= 0) issue_tile(kv_nxt, (it + 1) & 1);
     }
+    const int kv0 = kv_cur;
+    kv_cur = kv_nxt;
     if (kv0 < 0) continue;
     if (CAUSAL && kv0 > wq_last) continue;  // whole tile above this wave's rows
+    const char *sK = smem + (it & 1) * kBufBytes;
+    const char *sV = sK + kTileBytes;
 
     // ---- S^T = K Q^T : kKt tiles of 32 keys x 32 query rows
     floatx16_t s[kKt];
@@ -273,12 +303,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p) {
 #pragma unroll
     for (int kt = 0; kt < kKt; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-    mx = fmaxf(mx, wave_half_swap(mx));
-    const float m_new = fmaxf(m_run, mx * p.c);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kt][i], s[kt][i + 1]));
+    mx = half_max(mx);
+    const float mt = mx * p.c;
+    const bool need = mt > m_run + kLazy;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = need ? mt : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float rs = 0.f;
     bf16x8_t pb[kKt][2];
 #pragma unroll
@@ -289,20 +328,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p) {
         rs += pv;
         pb[kt][i >> 3][i & 7] = (__bf16)pv;
       }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int dt = 0; dt < kDt; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    l_run += rs;
 
     // ---- O^T += V^T P^T.  MFMA k index (8 per lane half) maps to keys
     // 16c + 8(e/4) + 4*hi + (e%4) of a 32-key tile, matching where the score
     // layout left P; V^T operands are read with the LDS transpose.
-    const int j16 = lane & 15;
 #pragma unroll
     for (int dt = 0; dt < kDt; ++dt) {
-      const int d0 = dt * 32 + ((l32 >> 4) << 4);  // 16 head-dim columns of this lane group
-      const int u = d0 >> 4;                       // 32 B unit
+      const int u = (dt * 32 + ((l32 >> 4) << 4)) >> 4;  // 32 B unit of this lane group's 16 columns
 #pragma unroll
       for (int kt = 0; kt < kKt; ++kt)
 #pragma unroll
@@ -313,7 +346,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p) {
               (lds_short4_t *)(sV + L::vv(key0, u, boff)));
           const short4_t hi8 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_short4_t *)(sV + L::vv(key0 + 8, u, boff)));
-          // whole-register reinterpretation (no per-element shuffles)
+          // whole-register reinterpretation (per-element inserts were lowered to
+          // byte permutes that duplicated elements)
           const uint2_t lo2 = __builtin_bit_cast(uint2_t, lo);
           const uint2_t hi2 = __builtin_bit_cast(uint2_t, hi8);
           const uint4_t packed = {lo2.x, lo2.y, hi2.x, hi2.y};
@@ -324,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p) {
   }
 
   // ---- epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log
-  const float l_tot = l_run + wave_half_swap(l_run);
+  const float l_tot = half_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < len) {
     uint16_t *orow = og + (int64_t)qrow * p.o_ss;
