@@ -60,27 +60,35 @@ struct Params {
 };
 
 // ---------------------------------------------------------------------------
-// LDS layouts.  Rows of D bf16 values, 16-byte chunks XOR-swizzled by row so
-// that 16 consecutive rows read at the same logical chunk land in 16
-// different 4-bank groups (K and Q, read as MFMA A/B operands), and 32-byte
-// units swizzled so that 4 consecutive rows read at the same logical unit are
-// conflict-free (V, read with the transpose instruction).
+// LDS layouts (rows of D bf16 values; bank behaviour measured with the
+// SQ_LDS_BANK_CONFLICT counter on gfx950).
+//  K and Q: 16 B chunks XOR-swizzled by row, so the 16 consecutive rows that
+//    one MFMA operand read touches at one logical chunk hit 16 distinct
+//    4-bank groups (ds_read_b128, conflict-free).
+//  V: 64 B pairs of 32 B units XOR-swizzled by row, so the 4 rows x 64 B that
+//    32 lanes of one transpose read touch land in 4 distinct 64 B bank ranges
+//    (ds_read_b64_tr_b16, conflict-free).
 // ---------------------------------------------------------------------------
 template <int D>
 struct Lds {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = D / 8;                       // 16 B chunks per row
   static constexpr int kRowsPerWin = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
+  static constexpr int kPairs = D / 32;                       // 64 B pairs per row
+  static constexpr int kPairSwz = kPairs < 4 ? kPairs : 4;
   __device__ static __forceinline__ int kswz(int r) { return (r / kRowsPerWin) % kChunks; }
   // byte offset of 16 B chunk `c` of row `r` (K / Q layout)
   __device__ static __forceinline__ int kq(int r, int c) {
     return r * kRowBytes + ((c ^ kswz(r)) << 4);
   }
-  static constexpr int kUnits = D / 16;                       // 32 B units per row
-  __device__ static __forceinline__ int vswz(int r) { return (r / kRowsPerWin) % kUnits; }
+  __device__ static __forceinline__ int vswz(int r) { return (r / kRowsPerWin) % kPairSwz; }
   // byte offset of byte `b` (0..31) of 32 B unit `u` of row `r` (V layout)
   __device__ static __forceinline__ int vv(int r, int u, int b) {
-    return r * kRowBytes + ((u ^ vswz(r)) << 5) + b;
+    return r * kRowBytes + ((((u >> 1) ^ vswz(r)) << 6) | ((u & 1) << 5)) + b;
+  }
+  // logical 16 B chunk that the V layout stores in physical chunk `pc` of row `r`
+  __device__ static __forceinline__ int v_logical_chunk(int r, int pc) {
+    return ((((pc >> 2) ^ vswz(r))) << 2) | (pc & 3);
   }
 };
 
@@ -135,6 +143,42 @@ __device__ __forceinline__ void decode_tile(const Params &p, bool heavy_first, i
   tile = heavy_first ? p.n_tiles - 1 - rank : rank;
 }
 
+// Direct global -> LDS loads of one KV tile (K then V) into one LDS buffer.
+// Each wave-wide load writes 64 consecutive 16 B LDS slots; each lane fetches
+// the global chunk that the swizzled layout places in its slot.  The per-lane
+// part of the global offset (koff, voff: row lrow of the tile) is fixed for
+// the whole kernel; only the tile's start row changes.  In a tile that runs
+// past the end of the sequence the missing rows re-read the last row (finite
+// data; those keys are masked).
+template <int D, int BN>
+struct TileShape {
+  static constexpr int kTileBytes = BN * D * 2;
+  static constexpr int kLoads = kTileBytes / 1024 / kWaves;  // wave-wide loads per wave
+  static_assert(kLoads * 1024 * kWaves == kTileBytes, "tile must split evenly over waves");
+};
+
+template <int D, int BN>
+__device__ __forceinline__ void issue_tile(char *kb, char *vb, const uint16_t *kt0,
+                                           const uint16_t *vt0, const int64_t *koff,
+                                           const int64_t *voff, const int *lrow, int64_t k_ss,
+                                           int64_t v_ss, int rows_left) {
+  constexpr int kLoads = TileShape<D, BN>::kLoads;
+  if (rows_left >= BN) {
+#pragma unroll
+    for (int n = 0; n < kLoads; ++n) {
+      __builtin_amdgcn_global_load_lds(kt0 + koff[n], (lds_void_t *)(kb + n * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vt0 + voff[n], (lds_void_t *)(vb + n * 1024), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < kLoads; ++n) {
+      const int64_t back = min(rows_left - 1 - lrow[n], 0);  // rows to step back
+      __builtin_amdgcn_global_load_lds(kt0 + koff[n] + back * k_ss, (lds_void_t *)(kb + n * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vt0 + voff[n] + back * v_ss, (lds_void_t *)(vb + n * 1024), 16, 0, 0);
+    }
+  }
+}
+
 template <int D, bool CAUSAL, bool LIST>
 __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_fwd_kernel(Params p) {
   using L = Lds<D>;
@@ -146,8 +190,6 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_fwd_kernel(Pa
   constexpr int kBufBytes = 2 * kTileBytes;  // one K tile then one V tile
   constexpr int kQBytes = kBM * D * 2;
   constexpr int kSmem = kQBytes > 2 * kBufBytes ? kQBytes : 2 * kBufBytes;
-  constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 1 KB per wave-wide 16 B load
-  static_assert(kLoadsPerWave * 1024 * kWaves == kTileBytes, "tile must split evenly over waves");
   __shared__ __attribute__((aligned(1024))) char smem[kSmem];
 
   int tile, unit;
@@ -220,23 +262,22 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_fwd_kernel(Pa
 
   // Direct global -> LDS loads of one KV tile into buffer `buf`.  Each wave-wide
   // load writes 64 consecutive 16 B LDS slots; each lane fetches the global
-  // chunk that the swizzled layout places in its slot.  Rows past the end of
-  // the sequence re-read the last row (finite data; those keys are masked).
-  auto issue_tile = [&](int kv0, int buf) {
-    char *kb = smem + buf * kBufBytes;
-    char *vb = kb + kTileBytes;
+  // chunk that the swizzled layout places in its slot.  The per-lane part of
+  // the global offset is fixed for the whole kernel; only the tile's start row
+  // changes.  In a tile that runs past the end of the sequence the missing
+  // rows re-read the last row (finite data; those keys are masked).
+  constexpr int kLoads = TileShape<D, kBN>::kLoads;
+  int64_t koff[kLoads], voff[kLoads];
+  int lrow[kLoads];
+  const int slot_byte0 = wave * kLoads * 1024;  // this wave's first LDS slot in a tile
 #pragma unroll
-    for (int n = 0; n < kLoadsPerWave; ++n) {
-      const int slot0 = (wave * kLoadsPerWave + n) * 64;
-      const int slot = slot0 + lane;
-      const int r = slot / L::kChunks, pc = slot % L::kChunks;
-      const int64_t row = min(kv0 + r, len - 1);
-      const int ck = pc ^ L::kswz(r);
-      const int cv = (((pc >> 1) ^ L::vswz(r)) << 1) | (pc & 1);
-      __builtin_amdgcn_global_load_lds(kg + row * p.k_ss + ck * 8, (lds_void_t *)(kb + slot0 * 16), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vg + row * p.v_ss + cv * 8, (lds_void_t *)(vb + slot0 * 16), 16, 0, 0);
-    }
-  };
+  for (int n = 0; n < kLoads; ++n) {
+    const int slot = (wave * kLoads + n) * 64 + lane;
+    const int r = slot / L::kChunks, pc = slot % L::kChunks;
+    lrow[n] = r;
+    koff[n] = (int64_t)r * p.k_ss + (pc ^ L::kswz(r)) * 8;
+    voff[n] = (int64_t)r * p.v_ss + L::v_logical_chunk(r, pc) * 8;
+  }
 
   floatx16_t oacc[kDt];
 #pragma unroll
@@ -253,7 +294,9 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_fwd_kernel(Pa
   const int wq_last = q0 + wave * 32 + 31;
 
   int kv_cur = n_iter > 0 ? kv_start(0) : -1;
-  if (kv_cur >= 0) issue_tile(kv_cur, 0);
+  if (kv_cur >= 0)
+    issue_tile<D, kBN>(smem + slot_byte0, smem + kTileBytes + slot_byte0, kg + (int64_t)kv_cur * p.k_ss,
+                       vg + (int64_t)kv_cur * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_cur);
 
   for (int it = 0; it < n_iter; ++it) {
     // tile `it` has landed (every wave waited for its own loads); every wave is
@@ -263,7 +306,11 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_fwd_kernel(Pa
     int kv_nxt = -1;
     if (it + 1 < n_iter) {
       kv_nxt = kv_start(it + 1);
-      if (kv_nxt >= 0) issue_tile(kv_nxt, (it + 1) & 1);
+      if (kv_nxt >= 0) {
+        char *buf = smem + ((it + 1) & 1) * kBufBytes;
+        issue_tile<D, kBN>(buf + slot_byte0, buf + kTileBytes + slot_byte0, kg + (int64_t)kv_nxt * p.k_ss,
+                           vg + (int64_t)kv_nxt * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_nxt);
+      }
     }
     const int kv0 = kv_cur;
     kv_cur = kv_nxt;
@@ -303,7 +350,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_fwd_kernel(Pa
 #pragma unroll
     for (int kt = 0; kt < kKt; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kt][i], s[kt][i + 1]));
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[kt][i]), s[kt][i + 1]);
     mx = half_max(mx);
     const float mt = mx * p.c;
     const bool need = mt > m_run + kLazy;

@@ -97,6 +97,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mha", choices=list(W.CONFIG_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention forward here is a "
@@ -104,6 +106,20 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give the
+        # scale between those counters and bytes actually moved.
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.warmup + args.steps} copies of {n} bytes")
+        return
+
     import attention_forward_flashattention_amd as attn
     from tests import _parity as P
 
