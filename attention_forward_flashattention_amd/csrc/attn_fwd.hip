@@ -31,9 +31,6 @@ typedef __attribute__((ext_vector_type(2))) unsigned int uint2_t;
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kBM = 128;      // query rows per workgroup
-constexpr int kWaves = 4;     // wave64s per workgroup; each owns 32 query rows
-constexpr int kThreads = 64 * kWaves;
 constexpr int kListBlock = 128;  // block-list granularity (rows and keys)
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLazy = 8.f;  // log2 headroom before the running max is raised
@@ -92,10 +89,23 @@ struct Lds {
   }
 };
 
-// Keys per KV tile: 64, or 32 at head_dim 256 to bound registers and LDS.
-template <int D>
-struct KvTile {
+// Kernel configuration.  NW wave64s per workgroup, each owning 32 query rows
+// (BM = 32 * NW rows per workgroup); BN keys per KV tile (64, or 32 at head_dim
+// 256 to bound registers and LDS).  Dense and packed problems use 8 waves
+// (256-row tiles: every K/V tile staged in LDS serves 256 query rows); the
+// block-list kernel uses 4 waves so a workgroup covers exactly one 128-row
+// query block of the list.
+template <int D_, int NW_>
+struct Config {
+  static constexpr int D = D_;
+  static constexpr int NW = NW_;
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kBM = 32 * NW;
   static constexpr int kBN = D == 256 ? 32 : 64;
+  static constexpr int kTileBytes = kBN * D * 2;
+  static constexpr int kLoads = kTileBytes / 1024 / NW;  // wave-wide 16 B loads per wave per tile
+  static_assert(kLoads * 1024 * NW == kTileBytes, "tile must split evenly over waves");
+  static constexpr int kMinBlocks = (NW == 4 && D <= 128) ? 2 : 1;  // 2 waves per SIMD
 };
 
 __device__ __forceinline__ uint4_t ld_global16(const uint16_t *p) {
@@ -150,20 +160,13 @@ __device__ __forceinline__ void decode_tile(const Params &p, bool heavy_first, i
 // the whole kernel; only the tile's start row changes.  In a tile that runs
 // past the end of the sequence the missing rows re-read the last row (finite
 // data; those keys are masked).
-template <int D, int BN>
-struct TileShape {
-  static constexpr int kTileBytes = BN * D * 2;
-  static constexpr int kLoads = kTileBytes / 1024 / kWaves;  // wave-wide loads per wave
-  static_assert(kLoads * 1024 * kWaves == kTileBytes, "tile must split evenly over waves");
-};
-
-template <int D, int BN>
+template <class C>
 __device__ __forceinline__ void issue_tile(char *kb, char *vb, const uint16_t *kt0,
                                            const uint16_t *vt0, const int64_t *koff,
                                            const int64_t *voff, const int *lrow, int64_t k_ss,
                                            int64_t v_ss, int rows_left) {
-  constexpr int kLoads = TileShape<D, BN>::kLoads;
-  if (rows_left >= BN) {
+  constexpr int kLoads = C::kLoads;
+  if (rows_left >= C::kBN) {
 #pragma unroll
     for (int n = 0; n < kLoads; ++n) {
       __builtin_amdgcn_global_load_lds(kt0 + koff[n], (lds_void_t *)(kb + n * 1024), 16, 0, 0);
@@ -179,18 +182,18 @@ __device__ __forceinline__ void issue_tile(char *kb, char *vb, const uint16_t *k
   }
 }
 
-template <int D, bool CAUSAL, bool LIST>
-__global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_fwd_kernel(Params p) {
+template <class C, bool CAUSAL, bool LIST>
+__global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Params p) {
+  constexpr int D = C::D;
   using L = Lds<D>;
-  constexpr int kBN = KvTile<D>::kBN;
+  constexpr int kBM = C::kBM;
+  constexpr int kBN = C::kBN;
   constexpr int kDc = D / 16;   // MFMA k-steps over the head dimension
   constexpr int kDt = D / 32;   // 32-row output tiles over the head dimension
   constexpr int kKt = kBN / 32; // 32-key score tiles per KV tile
-  constexpr int kTileBytes = kBN * D * 2;
+  constexpr int kTileBytes = C::kTileBytes;
   constexpr int kBufBytes = 2 * kTileBytes;  // one K tile then one V tile
-  constexpr int kQBytes = kBM * D * 2;
-  constexpr int kSmem = kQBytes > 2 * kBufBytes ? kQBytes : 2 * kBufBytes;
-  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes];
 
   int tile, unit;
   decode_tile(p, CAUSAL || LIST, tile, unit);
@@ -219,25 +222,19 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_fwd_kernel(Pa
   const int hi = lane >> 5;  // lane half
   const int j16 = lane & 15;
 
-  // ---- Q tile: global -> LDS (coalesced 16 B chunks) -> registers (MFMA B operand)
-  {
-    constexpr int kChunksTotal = kBM * L::kChunks;
-    for (int id = tid; id < kChunksTotal; id += kThreads) {
-      const int r = id / L::kChunks, c = id % L::kChunks;
-      uint4_t x = {0u, 0u, 0u, 0u};
-      if (q0 + r < len) x = ld_global16(qg + (int64_t)(q0 + r) * p.q_ss + c * 8);
-      *reinterpret_cast<uint4_t *>(smem + L::kq(r, c)) = x;
-    }
-  }
-  __syncthreads();
+  // ---- Q rows of this wave straight into registers (MFMA B operand: lane
+  // l32 holds head-dim values 16*dc + 8*hi .. +7 of its row); rows past the
+  // end of the sequence read as zero
   bf16x8_t qreg[kDc];
   {
-    const int r = wave * 32 + l32;
+    const int r = q0 + wave * 32 + l32;
 #pragma unroll
-    for (int dc = 0; dc < kDc; ++dc)
-      qreg[dc] = *reinterpret_cast<const bf16x8_t *>(smem + L::kq(r, dc * 2 + hi));
+    for (int dc = 0; dc < kDc; ++dc) {
+      uint4_t x = {0u, 0u, 0u, 0u};
+      if (r < len) x = ld_global16(qg + (int64_t)r * p.q_ss + dc * 16 + hi * 8);
+      qreg[dc] = __builtin_bit_cast(bf16x8_t, x);
+    }
   }
-  __syncthreads();
 
   // ---- KV iteration space
   int n_iter;
@@ -266,7 +263,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_fwd_kernel(Pa
   // the global offset is fixed for the whole kernel; only the tile's start row
   // changes.  In a tile that runs past the end of the sequence the missing
   // rows re-read the last row (finite data; those keys are masked).
-  constexpr int kLoads = TileShape<D, kBN>::kLoads;
+  constexpr int kLoads = C::kLoads;
   int64_t koff[kLoads], voff[kLoads];
   int lrow[kLoads];
   const int slot_byte0 = wave * kLoads * 1024;  // this wave's first LDS slot in a tile
@@ -295,7 +292,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_fwd_kernel(Pa
 
   int kv_cur = n_iter > 0 ? kv_start(0) : -1;
   if (kv_cur >= 0)
-    issue_tile<D, kBN>(smem + slot_byte0, smem + kTileBytes + slot_byte0, kg + (int64_t)kv_cur * p.k_ss,
+    issue_tile<C>(smem + slot_byte0, smem + kTileBytes + slot_byte0, kg + (int64_t)kv_cur * p.k_ss,
                        vg + (int64_t)kv_cur * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_cur);
 
   for (int it = 0; it < n_iter; ++it) {
@@ -308,7 +305,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_fwd_kernel(Pa
       kv_nxt = kv_start(it + 1);
       if (kv_nxt >= 0) {
         char *buf = smem + ((it + 1) & 1) * kBufBytes;
-        issue_tile<D, kBN>(buf + slot_byte0, buf + kTileBytes + slot_byte0, kg + (int64_t)kv_nxt * p.k_ss,
+        issue_tile<C>(buf + slot_byte0, buf + kTileBytes + slot_byte0, kg + (int64_t)kv_nxt * p.k_ss,
                            vg + (int64_t)kv_nxt * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_nxt);
       }
     }
@@ -481,24 +478,28 @@ int validate(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t
     if (!cu_seqlens && !stride_ok(t->stride_batch)) return ATTN_ERR_UNSUPPORTED;
   }
   if (!empty) {
-    const int64_t tiles = (q->seqlen + kBM - 1) / kBM;
+    const int64_t tiles = (q->seqlen + 127) / 128;
     if (tiles * (int64_t)q->batch * q->heads > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
   }
   return ATTN_OK;
 }
 
-template <int D, bool CAUSAL, bool LIST>
-int launch(const Params &p, int64_t n_blocks, hipStream_t stream) {
-  void *args[] = {const_cast<Params *>(&p)};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<D, CAUSAL, LIST>),
-                                 dim3((unsigned)n_blocks), dim3(kThreads), args, 0, stream);
+template <class C, bool CAUSAL, bool LIST>
+int launch(Params p, hipStream_t stream) {
+  p.n_tiles = (p.seqlen + C::kBM - 1) / C::kBM;
+  const int64_t n_blocks = (int64_t)p.n_tiles * p.n_units;
+  void *args[] = {&p};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<C, CAUSAL, LIST>),
+                                 dim3((unsigned)n_blocks), dim3(C::kThreads), args, 0, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 template <int D>
-int launch_d(const Params &p, bool causal, bool list, int64_t n, hipStream_t s) {
-  if (list) return causal ? launch<D, true, true>(p, n, s) : launch<D, false, true>(p, n, s);
-  return causal ? launch<D, true, false>(p, n, s) : launch<D, false, false>(p, n, s);
+int launch_d(const Params &p, bool causal, bool list, hipStream_t s) {
+  using Dense = Config<D, D == 256 ? 4 : 8>;
+  using Listed = Config<D, 4>;
+  if (list) return causal ? launch<Listed, true, true>(p, s) : launch<Listed, false, true>(p, s);
+  return causal ? launch<Dense, true, false>(p, s) : launch<Dense, false, false>(p, s);
 }
 
 }  // namespace
@@ -535,17 +536,16 @@ extern "C" int attn_fwd(const attn_tensor_t *q, const attn_tensor_t *k, const at
   p.seqlen = q->seqlen;
   p.hq = q->heads;
   p.group = q->heads / k->heads;
-  p.n_tiles = (q->seqlen + kBM - 1) / kBM;
+  p.n_tiles = 0;  // set per configuration at launch
   p.n_units = q->batch * q->heads;
   p.xcd_remap = (p.n_units % 8) == 0 ? 1 : 0;
   p.c = scale * 1.44269504088896340736f;
-  const int64_t n = (int64_t)p.n_tiles * p.n_units;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool list = block_list != nullptr;
   switch (q->head_dim) {
-    case 64: return launch_d<64>(p, causal, list, n, s);
-    case 128: return launch_d<128>(p, causal, list, n, s);
-    default: return launch_d<256>(p, causal, list, n, s);
+    case 64: return launch_d<64>(p, causal, list, s);
+    case 128: return launch_d<128>(p, causal, list, s);
+    default: return launch_d<256>(p, causal, list, s);
   }
 }
 
