@@ -47,6 +47,9 @@ def load_library(path: str = LIB_PATH):
     """Load the HIP library (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        # torch ships its own HIP runtime; importing it first makes this library
+        # bind to the same runtime instance that owns torch's memory and streams
+        import torch  # noqa: F401
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build it with "
                                "`python -m attention_forward_flashattention_amd.build`")

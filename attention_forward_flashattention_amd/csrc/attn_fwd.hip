@@ -1,15 +1,18 @@
 // attn_fwd.hip — fused softmax-attention forward for AMD Instinct MI355X (gfx950).
 //
-// One workgroup computes a tile of BM = 128 query rows of one (sequence, query
-// head).  Four wave64s each own 32 of those rows and keep them in registers for
-// the whole kernel.  KV tiles of BN = 64 keys are streamed through LDS; for
-// each tile a wave computes the transposed score tile S^T = K Q^T with
-// 32x32x16 bf16 MFMAs, so that every lane holds the scores of ONE query row
-// (the softmax row statistics then need one exchange between the two lane
-// halves instead of a 32-lane reduction), runs the online softmax in base 2
-// with scale*log2(e) folded into one FMA, and accumulates O^T = V^T P^T with
-// the same MFMA, P staying in registers.  V^T operands come straight from the
-// row-major V tile with the gfx950 LDS transpose read (ds_read_b64_tr_b16).
+// One workgroup computes a tile of query rows of one (sequence, query head):
+// 256 rows in eight wave64s for dense and packed problems, 128 rows in four
+// wave64s for the block-list kernel (one query block of the list).  Each wave
+// owns 32 rows and keeps them in registers for the whole kernel.  KV tiles of
+// BN keys (64; 32 at head_dim 256) are streamed into double-buffered LDS with
+// direct global-to-LDS loads; for each tile a wave computes the transposed
+// score tile S^T = K Q^T with 32x32x16 bf16 MFMAs, so that every lane holds
+// the scores of ONE query row (the softmax row statistics then need one
+// exchange between the two lane halves instead of a 32-lane reduction), runs
+// the online softmax in base 2 with scale*log2(e) folded into one FMA, and
+// accumulates O^T = V^T P^T with the same MFMA, P staying in registers.  V^T
+// operands come straight from the row-major V tile with the gfx950 LDS
+// transpose read (ds_read_b64_tr_b16).
 //
 // The computation is the softmax attention that FlashAttention-style kernels
 // evaluate tile by tile in on-chip memory (AdaSplash-2 explainer, technical
@@ -133,19 +136,23 @@ __device__ __forceinline__ float half_sum(float x) {
 }
 
 // Decode the workgroup id into (query tile, sequence, head).  Workgroups are
-// dealt round-robin over the 8 XCDs; when the (sequence, head) units divide
-// evenly, each XCD gets a contiguous range of units so that the query heads
-// that share a KV head (and all tiles of a head) share that XCD's L2.
-// Causal and block-list tiles are issued heaviest first.
+// dealt round-robin over the 8 XCDs (each with its own L2).  When the
+// (sequence, head) units split evenly, the `group` query heads that share one
+// KV head stay together and those groups are dealt round-robin over the XCDs,
+// so every XCD gets the same mix of sequences (packed batches stay balanced)
+// and the heads that read the same K/V share one L2.  Within an XCD, causal
+// and block-list tiles are issued heaviest first.
 __device__ __forceinline__ void decode_tile(const Params &p, bool heavy_first, int &tile,
                                             int &unit) {
   const int w = blockIdx.x;
   int rank;
   if (p.xcd_remap) {
-    const int upx = p.n_units >> 3;
+    const int upx = p.n_units >> 3;  // units per XCD
+    const int xcd = w & 7;
     const int local = w >> 3;
     rank = local / upx;
-    unit = (w & 7) * upx + local % upx;
+    const int lu = local % upx;      // unit slot within this XCD
+    unit = ((lu / p.group) * 8 + xcd) * p.group + lu % p.group;
   } else {
     rank = w / p.n_units;
     unit = w % p.n_units;
@@ -357,9 +364,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < kDt; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+      for (int dt = 0; dt < kDt; ++dt) oacc[dt] = oacc[dt] * alpha;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float rs = 0.f;
@@ -538,7 +543,7 @@ extern "C" int attn_fwd(const attn_tensor_t *q, const attn_tensor_t *k, const at
   p.group = q->heads / k->heads;
   p.n_tiles = 0;  // set per configuration at launch
   p.n_units = q->batch * q->heads;
-  p.xcd_remap = (p.n_units % 8) == 0 ? 1 : 0;
+  p.xcd_remap = (p.n_units % (8 * p.group)) == 0 ? 1 : 0;
   p.c = scale * 1.44269504088896340736f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool list = block_list != nullptr;
