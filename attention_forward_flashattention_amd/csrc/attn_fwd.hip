@@ -22,17 +22,18 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "attn_fwd.h"
 
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) short short4_t;
 typedef __attribute__((ext_vector_type(16))) float floatx16_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int uint4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned int uint2_t;
-typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
 
 constexpr int kListBlock = 128;  // block-list granularity (rows and keys)
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -110,6 +111,52 @@ struct Config {
   static_assert(kLoads * 1024 * NW == kTileBytes, "tile must split evenly over waves");
   static constexpr int kMinBlocks = (NW == 4 && D <= 128) ? 2 : 1;  // 2 waves per SIMD
 };
+
+// Compile-time LDS buffer index of a main-loop step.
+template <int B>
+struct BufTag {
+  static constexpr int value = B;
+};
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, so that i can be
+// used as a template argument (immediate offsets of inline assembly).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Byte offset (within a V tile) of the rows read by PV step i: dt = i % kDt,
+// (kt, c) = i / kDt; a step reads 16 keys starting at key 32 kt + 16 c.
+template <class L, int kDt>
+__host__ __device__ constexpr int tr_off(int i) {
+  return ((i / kDt) >> 1) * 32 * L::kRowBytes + ((i / kDt) & 1) * 16 * L::kRowBytes;
+}
+
+// Two LDS transpose reads (rows +0 and +kRow8 bytes apart: keys +0..7 and
+// +8..15 of a 16-key group) forming one MFMA A operand.  Written as inline
+// assembly: the compiler builtin for this read makes the compiler wait for every direct
+// global-to-LDS load in flight before it (the prefetch of the next tile),
+// which the double-buffered layout never needs.  The caller waits for the
+// result with lgkm_wait before using it.
+template <int kOff, int kRow8>
+__device__ __forceinline__ bf16x8_t tr_pair(uint32_t addr) {
+  uint2_t lo, hi;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(addr), "i"(kOff));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(addr), "i"(kOff + kRow8));
+  const uint4_t packed = {lo.x, lo.y, hi.x, hi.y};
+  return __builtin_bit_cast(bf16x8_t, packed);
+}
+
+// Wait until at most N LDS operations are outstanding; `x` is tied through so
+// its uses cannot move above the wait.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(bf16x8_t &x) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
+}
 
 __device__ __forceinline__ uint4_t ld_global16(const uint16_t *p) {
   return *reinterpret_cast<const uint4_t *>(p);
@@ -302,7 +349,28 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     issue_tile<C>(smem + slot_byte0, smem + kTileBytes + slot_byte0, kg + (int64_t)kv_cur * p.k_ss,
                        vg + (int64_t)kv_cur * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_cur);
 
-  for (int it = 0; it < n_iter; ++it) {
+  // Per-lane LDS byte offsets of the MFMA operand reads within a tile.  The
+  // swizzles depend only on a row's position within 32 rows (K) and within 4
+  // rows (V), so every other read is one of these plus a compile-time row
+  // offset.  The empty asm keeps each offset in one register (otherwise the
+  // compiler re-splits it into row and chunk parts and re-adds them per read).
+  int kaddr[kDc], vaddr[kDt];
+  uint32_t vlds[kDt];
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char_t *)smem;
+#pragma unroll
+  for (int dc = 0; dc < kDc; ++dc) {
+    kaddr[dc] = L::kq(l32, dc * 2 + hi);
+    asm volatile("" : "+v"(kaddr[dc]));
+  }
+#pragma unroll
+  for (int dt = 0; dt < kDt; ++dt) {
+    vaddr[dt] = L::vv(4 * hi + (j16 >> 2), 2 * dt + (l32 >> 4), (j16 & 3) * 8);
+    asm volatile("" : "+v"(vaddr[dt]));
+    vlds[dt] = smem_lds + (uint32_t)vaddr[dt];
+  }
+
+  auto step = [&](const int it, auto buf_tag) {
+    constexpr int kBuf = decltype(buf_tag)::value;  // LDS buffer of tile `it` (= it % 2)
     // tile `it` has landed (every wave waited for its own loads); every wave is
     // done reading the other buffer
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -311,28 +379,41 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     if (it + 1 < n_iter) {
       kv_nxt = kv_start(it + 1);
       if (kv_nxt >= 0) {
-        char *buf = smem + ((it + 1) & 1) * kBufBytes;
+        char *buf = smem + (1 - kBuf) * kBufBytes;
         issue_tile<C>(buf + slot_byte0, buf + kTileBytes + slot_byte0, kg + (int64_t)kv_nxt * p.k_ss,
                            vg + (int64_t)kv_nxt * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_nxt);
       }
     }
     const int kv0 = kv_cur;
     kv_cur = kv_nxt;
-    if (kv0 < 0) continue;
-    if (CAUSAL && kv0 > wq_last) continue;  // whole tile above this wave's rows
-    const char *sK = smem + (it & 1) * kBufBytes;
+    if (kv0 < 0) return;
+    if (CAUSAL && kv0 > wq_last) return;  // whole tile above this wave's rows
+    const char *sK = smem + kBuf * kBufBytes;
     const char *sV = sK + kTileBytes;
 
     // ---- S^T = K Q^T : kKt tiles of 32 keys x 32 query rows
     floatx16_t s[kKt];
+    {
+      // LDS operand reads run kRing MFMAs ahead of their use, and consecutive
+      // MFMAs alternate between the kKt independent accumulators, so neither
+      // the LDS latency nor the MFMA dependency latency is exposed
+      constexpr int kRing = 4;
+      constexpr int kSteps = kKt * kDc;  // step i: kt = i % kKt, dc = i / kKt
+      auto load = [&](int i) {
+        return *reinterpret_cast<const bf16x8_t *>(sK + kaddr[i / kKt] + (i % kKt) * 32 * L::kRowBytes);
+      };
+      bf16x8_t ring[kRing];
 #pragma unroll
-    for (int kt = 0; kt < kKt; ++kt) {
+      for (int i = 0; i < kRing; ++i) ring[i] = load(i);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
-#pragma unroll
-      for (int dc = 0; dc < kDc; ++dc) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(sK + L::kq(kt * 32 + l32, dc * 2 + hi));
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], s[kt], 0, 0, 0);
+      for (int i = 0; i < kSteps; ++i) {
+        const int kt = i % kKt, dc = i / kKt;
+        if (dc == 0)
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], floatx16_t{}, 0, 0, 0);
+        else
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], s[kt], 0, 0, 0);
+        if (i + kRing < kSteps) ring[i % kRing] = load(i + kRing);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -382,28 +463,36 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     // ---- O^T += V^T P^T.  MFMA k index (8 per lane half) maps to keys
     // 16c + 8(e/4) + 4*hi + (e%4) of a 32-key tile, matching where the score
     // layout left P; V^T operands are read with the LDS transpose.
-#pragma unroll
-    for (int dt = 0; dt < kDt; ++dt) {
-      const int u = (dt * 32 + ((l32 >> 4) << 4)) >> 4;  // 32 B unit of this lane group's 16 columns
-#pragma unroll
-      for (int kt = 0; kt < kKt; ++kt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int key0 = kt * 32 + 16 * c + 4 * hi + (j16 >> 2);
-          const int boff = (j16 & 3) * 8;
-          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_short4_t *)(sV + L::vv(key0, u, boff)));
-          const short4_t hi8 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_short4_t *)(sV + L::vv(key0 + 8, u, boff)));
-          // whole-register reinterpretation (per-element inserts were lowered to
-          // byte permutes that duplicated elements)
-          const uint2_t lo2 = __builtin_bit_cast(uint2_t, lo);
-          const uint2_t hi2 = __builtin_bit_cast(uint2_t, hi8);
-          const uint4_t packed = {lo2.x, lo2.y, hi2.x, hi2.y};
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, packed);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][c], oacc[dt], 0, 0, 0);
-        }
+    {
+      // same operand ring as for S; consecutive MFMAs alternate between the
+      // kDt output accumulators
+      constexpr int kRing = 4;
+      constexpr int kSteps = kDt * kKt * 2;  // step i: dt = i % kDt, (kt, c) = i / kDt
+      constexpr int kVOff = kBuf * kBufBytes + kTileBytes;  // V tile of this buffer
+      bf16x8_t ring[kRing];
+      static_for<kRing>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        ring[i] = tr_pair<kVOff + tr_off<L, kDt>(i), 8 * L::kRowBytes>(vlds[i % kDt]);
+      });
+      static_for<kSteps>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int dt = i % kDt, kc = i / kDt, kt = kc >> 1, c = kc & 1;
+        // the reads of step i are done once at most the reads issued after
+        // them are outstanding (LDS reads complete in order)
+        lgkm_wait<2 * (kSteps - 1 - i < kRing - 1 ? kSteps - 1 - i : kRing - 1)>(ring[i % kRing]);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], pb[kt][c], oacc[dt], 0, 0, 0);
+        if constexpr (i + kRing < kSteps)
+          ring[i % kRing] = tr_pair<kVOff + tr_off<L, kDt>(i + kRing), 8 * L::kRowBytes>(vlds[(i + kRing) % kDt]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
+  };
+  // two tiles per trip so that each step's LDS buffer is a compile-time constant
+  // (every LDS operand address is then a loop-invariant lane offset plus an
+  // immediate)
+  for (int it = 0; it < n_iter; it += 2) {
+    step(it, BufTag<0>{});
+    if (it + 1 < n_iter) step(it + 1, BufTag<1>{});
   }
 
   // ---- epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log
