@@ -93,8 +93,11 @@ def cpu_baseline(w: W.Workload, budget_s: float = 20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed back-to-back launches for this long before the warm-up steps "
+                         "(the GPU clock takes tens of milliseconds of load to reach its sustained level)")
     ap.add_argument("--workload", default="mha", choices=list(W.CONFIG_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -136,6 +139,16 @@ def main():
         attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale, block_list=bl, out=out,
                       lse=lse, max_seqlen=w.seqlen if cu is not None else None)
 
+    # Settle the clock: the GPU ramps its engine clock over the first tens of
+    # milliseconds of load; without this the timed steps of a short kernel run
+    # partly at a lower clock than the sustained one.
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        step()
+        n_settle += 1
+        if n_settle % 16 == 0:
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -166,7 +179,7 @@ def main():
     per_launch = [a.elapsed_time(b) for a, b in evs]
     log(f"workload {w.name}: {flops / 1e9:.2f} GFLOP/launch, {ms_per_step * 1e3:.1f} us/step back to back "
         f"(single launches: median {np.median(per_launch) * 1e3:.1f} us, min {min(per_launch) * 1e3:.1f} us), "
-        f"wall {wall * 1e3 / args.steps:.1f} us/step, {tflops:.1f} TFLOP/s = "
+        f"wall {wall * 1e6 / args.steps:.1f} us/step, {n_settle} settle launches, {tflops:.1f} TFLOP/s = "
         f"{100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
 
     cpu = None
