@@ -32,6 +32,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float floatx16_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int uint4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned int uint2_t;
+typedef __attribute__((ext_vector_type(2))) float floatx2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
@@ -247,7 +249,11 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   constexpr int kKt = kBN / 32; // 32-key score tiles per KV tile
   constexpr int kTileBytes = C::kTileBytes;
   constexpr int kBufBytes = 2 * kTileBytes;  // one K tile then one V tile
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes];
+  // With one workgroup per CU the O staging area of the epilogue has LDS of its
+  // own, so a wave can write out its rows while others still read K/V.
+  constexpr bool kOwnStage = C::kMinBlocks == 1;
+  constexpr int kStageBytes = C::NW * 32 * D * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes + (kOwnStage ? kStageBytes : 0)];
 
   int tile, unit;
   decode_tile(p, CAUSAL || LIST, tile, unit);
@@ -275,20 +281,6 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   const int l32 = lane & 31;
   const int hi = lane >> 5;  // lane half
   const int j16 = lane & 15;
-
-  // ---- Q rows of this wave straight into registers (MFMA B operand: lane
-  // l32 holds head-dim values 16*dc + 8*hi .. +7 of its row); rows past the
-  // end of the sequence read as zero
-  bf16x8_t qreg[kDc];
-  {
-    const int r = q0 + wave * 32 + l32;
-#pragma unroll
-    for (int dc = 0; dc < kDc; ++dc) {
-      uint4_t x = {0u, 0u, 0u, 0u};
-      if (r < len) x = ld_global16(qg + (int64_t)r * p.q_ss + dc * 16 + hi * 8);
-      qreg[dc] = __builtin_bit_cast(bf16x8_t, x);
-    }
-  }
 
   // ---- KV iteration space
   int n_iter;
@@ -348,6 +340,21 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   if (kv_cur >= 0)
     issue_tile<C>(smem + slot_byte0, smem + kTileBytes + slot_byte0, kg + (int64_t)kv_cur * p.k_ss,
                        vg + (int64_t)kv_cur * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_cur);
+
+  // ---- Q rows of this wave straight into registers (MFMA B operand: lane
+  // l32 holds head-dim values 16*dc + 8*hi .. +7 of its row); rows past the
+  // end of the sequence read as zero.  Loaded after the first K/V tile is
+  // issued, so that the two latencies overlap.
+  bf16x8_t qreg[kDc];
+  {
+    const int r = q0 + wave * 32 + l32;
+#pragma unroll
+    for (int dc = 0; dc < kDc; ++dc) {
+      uint4_t x = {0u, 0u, 0u, 0u};
+      if (r < len) x = ld_global16(qg + (int64_t)r * p.q_ss + dc * 16 + hi * 8);
+      qreg[dc] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
 
   // Per-lane LDS byte offsets of the MFMA operand reads within a tile.  The
   // swizzles depend only on a row's position within 32 rows (K) and within 4
@@ -495,24 +502,53 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     if (it + 1 < n_iter) step(it + 1, BufTag<1>{});
   }
 
-  // ---- epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log
+  // ---- epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log.
+  // O goes out through LDS: each wave writes its 32 x D tile there (16 B
+  // chunks XOR-swizzled by row) and reads it back so that 16 consecutive
+  // lanes store one whole row with 16-byte stores (the accumulator layout
+  // would otherwise store 8 bytes per lane into 32 different rows at a time).
   const float l_tot = half_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < len) {
-    uint16_t *orow = og + (int64_t)qrow * p.o_ss;
+  if (!kOwnStage) __syncthreads();  // every wave is done with the K/V buffers
+  {
+    constexpr int kRowB = D * 2;           // bytes per O row
+    constexpr int kCh = D / 8;             // 16 B chunks per row
+    constexpr int kRowsPerStore = 1024 / kRowB;
+    char *so = smem + (kOwnStage ? 2 * kBufBytes : 0) + wave * 32 * kRowB;
 #pragma unroll
     for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = dt * 32 + g4 * 8 + hi * 4;
-        __bf16 o4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[dt][g4 * 4 + e] * inv);
-        uint2 w;
-        w.x = (uint32_t)__builtin_bit_cast(uint16_t, o4[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o4[1]) << 16);
-        w.y = (uint32_t)__builtin_bit_cast(uint16_t, o4[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, o4[3]) << 16);
-        *reinterpret_cast<uint2 *>(orow + d) = w;
+        const floatx2_t f01 = {oacc[dt][g4 * 4 + 0] * inv, oacc[dt][g4 * 4 + 1] * inv};
+        const floatx2_t f23 = {oacc[dt][g4 * 4 + 2] * inv, oacc[dt][g4 * 4 + 3] * inv};
+        uint2_t w;
+        w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f01, bf16x2_t));
+        w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f23, bf16x2_t));
+        const int ch = (dt * 4 + g4) ^ (l32 % kCh);
+        *reinterpret_cast<uint2_t *>(so + l32 * kRowB + ch * 16 + hi * 8) = w;
       }
+    constexpr int kStores = 32 / kRowsPerStore;
+    const int r0 = lane / kCh;  // row (within the wave's 32) of this lane's first store
+    const int ch = lane % kCh;
+    uint4_t x[kStores];
+#pragma unroll
+    for (int k = 0; k < kStores; ++k) {
+      const int r = k * kRowsPerStore + r0;
+      x[k] = *reinterpret_cast<const uint4_t *>(so + r * kRowB + ((ch ^ (r % kCh)) * 16));
+    }
+    uint16_t *orow = og + (int64_t)(q0 + wave * 32 + r0) * p.o_ss + ch * 8;
+    const int64_t step_rows = (int64_t)kRowsPerStore * p.o_ss;
+    if (q0 + wave * 32 + 32 <= len) {
+#pragma unroll
+      for (int k = 0; k < kStores; ++k) *reinterpret_cast<uint4_t *>(orow + k * step_rows) = x[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < kStores; ++k)
+        if (q0 + wave * 32 + k * kRowsPerStore + r0 < len)
+          *reinterpret_cast<uint4_t *>(orow + k * step_rows) = x[k];
+    }
+  }
+  if (qrow < len) {
     if (p.lse && hi == 0) {
       const float v = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
       int64_t idx;
