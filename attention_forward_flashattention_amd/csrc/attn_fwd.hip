@@ -39,7 +39,9 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 
 constexpr int kListBlock = 128;  // block-list granularity (rows and keys)
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLazy = 8.f;  // log2 headroom before the running max is raised
+// A tile's P is accepted against the running max while every row sum of the
+// tile stays at or below this (so every P is at most 2^12).
+constexpr float kFastSum = 4096.f;
 // s_waitcnt immediate that waits for vmcnt == 0 and leaves the other counters
 // free (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
@@ -182,6 +184,23 @@ __device__ __forceinline__ float half_sum(float x) {
   float a, b;
   half_pair(x, a, b);
   return a + b;
+}
+
+// P = 2^(c s - m) for one tile of scores, rounded to bf16 in the MFMA
+// operand layout; returns this lane's sum of the unrounded P.
+template <int kKt>
+__device__ __forceinline__ float exp_tile(const floatx16_t (&s)[kKt], float c, float m,
+                                          bf16x8_t (&pb)[kKt][2]) {
+  float rs = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < kKt; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c, -m));
+      rs += pv;
+      pb[kt][i >> 3][i & 7] = (__bf16)pv;
+    }
+  return rs;
 }
 
 // Decode the workgroup id into (query tile, sequence, head).  Workgroups are
@@ -328,8 +347,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
   // Running max of c*s for this lane's row (c = scale*log2 e).  It is raised
-  // lazily: only when a tile's max exceeds it by more than kLazy, so P values
-  // stay below 2^kLazy and most tiles skip the rescale of O.
+  // lazily (see the softmax step below), so most tiles neither take the
+  // tile's max nor rescale O.
   float m_run = -INFINITY;
   float l_run = 0.f;  // running sum over this lane's half of the keys
 
@@ -376,6 +395,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     vlds[dt] = smem_lds + (uint32_t)vaddr[dt];
   }
 
+  bool first = true;  // no tile processed yet by this wave
   auto step = [&](const int it, auto buf_tag) {
     constexpr int kBuf = decltype(buf_tag)::value;  // LDS buffer of tile `it` (= it % 2)
     // tile `it` has landed (every wave waited for its own loads); every wave is
@@ -437,34 +457,37 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         }
     }
 
-    // ---- online softmax (base 2, scale folded into c)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < kKt; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[kt][i]), s[kt][i + 1]);
-    mx = half_max(mx);
-    const float mt = mx * p.c;
-    const bool need = mt > m_run + kLazy;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_new = need ? mt : m_run;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < kDt; ++dt) oacc[dt] = oacc[dt] * alpha;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float rs = 0.f;
+    // ---- online softmax (base 2, scale folded into c).  P is first computed
+    // against the running max as it stands; the tile's own max is taken only
+    // on the wave's first tile or when some row sum exceeds kFastSum (a score
+    // well above the running max).  Then the max is raised to the tile's,
+    // O and l are rescaled and P is computed again.
     bf16x8_t pb[kKt][2];
+    float rs = 0.f;
+    bool slow = first;
+    if (!first) {
+      rs = exp_tile(s, p.c, m_run == -INFINITY ? 0.f : m_run, pb);
+      slow = __builtin_amdgcn_ballot_w64(rs > kFastSum) != 0;
+    }
+    first = false;
+    if (slow) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < kKt; ++kt)
+      for (int kt = 0; kt < kKt; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], p.c, -m_use));
-        rs += pv;
-        pb[kt][i >> 3][i & 7] = (__bf16)pv;
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[kt][i]), s[kt][i + 1]);
+      const float mt = half_max(mx) * p.c;
+      const bool need = mt > m_run;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? mt : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt) oacc[dt] = oacc[dt] * alpha;
       }
+      rs = exp_tile(s, p.c, m_run == -INFINITY ? 0.f : m_run, pb);
+    }
     l_run += rs;
 
     // ---- O^T += V^T P^T.  MFMA k index (8 per lane half) maps to keys

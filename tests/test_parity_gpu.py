@@ -202,6 +202,20 @@ def test_large_scores_shifted_keys():
     note(f"  {stats}")
 
 
+def test_late_large_score_raises_running_max():
+    """A key late in the sequence scores far above every earlier key (P would be
+    ~2^50 against the running max): the kernel must raise the max and rescale O
+    and l mid-row.  Q is positive so that key 700 wins in every row that sees it."""
+    w = W.make_dense("late", 22, 1, 1024, 4, 2, 128, True)
+    qf = np.abs(W.bf16_bits_to_f32(w.q))
+    w.q = W.f32_to_bf16_bits(qf)
+    kf = W.bf16_bits_to_f32(w.k)
+    kf[0, 700] = 4.0
+    w.k = W.f32_to_bf16_bits(kf)
+    stats = P.check_workload(w)
+    note(f"  {stats}")
+
+
 def test_deterministic():
     w = W.make_dense("det", 21, 2, 700, 8, 2, 128, True)
     t = P.to_device(w)
