@@ -100,6 +100,8 @@ def main():
                          "(the GPU clock takes tens of milliseconds of load to reach its sustained level)")
     ap.add_argument("--workload", default="mha", choices=list(W.CONFIG_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="launches timed one by one after evicting the caches (secondary figure)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -182,6 +184,49 @@ def main():
         f"wall {wall * 1e6 / args.steps:.1f} us/step, {n_settle} settle launches, {tflops:.1f} TFLOP/s = "
         f"{100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
 
+    # Cold-cache launches (secondary): a 512 MiB write evicts L2 and the 256 MiB
+    # Infinity Cache before each launch, outside the timed events.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=q.device)
+    cold = []
+    for _ in range(args.cold_reps):
+        scratch.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del scratch
+    extra = {}
+    if cold:
+        extra["cold_cache_ms_median"] = round(float(np.median(cold)), 5)
+        extra["cold_cache_ms_min"] = round(float(min(cold)), 5)
+        log(f"cold cache (L2 and Infinity Cache evicted before each launch): median {np.median(cold) * 1e3:.1f} us, "
+            f"min {min(cold) * 1e3:.1f} us over {len(cold)} launches")
+
+    if bl is not None:
+        # block-sparse speedup: the dense causal launch on the same inputs
+        def dense():
+            attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale, block_list=None, out=out,
+                          lse=lse, max_seqlen=w.seqlen if cu is not None else None)
+        dense()
+        torch.cuda.synchronize()
+        n_dense = max(2, args.steps // 20)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_dense):
+            dense()
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / n_dense
+        wd = W.Workload(w.name, w.seed, w.batch, w.seqlen, w.hq, w.hkv, w.d, w.causal, w.scale, w.q, w.k, w.v)
+        ideal = W.counted_flops(wd) / flops
+        extra["dense_causal_ms_per_step"] = round(dense_ms, 4)
+        extra["sparse_speedup"] = round(dense_ms / ms_per_step, 3)
+        extra["sparse_speedup_ideal"] = round(ideal, 3)
+        log(f"dense causal on the same inputs: {dense_ms:.2f} ms/step; block-sparse speedup "
+            f"{dense_ms / ms_per_step:.2f}x (ideal {ideal:.2f}x)")
+
     cpu = None
     if not args.no_cpu_baseline and not w.packed and w.row_ptr is None:
         cpu = cpu_baseline(w)
@@ -204,7 +249,7 @@ def main():
                    if w.name == "mha" else w.name,
                    "batch": w.batch, "seq_len": w.seqlen, "heads_q": w.hq, "heads_kv": w.hkv,
                    "head_dim": w.d, "causal": w.causal, "flops_per_step": flops,
-                   "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)},
+                   "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), **extra},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic()},
