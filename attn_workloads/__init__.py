@@ -97,6 +97,7 @@ class Workload:
     row_ptr: Optional[np.ndarray] = None         # int32 [n_qblk+1] block list (CSR)
     col_idx: Optional[np.ndarray] = None         # int32 [nnz], visiting order
     sample_rows: Optional[np.ndarray] = None     # int64 token positions checked one by one
+    block_mask: Optional[np.ndarray] = None      # uint32 [n_seqs|1, Hkv|1, n_qblk, words] bit mask
 
     @property
     def packed(self) -> bool:
@@ -191,6 +192,29 @@ def full_causal_list(n_qblk: int, shuffle_seed: Optional[int] = None):
     return row_ptr, np.concatenate(rows).astype(np.int32)
 
 
+def list_visibility(row_ptr: np.ndarray, col_idx: np.ndarray, n_kblk: int) -> np.ndarray:
+    """bool [n_qblk, n_kblk]: True where a CSR block list names KV block kb for query block qb."""
+    n_qblk = len(row_ptr) - 1
+    vis = np.zeros((n_qblk, n_kblk), dtype=bool)
+    for qb in range(n_qblk):
+        ids = col_idx[row_ptr[qb]:row_ptr[qb + 1]]
+        ids = ids[(ids >= 0) & (ids < n_kblk)]
+        vis[qb, ids] = True
+    return vis
+
+
+def pack_block_mask(visible: np.ndarray) -> np.ndarray:
+    """Bit-pack a block visibility matrix: bool [..., n_qblk, n_kblk] -> uint32
+    [..., n_qblk, ceil(n_kblk/32)], KV block kb in bit kb % 32 of word kb // 32."""
+    visible = np.asarray(visible, dtype=bool)
+    n_k = visible.shape[-1]
+    words = (n_k + 31) // 32
+    padded = np.zeros(visible.shape[:-1] + (words * 32,), dtype=bool)
+    padded[..., :n_k] = visible
+    bits = padded.reshape(visible.shape[:-1] + (words, 32)).astype(np.uint64)
+    return (bits << np.arange(32, dtype=np.uint64)).sum(axis=-1).astype(np.uint32)
+
+
 def sample_positions(gen: np.random.Generator, s: int, n: int = 256) -> np.ndarray:
     """n distinct positions: {0, 127, 128, S-1} plus the rest drawn without replacement."""
     fixed = sorted({p for p in (0, 127, 128, s - 1) if 0 <= p < s})
@@ -239,11 +263,31 @@ def make_sparse(name, seed, s, hq, hkv, d, budget=0.10, n_sample=256) -> Workloa
                     sample_rows=sample_positions(g["sample_rows"], s, n_sample))
 
 
-CONFIG_NAMES = ("tiny", "mha", "gqa", "varlen_d64", "varlen_d128", "varlen_d256", "sparse")
+def make_sparse_mask(name, seed, s, hq, hkv, d, budget=0.10, n_sample=256) -> Workload:
+    """The block-sparse workload with a separate block set per KV head, given as
+    a bit-packed mask [1, Hkv, n_qblk, words].  Each KV head's set follows the
+    rule of ``build_block_list`` with its own seeded block scores."""
+    g = streams(seed)
+    n_qblk = (s + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    scores = g["block_scores"].random(size=(hkv, n_qblk, n_qblk))
+    vis = np.zeros((1, hkv, n_qblk, n_qblk), dtype=bool)
+    for c in range(hkv):
+        row_ptr, col_idx = build_block_list(n_qblk, scores[c], budget)
+        vis[0, c] = list_visibility(row_ptr, col_idx, n_qblk)
+    return Workload(name=name, seed=seed, batch=1, seqlen=s, hq=hq, hkv=hkv, d=d, causal=True,
+                    scale=default_scale(d),
+                    q=normal_bf16(g["q"], (1, s, hq, d)), k=normal_bf16(g["k"], (1, s, hkv, d)),
+                    v=normal_bf16(g["v"], (1, s, hkv, d)), block_mask=pack_block_mask(vis),
+                    sample_rows=sample_positions(g["sample_rows"], s, n_sample))
+
+
+CONFIG_NAMES = ("tiny", "mha", "gqa", "varlen_d64", "varlen_d128", "varlen_d256", "sparse",
+                "sparse_mask")
 
 
 def make(name: str) -> Workload:
-    """Build one of the named workloads (seed 1..5 in the order tiny, mha, gqa, varlen, sparse)."""
+    """Build one of the named workloads (seed 1..6 in the order tiny, mha, gqa, varlen, sparse,
+    sparse_mask)."""
     if name == "tiny":
         return make_dense("tiny", 1, 1, 128, 2, 2, 64, False)
     if name == "mha":
@@ -255,6 +299,8 @@ def make(name: str) -> Workload:
         return make_varlen(name, 4, varlen_lengths(4), 32, 8, d, True)
     if name == "sparse":
         return make_sparse("sparse", 5, 131072, 32, 8, 128)
+    if name == "sparse_mask":
+        return make_sparse_mask("sparse_mask", 6, 131072, 32, 8, 128)
     raise KeyError(name)
 
 
@@ -274,6 +320,22 @@ def counted_flops(w: Workload) -> float:
     and half of that for the diagonal block.  Skipped blocks count nothing.
     """
     per_pair = 4.0 * w.d * w.hq
+    if w.block_mask is not None:
+        # per (sequence, kv head) set, counted for each of its g query heads
+        m = w.block_mask
+        vis = np.unpackbits(np.ascontiguousarray(m).view(np.uint8), axis=-1, bitorder="little")
+        n_qblk = m.shape[2]
+        vis = vis[..., :n_qblk].astype(bool)          # [S|1, H|1, n_qblk, n_kblk]
+        qb = np.arange(n_qblk)[:, None]
+        kb = np.arange(n_qblk)[None, :]
+        if w.causal:
+            w_blk = np.where(kb < qb, 1.0, np.where(kb == qb, 0.5, 0.0))
+        else:
+            w_blk = np.ones((n_qblk, n_qblk))
+        per_set = (vis * w_blk).sum(axis=(-1, -2))     # [S|1, H|1]
+        per_set = np.broadcast_to(per_set, (max(1, m.shape[0]), w.hkv))
+        g = w.hq // w.hkv
+        return 4.0 * w.d * g * SPARSE_BLOCK * SPARSE_BLOCK * float(per_set.sum())
     if w.row_ptr is not None:
         n_q = np.repeat(np.arange(len(w.row_ptr) - 1), np.diff(w.row_ptr))
         diag = int(np.sum(w.col_idx == n_q))

@@ -48,6 +48,12 @@ def _load():
                                         ctypes.c_int, ctypes.c_int, ctypes.c_double, P, P,
                                         ctypes.c_int, ctypes.c_int, P, ctypes.c_int64, P, P, P,
                                         ctypes.c_int]
+        lib.oracle_attn_fwd_mask.restype = ctypes.c_int
+        lib.oracle_attn_fwd_mask.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_double, P,
+                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, P, ctypes.c_int64, P, P,
+                                             P, ctypes.c_int]
         lib.oracle_default_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -62,12 +68,16 @@ def _ptr(a: Optional[np.ndarray]):
 
 
 def attn_fwd(q, k, v, cu_seqlens, causal: bool, scale: float, row_ptr=None, col_idx=None,
-             block: int = 128, rows=None, nthreads: int = 0, with_psum: bool = False):
+             block: int = 128, rows=None, nthreads: int = 0, with_psum: bool = False,
+             block_mask=None):
     """Exact attention forward.
 
     q:  float64 [T, Hq, D] (all tokens) or [len(rows), Hq, D] when ``rows`` is given
     k, v: float64 [T, Hkv, D];  cu_seqlens: int [n+1]
     row_ptr/col_idx: optional block list (single sequence only), ``block`` rows per block
+    block_mask: optional uint32 [n_seqs or 1, Hkv or 1, n_qblk, words] bit-packed
+        block mask (bit kb%32 of word kb//32: KV block kb visible); a size-1
+        leading dimension is shared by every sequence / kv head
     rows: optional packed token ids to compute
     Returns (O [n_q, Hq, D], LSE [n_q, Hq]) or (O, LSE, sum_j P) with ``with_psum``.
     """
@@ -92,11 +102,25 @@ def attn_fwd(q, k, v, cu_seqlens, causal: bool, scale: float, row_ptr=None, col_
     out = np.zeros((n_q, hq, d), dtype=np.float64)
     lse = np.zeros((n_q, hq), dtype=np.float64)
     psum = np.zeros((n_q, hq), dtype=np.float64) if with_psum else None
-    rc = _load().oracle_attn_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(cu), n_seqs, hq, hkv, d, int(bool(causal)),
-        float(scale), _ptr(rp), _ptr(ci), 0 if rp is None else len(rp) - 1, int(block),
-        _ptr(rows_a), 0 if rows_a is None else len(rows_a), _ptr(out), _ptr(lse), _ptr(psum),
-        int(nthreads))
+    if block_mask is not None:
+        if rp is not None:
+            raise ValueError("a block list and a block mask together")
+        m = np.ascontiguousarray(block_mask, dtype=np.uint32)
+        if m.ndim != 4 or m.shape[0] not in (1, n_seqs) or m.shape[1] not in (1, hkv):
+            raise ValueError(f"block_mask shape {m.shape}")
+        n_qblk, words = m.shape[2], m.shape[3]
+        ss = m.shape[1] * n_qblk * words if m.shape[0] > 1 else 0
+        sh = n_qblk * words if m.shape[1] > 1 else 0
+        rc = _load().oracle_attn_fwd_mask(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(cu), n_seqs, hq, hkv, d, int(bool(causal)),
+            float(scale), _ptr(m), ss, sh, words, n_qblk, int(block), _ptr(rows_a),
+            0 if rows_a is None else len(rows_a), _ptr(out), _ptr(lse), _ptr(psum), int(nthreads))
+    else:
+        rc = _load().oracle_attn_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(cu), n_seqs, hq, hkv, d, int(bool(causal)),
+            float(scale), _ptr(rp), _ptr(ci), 0 if rp is None else len(rp) - 1, int(block),
+            _ptr(rows_a), 0 if rows_a is None else len(rows_a), _ptr(out), _ptr(lse), _ptr(psum),
+            int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_attn_fwd failed with code {rc}")
     if with_psum:
@@ -120,4 +144,4 @@ def run_workload(w, rows=None, nthreads: int = 0, with_psum: bool = False):
     else:
         qf = bf16_bits_to_f32(q[np.asarray(rows, dtype=np.int64)]).astype(np.float64)
     return attn_fwd(qf, kf, vf, w.cu_seqlens_or_fixed(), w.causal, w.scale, w.row_ptr, w.col_idx,
-                    128, rows, nthreads, with_psum)
+                    128, rows, nthreads, with_psum, getattr(w, "block_mask", None))

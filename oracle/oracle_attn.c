@@ -11,7 +11,9 @@
  * query position i (0 <= i < L), with g = Hq/Hkv and kv head c = floor(h/g):
  *
  *   A(i)  = { j : 0 <= j < L, (!causal || j <= i),
- *                 (no list || floor(j/blk) is listed for query block floor(i/blk)) }
+ *                 (no list || floor(j/blk) is listed for query block floor(i/blk)),
+ *                 (no mask || bit floor(j/blk) of the mask row of query block
+ *                             floor(i/blk), for sequence b and kv head c, is 1) }
  *   s_j   = scale * sum_d q[i,h,d] * k[j,c,d]          for j in A(i)
  *   m     = max_{j in A(i)} s_j
  *   LSE_i = m + ln( sum_{j in A(i)} exp(s_j - m) )      (natural log)
@@ -27,7 +29,12 @@
  * blocks that are skipped are never visited and contribute nothing.  The CoSA
  * explainer (lay summary) says the kernel receives an ordered priority list of
  * blocks; the order is a visiting order only, so A(i) is the set of listed
- * blocks.  Causal masking, grouped-query heads, packed variable-length batches
+ * blocks.  The AdaSplash-2 explainer (section 2, sparsity-aware execution,
+ * "bit-packed block masking") stores which blocks hold non-zero weights as a
+ * bit mask, 32 blocks per 32-bit word; a block is visited iff its bit is 1.
+ * Here bit (kb mod 32) of word floor(kb/32) of a query block's mask row
+ * says whether KV block kb is visible; each (sequence, kv head) may have
+ * its own mask.  Causal masking, grouped-query heads, packed variable-length batches
  * and the log-sum-exp output are fixed by the workload definitions, not the
  * pages.
  *
@@ -51,6 +58,9 @@ typedef struct {
   int n_seqs, hq, hkv, d, causal;
   double scale;
   const int32_t *row_ptr, *col_idx;
+  const uint32_t *mask;       /* bit mask (see oracle_attn_fwd_mask), or NULL */
+  int64_t mask_ss, mask_sh;   /* words between the masks of consecutive sequences / kv heads */
+  int mask_words;             /* words per query-block row */
   int n_qblk, blk;
   const int64_t *rows;
   int64_t n_rows;
@@ -90,7 +100,14 @@ static int one_row(job_t *J, int64_t r, int h, double *srow, unsigned char *allo
   double *oi = J->out + ((size_t)r * J->hq + h) * d;
 
   /* allowed set A(i) */
-  if (J->row_ptr) {
+  if (J->mask) {
+    const int64_t n_kvblk = (L + J->blk - 1) / J->blk;
+    const int qb = (int)(i / J->blk);
+    const uint32_t *row = J->mask + (int64_t)b * J->mask_ss + (int64_t)c * J->mask_sh +
+                          (int64_t)qb * J->mask_words;
+    for (int64_t cb = 0; cb < n_kvblk; ++cb)
+      listed[cb] = (unsigned char)((row[cb / 32] >> (cb % 32)) & 1u);
+  } else if (J->row_ptr) {
     const int64_t n_kvblk = (L + J->blk - 1) / J->blk;
     const int qb = (int)(i / J->blk);
     memset(listed, 0, (size_t)n_kvblk);
@@ -102,7 +119,7 @@ static int one_row(job_t *J, int64_t r, int h, double *srow, unsigned char *allo
   for (int64_t j = 0; j < L; ++j) {
     unsigned char ok = 1;
     if (J->causal && j > i) ok = 0;
-    if (ok && J->row_ptr && !listed[j / J->blk]) ok = 0;
+    if (ok && (J->row_ptr || J->mask) && !listed[j / J->blk]) ok = 0;
     allowed[j] = ok;
   }
 
@@ -191,13 +208,23 @@ static void *worker(void *arg) {
  *   nthreads worker threads (<= 0: online CPU count)
  * Returns 0, or a negative code on bad arguments / allocation failure.
  */
-int oracle_attn_fwd(const double *q, const double *k, const double *v, const int32_t *cu,
-                    int n_seqs, int hq, int hkv, int d, int causal, double scale,
-                    const int32_t *row_ptr, const int32_t *col_idx, int n_qblk, int blk,
-                    const int64_t *rows, int64_t n_rows, double *out, double *lse,
-                    double *psum, int nthreads) {
+static int run(const double *q, const double *k, const double *v, const int32_t *cu,
+               int n_seqs, int hq, int hkv, int d, int causal, double scale,
+               const int32_t *row_ptr, const int32_t *col_idx, const uint32_t *mask,
+               int64_t mask_ss, int64_t mask_sh, int mask_words, int n_qblk, int blk,
+               const int64_t *rows, int64_t n_rows, double *out, double *lse, double *psum,
+               int nthreads) {
   if (!q || !k || !v || !cu || !out || !lse || n_seqs < 1 || hq < 1 || hkv < 1 || d < 1)
     return ORACLE_EINVAL;
+  if (row_ptr && mask) return ORACLE_EINVAL;
+  if (mask) {
+    if (blk < 1 || mask_words < 1 || mask_ss < 0 || mask_sh < 0) return ORACLE_EINVAL;
+    for (int b = 0; b < n_seqs; ++b) {
+      const int64_t len = (int64_t)cu[b + 1] - cu[b];
+      const int64_t nb = (len + blk - 1) / blk;
+      if (nb > n_qblk || nb > 32 * (int64_t)mask_words) return ORACLE_EINVAL;
+    }
+  }
   if (hq % hkv != 0) return ORACLE_EINVAL;
   if (row_ptr && (n_seqs != 1 || blk < 1 || !col_idx)) return ORACLE_EINVAL;
   const int64_t T = cu[n_seqs];
@@ -219,7 +246,8 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v, const int
   memset(&J, 0, sizeof(J));
   J.q = q; J.k = k; J.v = v; J.cu = cu; J.n_seqs = n_seqs; J.hq = hq; J.hkv = hkv; J.d = d;
   J.causal = causal; J.scale = scale; J.row_ptr = row_ptr; J.col_idx = col_idx;
-  J.n_qblk = n_qblk; J.blk = row_ptr ? blk : 1; J.rows = rows; J.n_rows = n_rows;
+  J.mask = mask; J.mask_ss = mask_ss; J.mask_sh = mask_sh; J.mask_words = mask_words;
+  J.n_qblk = n_qblk; J.blk = (row_ptr || mask) ? blk : 1; J.rows = rows; J.n_rows = n_rows;
   J.out = out; J.lse = lse; J.psum = psum; J.n_tasks = n_q * hq; J.nthreads = nthreads;
 
   pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
@@ -239,6 +267,34 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v, const int
   free(th);
   free(ws);
   return J.status;
+}
+
+int oracle_attn_fwd(const double *q, const double *k, const double *v, const int32_t *cu,
+                    int n_seqs, int hq, int hkv, int d, int causal, double scale,
+                    const int32_t *row_ptr, const int32_t *col_idx, int n_qblk, int blk,
+                    const int64_t *rows, int64_t n_rows, double *out, double *lse,
+                    double *psum, int nthreads) {
+  return run(q, k, v, cu, n_seqs, hq, hkv, d, causal, scale, row_ptr, col_idx, NULL, 0, 0, 0,
+             n_qblk, blk, rows, n_rows, out, lse, psum, nthreads);
+}
+
+/*
+ * oracle_attn_fwd_mask — as oracle_attn_fwd, with a bit-packed block mask in
+ * place of the list.  The mask row of query block qb for sequence b and kv
+ * head c starts at  mask + b*mask_ss + c*mask_sh + qb*mask_words  (host
+ * uint32 words; strides may be 0 to share a mask); bit (kb mod 32) of word
+ * floor(kb/32) set means KV block kb is visible.  Blocks of blk positions;
+ * every sequence needs ceil(L/blk) <= n_qblk rows and <= 32*mask_words bits.
+ * Any number of sequences.
+ */
+int oracle_attn_fwd_mask(const double *q, const double *k, const double *v, const int32_t *cu,
+                         int n_seqs, int hq, int hkv, int d, int causal, double scale,
+                         const uint32_t *mask, int64_t mask_ss, int64_t mask_sh, int mask_words,
+                         int n_qblk, int blk, const int64_t *rows, int64_t n_rows, double *out,
+                         double *lse, double *psum, int nthreads) {
+  if (!mask) return ORACLE_EINVAL;
+  return run(q, k, v, cu, n_seqs, hq, hkv, d, causal, scale, NULL, NULL, mask, mask_ss, mask_sh,
+             mask_words, n_qblk, blk, rows, n_rows, out, lse, psum, nthreads);
 }
 
 /* Number of worker threads the oracle uses for nthreads <= 0. */

@@ -114,3 +114,21 @@ def test_bench_workload_numbers():
     w = W.make("mha")
     assert W.counted_flops(w) == 68719476736.0
     assert W.algorithmic_bytes(w) == 2 * 4 * 2048 * 128 * (2 * 16 + 2 * 16) + 4 * 4 * 2048 * 16
+
+
+def test_block_mask_generator():
+    """Per-KV-head masks: each head's set follows the list rule with its own scores."""
+    w = W.make_sparse_mask("m", 6, 4096, 4, 2, 64)
+    assert w.block_mask.shape == (1, 2, 32, 1) and w.block_mask.dtype == np.uint32
+    assert sha(w.block_mask) == "8c22e869bce01c3ffe8f3584c97f63e1fdb4757a25c80cad29bba3da46d283f1"
+    vis = np.unpackbits(w.block_mask.view(np.uint8), axis=-1, bitorder="little")[..., :32].astype(bool)
+    for c in range(2):
+        for i in range(32):
+            row = vis[0, c, i]
+            assert row[0] and row[i] and (i == 0 or row[i - 1])
+            assert int(row.sum()) == W.sparse_budget(i)
+            assert not row[i + 1:].any()
+    assert (vis[0, 0] != vis[0, 1]).any()
+    # counted flops: 128x128 pairs per visible off-diagonal block, half for the diagonal, g heads each
+    per_head = sum(W.sparse_budget(i) - 0.5 for i in range(32))
+    assert W.counted_flops(w) == 4 * 64 * 2 * 128 * 128 * 2 * per_head
