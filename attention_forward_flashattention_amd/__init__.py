@@ -34,6 +34,12 @@ class AttnBlockList(ctypes.Structure):
                 ("num_q_blocks", ctypes.c_int32)]
 
 
+class AttnBlockMask(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_void_p), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("num_q_blocks", ctypes.c_int32), ("words_per_row", ctypes.c_int32),
+                ("stride_seq", ctypes.c_int64), ("stride_head", ctypes.c_int64)]
+
+
 class AttnError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"attn_fwd failed: {msg} (status {status})")
@@ -61,6 +67,11 @@ def load_library(path: str = LIB_PATH):
         lib.attn_fwd.argtypes = [T, T, T, P, ctypes.c_int, ctypes.c_float, BL, T, P, P]
         lib.attn_fwd_validate.restype = ctypes.c_int
         lib.attn_fwd_validate.argtypes = [T, T, T, P, ctypes.c_int, ctypes.c_float, BL, T]
+        BM = ctypes.POINTER(AttnBlockMask)
+        lib.attn_fwd_mask.restype = ctypes.c_int
+        lib.attn_fwd_mask.argtypes = [T, T, T, P, ctypes.c_int, ctypes.c_float, BM, T, P, P]
+        lib.attn_fwd_mask_validate.restype = ctypes.c_int
+        lib.attn_fwd_mask_validate.argtypes = [T, T, T, P, ctypes.c_int, ctypes.c_float, BM, T]
         lib.attn_status_str.restype = ctypes.c_char_p
         lib.attn_status_str.argtypes = [ctypes.c_int]
         lib.attn_version.restype = ctypes.c_int
@@ -93,20 +104,42 @@ def _stream_handle(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def block_mask_descriptor(mask) -> AttnBlockMask:
+    """C descriptor of a bit-packed block mask tensor.
+
+    mask: int32 or uint32 device tensor [B or 1, Hkv or 1, num_q_blocks, words]; a
+    size-1 leading dimension is shared by every sequence / KV head.  Bit kb % 32
+    of word kb // 32 of row qb: KV block kb visible to query block qb.
+    """
+    import torch
+
+    if mask.dim() != 4 or not mask.is_cuda or mask.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("block_mask must be a 4-d int32/uint32 device tensor [B|1, Hkv|1, n_qblk, words]")
+    if mask.stride(3) != 1 or mask.stride(2) != mask.shape[3]:
+        raise ValueError("block_mask rows must be contiguous")
+    ss = mask.stride(0) if mask.shape[0] > 1 else 0
+    sh = mask.stride(1) if mask.shape[1] > 1 else 0
+    return AttnBlockMask(mask.data_ptr(), 128, 128, int(mask.shape[2]), int(mask.shape[3]), ss, sh)
+
+
 def attn_fwd(q, k, v, cu_seqlens=None, causal: bool = False, scale: Optional[float] = None,
              block_list: Optional[Tuple] = None, out=None, lse=None, max_seqlen: Optional[int] = None,
-             return_lse: bool = True, stream=None):
+             return_lse: bool = True, stream=None, block_mask=None):
     """O = softmax(scale * Q K^T + mask) V and the natural-log LSE per row.
 
     q: bf16 [B, S, Hq, D] (or packed [T, Hq, D] with ``cu_seqlens`` int32 [B+1])
     k, v: bf16 [B, S, Hkv, D] (or packed [T, Hkv, D])
     block_list: optional (row_ptr, col_idx) int32 device tensors, 128x128 blocks
+    block_mask: optional bit-packed block mask (see ``block_mask_descriptor``);
+        not together with ``block_list``
     out: optional bf16 output like q;  lse: optional fp32 [B, Hq, S] (packed [Hq, T])
     max_seqlen: packed form only, an upper bound on every sequence length
     Returns (out, lse) (lse None when ``return_lse`` is false and none is given).
     """
     import torch
 
+    if block_list is not None and block_mask is not None:
+        raise ValueError("give a block list or a block mask, not both")
     lib = load_library()
     packed = cu_seqlens is not None
     if packed:
@@ -150,11 +183,17 @@ def attn_fwd(q, k, v, cu_seqlens=None, causal: bool = False, scale: Optional[flo
                 raise ValueError("block list tensors must be contiguous int32 device tensors")
         bl = AttnBlockList(row_ptr.data_ptr(), col_idx.data_ptr() if col_idx.numel() else row_ptr.data_ptr(),
                            128, 128, int(row_ptr.numel()) - 1)
-    st = lib.attn_fwd(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
-                      ctypes.c_void_p(cu_seqlens.data_ptr()) if packed else None,
-                      int(bool(causal)), float(scale), ctypes.byref(bl) if bl is not None else None,
-                      ctypes.byref(do), ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
-                      ctypes.c_void_p(_stream_handle(stream)))
+    cu_p = ctypes.c_void_p(cu_seqlens.data_ptr()) if packed else None
+    lse_p = ctypes.c_void_p(lse.data_ptr()) if lse is not None else None
+    if block_mask is not None:
+        bm = block_mask_descriptor(block_mask)
+        st = lib.attn_fwd_mask(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), cu_p,
+                               int(bool(causal)), float(scale), ctypes.byref(bm), ctypes.byref(do),
+                               lse_p, ctypes.c_void_p(_stream_handle(stream)))
+    else:
+        st = lib.attn_fwd(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), cu_p,
+                          int(bool(causal)), float(scale), ctypes.byref(bl) if bl is not None else None,
+                          ctypes.byref(do), lse_p, ctypes.c_void_p(_stream_handle(stream)))
     if st != ATTN_OK:
         raise AttnError(st, status_str(st))
     return out, lse

@@ -37,7 +37,9 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
-constexpr int kListBlock = 128;  // block-list granularity (rows and keys)
+constexpr int kListBlock = 128;  // block-list / block-mask granularity (rows and keys)
+// KV iteration modes: every key, an ordered block list, a bit-packed block mask
+enum { kDense = 0, kList = 1, kMask = 2 };
 constexpr float kLn2 = 0.69314718055994530942f;
 // A tile's P is accepted against the running max while every row sum of the
 // tile stays at or below this (so every P is at most 2^12).
@@ -57,6 +59,9 @@ struct Params {
   const int32_t *cu;       // packed sequences, or null
   const int32_t *row_ptr;  // block list, or null
   const int32_t *col_idx;
+  const uint32_t *mask;    // bit-packed block mask, or null
+  int64_t mask_ss, mask_sh; // words between masks of consecutive sequences / kv heads
+  int mask_words;          // words per query-block row of a mask
   int batch, seqlen, hq, group;
   int n_tiles;   // query tiles per (sequence, head) = ceil(seqlen / BM)
   int n_units;   // batch * hq
@@ -257,9 +262,10 @@ __device__ __forceinline__ void issue_tile(char *kb, char *vb, const uint16_t *k
   }
 }
 
-template <class C, bool CAUSAL, bool LIST>
+template <class C, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Params p) {
   constexpr int D = C::D;
+  constexpr bool LIST = MODE != kDense;  // block-sparse: one 128-row query block per workgroup
   using L = Lds<D>;
   constexpr int kBM = C::kBM;
   constexpr int kBN = C::kBN;
@@ -302,24 +308,55 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   const int j16 = lane & 15;
 
   // ---- KV iteration space
+  constexpr int kSub = kListBlock / kBN;  // KV tiles per 128-key block
   int n_iter;
   int e0 = 0;
   const int n_kvblk = (len + kListBlock - 1) / kListBlock;
-  if (LIST) {
+  // block mask: this query block's row of the (sequence, kv head) mask; under
+  // causal masking only blocks up to the query block count
+  const uint32_t *mrow = nullptr;
+  const int m_lim = CAUSAL ? min(n_kvblk, tile + 1) : n_kvblk;
+  const int m_words = (m_lim + 31) >> 5;
+  auto m_valid = [&](int w) -> uint32_t {  // bits of word w below m_lim
+    const int left = m_lim - 32 * w;
+    return left >= 32 ? 0xffffffffu : (left <= 0 ? 0u : ((1u << left) - 1u));
+  };
+  if (MODE == kList) {
     e0 = p.row_ptr[tile];
-    n_iter = (p.row_ptr[tile + 1] - e0) * (kListBlock / kBN);
+    n_iter = (p.row_ptr[tile + 1] - e0) * kSub;
+  } else if (MODE == kMask) {
+    mrow = p.mask + b * p.mask_ss + kvh * p.mask_sh + (int64_t)tile * p.mask_words;
+    int n_blk = 0;
+    for (int w = 0; w < m_words; ++w) n_blk += __builtin_popcount(mrow[w] & m_valid(w));
+    n_iter = n_blk * kSub;
   } else {
     const int kv_end = CAUSAL ? min(len, q0 + kBM) : len;
     n_iter = (kv_end + kBN - 1) / kBN;
   }
-  // kv start of iteration `it`, or -1 to skip it (block-list ids out of range
-  // or, under causal masking, wholly above this query tile)
+  // kv start of iteration `it` (called for it = 0, 1, 2, ... in order), or -1
+  // to skip it (block-list ids out of range or, under causal masking, wholly
+  // above this query tile).  The mask is walked set bit by set bit: lowest
+  // bit first, words in order.
+  int m_w = -1;        // mask word being walked
+  uint32_t m_bits = 0; // its set bits not yet visited
+  int m_blk = 0;       // block of the current iteration
   auto kv_start = [&](int it) -> int {
-    if (!LIST) return it * kBN;
-    const int cb = p.col_idx[e0 + it / (kListBlock / kBN)];
+    if (MODE == kDense) return it * kBN;
+    if (MODE == kMask) {
+      if (it % kSub == 0) {
+        while (m_bits == 0) {
+          if (++m_w >= m_words) return -1;
+          m_bits = mrow[m_w] & m_valid(m_w);
+        }
+        m_blk = 32 * m_w + __builtin_ctz(m_bits);
+        m_bits &= m_bits - 1u;
+      }
+      return m_blk * kListBlock + (it % kSub) * kBN;
+    }
+    const int cb = p.col_idx[e0 + it / kSub];
     if (cb < 0 || cb >= n_kvblk) return -1;
     if (CAUSAL && cb * kListBlock > q0 + kBM - 1) return -1;
-    return cb * kListBlock + (it % (kListBlock / kBN)) * kBN;
+    return cb * kListBlock + (it % kSub) * kBN;
   };
 
   // Direct global -> LDS loads of one KV tile into buffer `buf`.  Each wave-wide
@@ -637,22 +674,74 @@ int validate(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t
   return ATTN_OK;
 }
 
-template <class C, bool CAUSAL, bool LIST>
+template <class C, bool CAUSAL, int MODE>
 int launch(Params p, hipStream_t stream) {
   p.n_tiles = (p.seqlen + C::kBM - 1) / C::kBM;
   const int64_t n_blocks = (int64_t)p.n_tiles * p.n_units;
   void *args[] = {&p};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<C, CAUSAL, LIST>),
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<C, CAUSAL, MODE>),
                                  dim3((unsigned)n_blocks), dim3(C::kThreads), args, 0, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 template <int D>
-int launch_d(const Params &p, bool causal, bool list, hipStream_t s) {
+int launch_d(const Params &p, bool causal, int mode, hipStream_t s) {
   using Dense = Config<D, D == 256 ? 4 : 8>;
   using Listed = Config<D, 4>;
-  if (list) return causal ? launch<Listed, true, true>(p, s) : launch<Listed, false, true>(p, s);
-  return causal ? launch<Dense, true, false>(p, s) : launch<Dense, false, false>(p, s);
+  if (mode == kList)
+    return causal ? launch<Listed, true, kList>(p, s) : launch<Listed, false, kList>(p, s);
+  if (mode == kMask)
+    return causal ? launch<Listed, true, kMask>(p, s) : launch<Listed, false, kMask>(p, s);
+  return causal ? launch<Dense, true, kDense>(p, s) : launch<Dense, false, kDense>(p, s);
+}
+
+// Checks of attn_fwd_mask beyond those of attn_fwd.
+int validate_mask(const attn_tensor_t *q, const attn_block_mask_t *m) {
+  if (!m) return ATTN_ERR_INVALID_ARG;
+  if (m->block_q != kListBlock || m->block_k != kListBlock) return ATTN_ERR_UNSUPPORTED;
+  if (m->stride_seq < 0 || m->stride_head < 0) return ATTN_ERR_INVALID_ARG;
+  const int64_t n_blk = (q->seqlen + kListBlock - 1) / kListBlock;
+  if (m->num_q_blocks < n_blk || (int64_t)m->words_per_row * 32 < n_blk || m->words_per_row < 1)
+    return ATTN_ERR_INVALID_ARG;
+  if (q->batch > 0 && q->seqlen > 0 && !m->bits) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+Params make_params(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                   const int32_t *cu_seqlens, float scale, attn_tensor_t *out, float *lse) {
+  Params p;
+  p.q = static_cast<const uint16_t *>(q->data);
+  p.k = static_cast<const uint16_t *>(k->data);
+  p.v = static_cast<const uint16_t *>(v->data);
+  p.o = static_cast<uint16_t *>(out->data);
+  p.lse = lse;
+  p.q_sb = q->stride_batch; p.q_ss = q->stride_seq; p.q_sh = q->stride_head;
+  p.k_sb = k->stride_batch; p.k_ss = k->stride_seq; p.k_sh = k->stride_head;
+  p.v_sb = v->stride_batch; p.v_ss = v->stride_seq; p.v_sh = v->stride_head;
+  p.o_sb = out->stride_batch; p.o_ss = out->stride_seq; p.o_sh = out->stride_head;
+  p.cu = cu_seqlens;
+  p.row_ptr = nullptr;
+  p.col_idx = nullptr;
+  p.mask = nullptr;
+  p.mask_ss = p.mask_sh = 0;
+  p.mask_words = 0;
+  p.batch = q->batch;
+  p.seqlen = q->seqlen;
+  p.hq = q->heads;
+  p.group = q->heads / k->heads;
+  p.n_tiles = 0;  // set per configuration at launch
+  p.n_units = q->batch * q->heads;
+  p.xcd_remap = (p.n_units % (8 * p.group)) == 0 ? 1 : 0;
+  p.c = scale * 1.44269504088896340736f;
+  return p;
+}
+
+int launch_any(const Params &p, int d, bool causal, int mode, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_d<64>(p, causal, mode, s);
+    case 128: return launch_d<128>(p, causal, mode, s);
+    default: return launch_d<256>(p, causal, mode, s);
+  }
 }
 
 }  // namespace
@@ -671,35 +760,37 @@ extern "C" int attn_fwd(const attn_tensor_t *q, const attn_tensor_t *k, const at
   const int st = validate(q, k, v, cu_seqlens, causal, scale, block_list, out);
   if (st != ATTN_OK) return st;
   if (q->batch == 0 || q->seqlen == 0) return ATTN_OK;
-
-  Params p;
-  p.q = static_cast<const uint16_t *>(q->data);
-  p.k = static_cast<const uint16_t *>(k->data);
-  p.v = static_cast<const uint16_t *>(v->data);
-  p.o = static_cast<uint16_t *>(out->data);
-  p.lse = lse;
-  p.q_sb = q->stride_batch; p.q_ss = q->stride_seq; p.q_sh = q->stride_head;
-  p.k_sb = k->stride_batch; p.k_ss = k->stride_seq; p.k_sh = k->stride_head;
-  p.v_sb = v->stride_batch; p.v_ss = v->stride_seq; p.v_sh = v->stride_head;
-  p.o_sb = out->stride_batch; p.o_ss = out->stride_seq; p.o_sh = out->stride_head;
-  p.cu = cu_seqlens;
-  p.row_ptr = block_list ? block_list->row_ptr : nullptr;
-  p.col_idx = block_list ? block_list->col_idx : nullptr;
-  p.batch = q->batch;
-  p.seqlen = q->seqlen;
-  p.hq = q->heads;
-  p.group = q->heads / k->heads;
-  p.n_tiles = 0;  // set per configuration at launch
-  p.n_units = q->batch * q->heads;
-  p.xcd_remap = (p.n_units % (8 * p.group)) == 0 ? 1 : 0;
-  p.c = scale * 1.44269504088896340736f;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool list = block_list != nullptr;
-  switch (q->head_dim) {
-    case 64: return launch_d<64>(p, causal, list, s);
-    case 128: return launch_d<128>(p, causal, list, s);
-    default: return launch_d<256>(p, causal, list, s);
+  Params p = make_params(q, k, v, cu_seqlens, scale, out, lse);
+  if (block_list) {
+    p.row_ptr = block_list->row_ptr;
+    p.col_idx = block_list->col_idx;
   }
+  return launch_any(p, q->head_dim, causal, block_list ? kList : kDense,
+                    static_cast<hipStream_t>(stream));
+}
+
+extern "C" int attn_fwd_mask_validate(const attn_tensor_t *q, const attn_tensor_t *k,
+                                      const attn_tensor_t *v, const int32_t *cu_seqlens,
+                                      int causal, float scale, const attn_block_mask_t *mask,
+                                      const attn_tensor_t *out) {
+  const int st = validate(q, k, v, cu_seqlens, causal, scale, nullptr, out);
+  if (st != ATTN_OK) return st;
+  return validate_mask(q, mask);
+}
+
+extern "C" int attn_fwd_mask(const attn_tensor_t *q, const attn_tensor_t *k,
+                             const attn_tensor_t *v, const int32_t *cu_seqlens, int causal,
+                             float scale, const attn_block_mask_t *mask, attn_tensor_t *out,
+                             float *lse, void *stream) {
+  const int st = attn_fwd_mask_validate(q, k, v, cu_seqlens, causal, scale, mask, out);
+  if (st != ATTN_OK) return st;
+  if (q->batch == 0 || q->seqlen == 0) return ATTN_OK;
+  Params p = make_params(q, k, v, cu_seqlens, scale, out, lse);
+  p.mask = mask->bits;
+  p.mask_ss = mask->stride_seq;
+  p.mask_sh = mask->stride_head;
+  p.mask_words = mask->words_per_row;
+  return launch_any(p, q->head_dim, causal, kMask, static_cast<hipStream_t>(stream));
 }
 
 extern "C" const char *attn_status_str(int status) {
@@ -712,4 +803,4 @@ extern "C" const char *attn_status_str(int status) {
   }
 }
 
-extern "C" int attn_version(void) { return 100; }
+extern "C" int attn_version(void) { return 200; }

@@ -130,7 +130,7 @@ def main():
 
     w = W.make(args.workload)
     flops = W.counted_flops(w)
-    q, k, v, cu, bl = P.to_device(w)
+    q, k, v, cu, sp = P.to_device(w)
     out = torch.empty_like(q)
     if cu is None:
         lse = torch.empty((w.batch, w.hq, w.seqlen), dtype=torch.float32, device=q.device)
@@ -138,8 +138,8 @@ def main():
         lse = torch.empty((w.hq, q.shape[0]), dtype=torch.float32, device=q.device)
 
     def step():
-        attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale, block_list=bl, out=out,
-                      lse=lse, max_seqlen=w.seqlen if cu is not None else None)
+        attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale, out=out, lse=lse,
+                      max_seqlen=w.seqlen if cu is not None else None, **sp)
 
     # Settle the clock: the GPU ramps its engine clock over the first tens of
     # milliseconds of load; without this the timed steps of a short kernel run
@@ -204,11 +204,11 @@ def main():
         log(f"cold cache (L2 and Infinity Cache evicted before each launch): median {np.median(cold) * 1e3:.1f} us, "
             f"min {min(cold) * 1e3:.1f} us over {len(cold)} launches")
 
-    if bl is not None:
+    if sp:
         # block-sparse speedup: the dense causal launch on the same inputs
         def dense():
-            attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale, block_list=None, out=out,
-                          lse=lse, max_seqlen=w.seqlen if cu is not None else None)
+            attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale, out=out, lse=lse,
+                          max_seqlen=w.seqlen if cu is not None else None)
         dense()
         torch.cuda.synchronize()
         n_dense = max(2, args.steps // 20)
@@ -228,7 +228,7 @@ def main():
             f"{dense_ms / ms_per_step:.2f}x (ideal {ideal:.2f}x)")
 
     cpu = None
-    if not args.no_cpu_baseline and not w.packed and w.row_ptr is None:
+    if not args.no_cpu_baseline and not w.packed and not sp:
         cpu = cpu_baseline(w)
         log(f"cpu oracle: {cpu}")
 

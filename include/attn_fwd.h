@@ -8,7 +8,9 @@
  * query heads per key/value head and kv head c = floor(h / g):
  *
  *   A(i)  = { j : 0 <= j < L_b, (causal == 0 || j <= i),
- *                 (no block list || floor(j/128) is listed for floor(i/128)) }
+ *                 (no block list || floor(j/128) is listed for floor(i/128)),
+ *                 (no block mask || the mask bit of block floor(j/128) is set
+ *                                   in the row of floor(i/128)) }
  *   O[b,i,h,:] = sum_{j in A(i)} softmax_j(scale * q.k_j) * v[b,j,c,:]
  *   lse[b,h,i] = ln sum_{j in A(i)} exp(scale * q.k_j)      (natural log)
  *   A(i) empty:  O = 0, lse = -inf.
@@ -72,6 +74,28 @@ typedef struct attn_block_list {
   int32_t num_q_blocks;     /* must equal ceil(seqlen / 128) */
 } attn_block_list_t;
 
+/* Bit-packed block mask (one per sequence and KV head).
+ * The AdaSplash-2 explainer (section 2, sparsity-aware GPU execution) keeps
+ * which blocks of the attention matrix to visit as a bit mask, 32 blocks per
+ * 32-bit word, and walks only the set bits (find-first-set / popcount).
+ * Here bit (kb % 32) of word kb / 32 of row qb says whether KV block kb
+ * (keys 128*kb .. 128*kb+127) is visible to query block qb (queries
+ * 128*qb .. 128*qb+127).  The row of query block qb for sequence b and KV
+ * head c starts at
+ *     bits + b*stride_seq + c*stride_head + qb*words_per_row
+ * (strides in 32-bit words; 0 shares one mask across sequences or heads).
+ * bits: device uint32, owned by the caller.  Set bits of blocks at or beyond
+ * a sequence's end, or above the query block under causal masking,
+ * contribute nothing.  Blocks are visited in ascending order. */
+typedef struct attn_block_mask {
+  const uint32_t *bits;
+  int32_t block_q, block_k; /* both must be 128 */
+  int32_t num_q_blocks;     /* rows per mask, >= ceil(seqlen / 128) */
+  int32_t words_per_row;    /* >= ceil(ceil(seqlen / 128) / 32) */
+  int64_t stride_seq;       /* words between the masks of consecutive sequences */
+  int64_t stride_head;      /* words between the masks of consecutive KV heads */
+} attn_block_mask_t;
+
 enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = -1, /* arguments contradict each other or are null */
@@ -122,6 +146,30 @@ int attn_fwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t
 int attn_fwd_validate(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
                       const int32_t *cu_seqlens, int causal, float scale,
                       const attn_block_list_t *block_list, const attn_tensor_t *out);
+
+/*
+ * attn_fwd_mask — fused attention forward with a bit-packed block mask in
+ * place of the block list: A(i) keeps key j only when the mask of the
+ * query's sequence and KV head has the bit of block floor(j/128) set in the
+ * row of query block floor(i/128).  Every other argument is as for attn_fwd;
+ * unlike the block list, the mask works with any batch size and with packed
+ * sequences (cu_seqlens).
+ *
+ * Returns what attn_fwd returns for the shared arguments, or:
+ *   ATTN_ERR_INVALID_ARG  mask == NULL, bits == NULL for a non-empty problem,
+ *                         negative strides, num_q_blocks < ceil(seqlen/128),
+ *                         words_per_row < max(1, ceil(ceil(seqlen/128)/32))
+ *   ATTN_ERR_UNSUPPORTED  block sizes other than 128
+ */
+int attn_fwd_mask(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                  const int32_t *cu_seqlens, int causal, float scale,
+                  const attn_block_mask_t *mask, attn_tensor_t *out, float *lse, void *stream);
+
+/* The argument checks of attn_fwd_mask alone (host code only). */
+int attn_fwd_mask_validate(const attn_tensor_t *q, const attn_tensor_t *k,
+                           const attn_tensor_t *v, const int32_t *cu_seqlens, int causal,
+                           float scale, const attn_block_mask_t *mask,
+                           const attn_tensor_t *out);
 
 /* Static description of a status code (never NULL). */
 const char *attn_status_str(int status);

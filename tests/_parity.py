@@ -17,7 +17,8 @@ O_REL_RMS = 1e-2   # ||O - O_ref||_2 / ||O_ref||_2, catches errors the loose max
 
 
 def to_device(w: W.Workload, layout: str = "bshd"):
-    """Device tensors for a workload: q, k, v (bf16), cu_seqlens, block list."""
+    """Device tensors for a workload: q, k, v (bf16), cu_seqlens, and the keyword
+    arguments that carry its block sparsity ({} dense, block_list or block_mask)."""
     import torch
 
     dev = torch.device("cuda:0")
@@ -31,11 +32,13 @@ def to_device(w: W.Workload, layout: str = "bshd"):
 
     q, k, v = t(w.q), t(w.k), t(w.v)
     cu = None if w.cu_seqlens is None else torch.from_numpy(w.cu_seqlens.astype(np.int32)).to(dev)
-    bl = None
+    sp = {}
     if w.row_ptr is not None:
-        bl = (torch.from_numpy(w.row_ptr.astype(np.int32)).to(dev),
-              torch.from_numpy(w.col_idx.astype(np.int32)).to(dev))
-    return q, k, v, cu, bl
+        sp["block_list"] = (torch.from_numpy(w.row_ptr.astype(np.int32)).to(dev),
+                            torch.from_numpy(w.col_idx.astype(np.int32)).to(dev))
+    if w.block_mask is not None:
+        sp["block_mask"] = torch.from_numpy(np.ascontiguousarray(w.block_mask).view(np.int32)).to(dev)
+    return q, k, v, cu, sp
 
 
 def run_gpu(w: W.Workload, layout: str = "bshd", tensors=None):
@@ -43,9 +46,9 @@ def run_gpu(w: W.Workload, layout: str = "bshd", tensors=None):
     import torch
     import attention_forward_flashattention_amd as attn
 
-    q, k, v, cu, bl = tensors if tensors is not None else to_device(w, layout)
-    out, lse = attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale, block_list=bl,
-                             max_seqlen=w.seqlen if cu is not None else None)
+    q, k, v, cu, sp = tensors if tensors is not None else to_device(w, layout)
+    out, lse = attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale,
+                             max_seqlen=w.seqlen if cu is not None else None, **sp)
     torch.cuda.synchronize()
     o = out.float().cpu().numpy().astype(np.float64)
     l = lse.cpu().numpy().astype(np.float64)

@@ -9,7 +9,7 @@ import subprocess
 import pytest
 
 import attention_forward_flashattention_amd as attn
-from attention_forward_flashattention_amd import AttnBlockList, AttnTensor
+from attention_forward_flashattention_amd import AttnBlockList, AttnBlockMask, AttnTensor
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
@@ -22,7 +22,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_validate", "attn_status_str", "attn_version"]
+    assert declared_functions() == ["attn_fwd", "attn_fwd_mask", "attn_fwd_mask_validate", "attn_fwd_validate",
+                                    "attn_status_str", "attn_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -33,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.attn_version() == 100
+    assert lib.attn_version() == 200
     assert attn.status_str(0) == "ok" and attn.status_str(-3) == "kernel launch failed"
 
 
@@ -118,3 +119,33 @@ def test_attn_fwd_returns_validation_errors_without_launching():
     st = lib.attn_fwd(ctypes.byref(e), ctypes.byref(e), ctypes.byref(e), None, 1, 0.1, None,
                       ctypes.byref(e), None, None)
     assert st == 0
+
+
+def validate_mask(q, k, v, mask, cu=None, causal=1, scale=0.125, out=None):
+    lib = attn.load_library()
+    out = out if out is not None else q
+    return lib.attn_fwd_mask_validate(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), cu, causal, scale,
+                                      ctypes.byref(mask) if mask is not None else None, ctypes.byref(out))
+
+
+def mask_desc(n_qblk=2, words=1, ss=0, sh=0, bq=128, bk=128, bits=FAKE):
+    return AttnBlockMask(bits, bq, bk, n_qblk, words, ss, sh)
+
+
+def test_block_mask_validation():
+    q, k, v = desc(b=2, s=256), desc(b=2, s=256, h=2), desc(b=2, s=256, h=2)
+    assert validate_mask(q, k, v, mask_desc()) == 0
+    assert validate_mask(q, k, v, mask_desc(ss=4, sh=2)) == 0           # per sequence and head
+    assert validate_mask(q, k, v, None) == -1                          # no descriptor
+    assert validate_mask(q, k, v, mask_desc(bits=None)) == -1          # no bits
+    assert validate_mask(q, k, v, mask_desc(n_qblk=1)) == -1           # fewer rows than query blocks
+    assert validate_mask(q, k, v, mask_desc(words=0)) == -1
+    assert validate_mask(q, k, v, mask_desc(ss=-1)) == -1
+    assert validate_mask(q, k, v, mask_desc(bq=64)) == -2              # block size other than 128
+    # 33 blocks need 2 words per row
+    q2, k2, v2 = desc(b=1, s=33 * 128), desc(b=1, s=33 * 128, h=2), desc(b=1, s=33 * 128, h=2)
+    assert validate_mask(q2, k2, v2, mask_desc(n_qblk=33, words=1)) == -1
+    assert validate_mask(q2, k2, v2, mask_desc(n_qblk=33, words=2)) == 0
+    # shared checks still apply
+    k.heads = 3
+    assert validate_mask(q, k, v, mask_desc()) == -1

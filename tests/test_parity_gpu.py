@@ -202,6 +202,97 @@ def test_large_scores_shifted_keys():
     note(f"  {stats}")
 
 
+# ---------------------------------------------------------------- bit-packed block masks
+def random_visibility(seed, n_s, n_h, n_qblk, n_kblk, p=0.5, diag=True):
+    rng = np.random.default_rng(seed)
+    vis = rng.random((n_s, n_h, n_qblk, n_kblk)) < p
+    if diag:
+        for qb in range(min(n_qblk, n_kblk)):
+            vis[..., qb, qb] = True
+    return vis
+
+
+MASK_CASES = [
+    # name, lengths (None = fixed B x S), B, S, hq, hkv, d, causal, mask sets (seq, head)
+    ("per_head_causal_d128", None, 2, 700, 4, 2, 128, True, (1, 2)),
+    ("per_seq_noncausal_d64", None, 3, 300, 4, 4, 64, False, (3, 1)),
+    ("per_seq_head_varlen_d128", [300, 1, 700, 129], 0, 0, 8, 2, 128, True, (4, 2)),
+    ("per_head_causal_d256", None, 1, 520, 4, 2, 256, True, (1, 2)),
+    ("two_words_causal_d64", None, 1, 40 * 128 + 17, 2, 2, 64, True, (1, 2)),
+    ("shared_noncausal_d128", None, 2, 400, 2, 1, 128, False, (1, 1)),
+]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=[c[0] for c in MASK_CASES])
+def test_block_mask_small_full(case):
+    name, lengths, b, s, hq, hkv, d, causal, (ns, nh) = case
+    note(f"block mask case {name}")
+    if lengths is None:
+        w = W.make_dense(name, 30, b, s, hq, hkv, d, causal)
+    else:
+        w = W.make_varlen(name, 31, lengths, hq, hkv, d, causal)
+    n_qblk = (w.seqlen + 127) // 128
+    w.block_mask = W.pack_block_mask(random_visibility(32, ns, nh, n_qblk, n_qblk, p=0.45))
+    stats = P.check_workload(w)
+    note(f"  {stats}")
+
+
+def test_block_mask_empty_rows():
+    """A query block whose mask row has no visible block: O = 0 and LSE = -inf there."""
+    w = W.make_dense("mask_empty", 33, 1, 384, 2, 1, 64, False)
+    vis = random_visibility(34, 1, 1, 3, 3, p=0.6)
+    vis[0, 0, 1, :] = False
+    w.block_mask = W.pack_block_mask(vis)
+    o, l = P.run_gpu(w)
+    assert np.all(o[128:256] == 0) and np.all(l[128:256] == -np.inf)
+    import oracle
+    o_ref, l_ref = oracle.run_workload(w)
+    P.compare(o, l, o_ref, l_ref, "mask_empty")
+
+
+def test_block_mask_zero_q_counts_per_head():
+    """Q = 0: LSE_i = ln |A(i)| with the count taken from each KV head's own mask."""
+    w = W.make_dense("mask_zq", 35, 1, 1024, 4, 2, 128, True)
+    w.q[:] = 0
+    vis = random_visibility(36, 1, 2, 8, 8, p=0.5)
+    w.block_mask = W.pack_block_mask(vis)
+    _, l = P.run_gpu(w)
+    for h in range(4):
+        c = h // 2
+        for i in range(0, 1024, 5):
+            qb = i // 128
+            n = sum(min(128, i + 1 - kb * 128) for kb in range(qb + 1) if vis[0, c, qb, kb])
+            assert abs(l[i, h] - math.log(n)) <= 1e-5, (h, i)
+
+
+def test_block_mask_of_list_matches_list():
+    """The bit-packed form of the block list gives the list's result (visit order differs)."""
+    w = sparse_small(s=4096, seed=37)
+    ol, ll = P.run_gpu(w)
+    vis = W.list_visibility(w.row_ptr, w.col_idx, 32)
+    w.row_ptr, w.col_idx = None, None
+    w.block_mask = W.pack_block_mask(vis[None, None])
+    om, lm = P.run_gpu(w)
+    P.compare(om, lm, ol, ll, "mask of list")
+
+
+def test_full_block_mask_equals_dense_causal():
+    w = W.make_dense("mask_full", 38, 1, 1000, 4, 2, 128, True)
+    od, ld = P.run_gpu(w)
+    n = 8
+    w.block_mask = W.pack_block_mask(np.tril(np.ones((n, n), bool))[None, None])
+    om, lm = P.run_gpu(w)
+    P.compare(om, lm, od, ld, "full mask")
+
+
+def test_block_mask_workload_sampled():
+    """Per-KV-head masks at S = 32768 (256 query blocks, 8 words per row), sampled rows."""
+    w = W.make_sparse_mask("mask_32k", 39, 32768, 32, 8, 128, n_sample=128)
+    note(f"per-head mask workload S=32768: {len(w.sample_rows)} sampled rows x {w.hq} heads")
+    stats = P.check_workload(w, rows=w.sample_rows)
+    note(f"  {stats}")
+
+
 def test_late_large_score_raises_running_max():
     """A key late in the sequence scores far above every earlier key (P would be
     ~2^50 against the running max): the kernel must raise the max and rescale O
