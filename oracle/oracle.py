@@ -1,4 +1,4 @@
-"""Python face of the fp64 CPU oracle (``oracle_attn.c``).
+"""Python face of the fp64 CPU oracle (``oracle_attn.c``, ``oracle_bwd.c``).
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg are the only callers.  The product path never imports this
@@ -6,9 +6,11 @@ module, and this module never imports the product package.
 
 ``attn_fwd`` computes exact softmax attention forward in float64 from the
 definition (see the header of ``oracle_attn.c`` for the formula and the
-passages of the pages it follows).  Every function's parity status is
-"pinned": ``tests/test_oracle_pins.py`` ties it to brute force, closed forms
-and invariants that do not go through this code.
+passages of the pages it follows); ``attn_bwd`` its exact gradients (header
+of ``oracle_bwd.c``).  Every function's parity status is "pinned":
+``tests/test_oracle_pins.py``, ``test_oracle_mask_pins.py`` and
+``test_oracle_bwd_pins.py`` tie them to brute force, finite differences,
+closed forms and invariants that do not go through this code.
 """
 from __future__ import annotations
 
@@ -20,7 +22,7 @@ from typing import Optional
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "oracle_attn.c")
+SRCS = [os.path.join(HERE, "oracle_attn.c"), os.path.join(HERE, "oracle_bwd.c")]
 LIB = os.path.join(HERE, "liboracle_attn.so")
 
 _lib = None
@@ -31,7 +33,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(LIB):
         tmp = LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
-                               "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"])
+                               "-Wall", "-Wextra", "-o", tmp, *SRCS, "-lm"])
         os.replace(tmp, LIB)
     return LIB
 
@@ -54,6 +56,11 @@ def _load():
                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_int, P, ctypes.c_int64, P, P,
                                              P, ctypes.c_int]
+        lib.oracle_attn_bwd.restype = ctypes.c_int
+        lib.oracle_attn_bwd.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_double, P,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                        P, P, P, ctypes.c_int]
         lib.oracle_default_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -105,12 +112,8 @@ def attn_fwd(q, k, v, cu_seqlens, causal: bool, scale: float, row_ptr=None, col_
     if block_mask is not None:
         if rp is not None:
             raise ValueError("a block list and a block mask together")
-        m = np.ascontiguousarray(block_mask, dtype=np.uint32)
-        if m.ndim != 4 or m.shape[0] not in (1, n_seqs) or m.shape[1] not in (1, hkv):
-            raise ValueError(f"block_mask shape {m.shape}")
-        n_qblk, words = m.shape[2], m.shape[3]
-        ss = m.shape[1] * n_qblk * words if m.shape[0] > 1 else 0
-        sh = n_qblk * words if m.shape[1] > 1 else 0
+        m, ss, sh, words = _mask_strides(block_mask, n_seqs, hkv)
+        n_qblk = m.shape[2]
         rc = _load().oracle_attn_fwd_mask(
             _ptr(q), _ptr(k), _ptr(v), _ptr(cu), n_seqs, hq, hkv, d, int(bool(causal)),
             float(scale), _ptr(m), ss, sh, words, n_qblk, int(block), _ptr(rows_a),
@@ -126,6 +129,49 @@ def attn_fwd(q, k, v, cu_seqlens, causal: bool, scale: float, row_ptr=None, col_
     if with_psum:
         return out, lse, psum
     return out, lse
+
+
+def _mask_strides(block_mask, n_seqs, hkv):
+    m = np.ascontiguousarray(block_mask, dtype=np.uint32)
+    if m.ndim != 4 or m.shape[0] not in (1, n_seqs) or m.shape[1] not in (1, hkv):
+        raise ValueError(f"block_mask shape {m.shape}")
+    n_qblk, words = m.shape[2], m.shape[3]
+    ss = m.shape[1] * n_qblk * words if m.shape[0] > 1 else 0
+    sh = n_qblk * words if m.shape[1] > 1 else 0
+    return m, ss, sh, words
+
+
+def attn_bwd(q, k, v, dout, cu_seqlens, causal: bool, scale: float, block_mask=None,
+             block: int = 128, nthreads: int = 0):
+    """Exact gradients of sum(O * dout) with respect to q, k and v.
+
+    q, dout: float64 [T, Hq, D];  k, v: float64 [T, Hkv, D];  cu_seqlens: int [n+1]
+    block_mask: optional uint32 [n_seqs or 1, Hkv or 1, n_qblk, words] (as in attn_fwd)
+    Returns (dq [T, Hq, D], dk [T, Hkv, D], dv [T, Hkv, D]).
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    do = np.ascontiguousarray(dout, dtype=np.float64)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    n_seqs = len(cu) - 1
+    t = int(cu[-1])
+    hq, d = q.shape[1], q.shape[2]
+    hkv = k.shape[1]
+    if q.shape != (t, hq, d) or do.shape != q.shape:
+        raise ValueError(f"q/dout shape {q.shape}/{do.shape} != {(t, hq, d)}")
+    if k.shape != (t, hkv, d) or v.shape != (t, hkv, d):
+        raise ValueError(f"k/v shape {k.shape}/{v.shape} != {(t, hkv, d)}")
+    m, ss, sh, words = (None, 0, 0, 0) if block_mask is None else _mask_strides(block_mask, n_seqs, hkv)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    rc = _load().oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(cu), n_seqs, hq, hkv, d,
+                                 int(bool(causal)), float(scale), _ptr(m), ss, sh, words, int(block),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_bwd failed with code {rc}")
+    return dq, dk, dv
 
 
 def run_workload(w, rows=None, nthreads: int = 0, with_psum: bool = False):
