@@ -1,7 +1,7 @@
-"""Fused softmax-attention forward for AMD Instinct MI355X (gfx950).
+"""Fused softmax attention, forward and backward, for AMD Instinct MI355X (gfx950).
 
 The work happens in ``libattn_fwd.so`` (hand-written HIP, C ABI declared in
-``include/attn_fwd.h``).  This module only marshals torch tensors into the C
+``include/attn_fwd.h`` and ``include/attn_bwd.h``).  This module only marshals torch tensors into the C
 descriptors: every step of the computation runs in the library's kernels.
 There is no fallback: if the library is missing, calls raise.
 """
@@ -41,8 +41,8 @@ class AttnBlockMask(ctypes.Structure):
 
 
 class AttnError(RuntimeError):
-    def __init__(self, status: int, msg: str):
-        super().__init__(f"attn_fwd failed: {msg} (status {status})")
+    def __init__(self, status: int, msg: str, what: str = "attn_fwd"):
+        super().__init__(f"{what} failed: {msg} (status {status})")
         self.status = status
 
 
@@ -72,6 +72,14 @@ def load_library(path: str = LIB_PATH):
         lib.attn_fwd_mask.argtypes = [T, T, T, P, ctypes.c_int, ctypes.c_float, BM, T, P, P]
         lib.attn_fwd_mask_validate.restype = ctypes.c_int
         lib.attn_fwd_mask_validate.argtypes = [T, T, T, P, ctypes.c_int, ctypes.c_float, BM, T]
+        lib.attn_bwd.restype = ctypes.c_int
+        lib.attn_bwd.argtypes = [T, T, T, T, T, P, P, ctypes.c_int, ctypes.c_float, BM, T, T, T, P,
+                                 ctypes.c_size_t, P]
+        lib.attn_bwd_validate.restype = ctypes.c_int
+        lib.attn_bwd_validate.argtypes = [T, T, T, T, T, P, P, ctypes.c_int, ctypes.c_float, BM, T, T,
+                                          T, P, ctypes.c_size_t]
+        lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.attn_bwd_workspace_size.argtypes = [T]
         lib.attn_status_str.restype = ctypes.c_char_p
         lib.attn_status_str.argtypes = [ctypes.c_int]
         lib.attn_version.restype = ctypes.c_int
@@ -197,3 +205,56 @@ def attn_fwd(q, k, v, cu_seqlens=None, causal: bool = False, scale: Optional[flo
     if st != ATTN_OK:
         raise AttnError(st, status_str(st))
     return out, lse
+
+
+def attn_bwd(q, k, v, out, dout, lse, cu_seqlens=None, causal: bool = False,
+             scale: Optional[float] = None, max_seqlen: Optional[int] = None, block_mask=None,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(out * dout) for out, lse = attn_fwd(q, k, v, ...).
+
+    q, out, dout: bf16 [B, S, Hq, D] (packed [T, Hq, D] with ``cu_seqlens``)
+    k, v: bf16 [B, S, Hkv, D] (packed [T, Hkv, D]);  lse: the forward's fp32 LSE
+    causal, scale, max_seqlen, block_mask: as for ``attn_fwd`` (the same values)
+    dq, dk, dv: optional bf16 outputs shaped like q, k, v
+    workspace: optional device buffer of at least ``attn_bwd_workspace_size`` bytes
+    """
+    import torch
+
+    lib = load_library()
+    packed = cu_seqlens is not None
+    if packed:
+        if q.dim() != 3:
+            raise ValueError("packed q must be [T, H, D]")
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with cu_seqlens")
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+            raise ValueError("cu_seqlens must be an int32 device tensor")
+        batch, seqlen = int(cu_seqlens.numel()) - 1, int(max_seqlen)
+    else:
+        if q.dim() != 4:
+            raise ValueError("q must be [B, S, H, D]")
+        batch, seqlen = int(q.shape[0]), int(q.shape[1])
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError(f"{name} must be a bfloat16 device tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 device tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(int(q.shape[-1]))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    descs = [describe(t, batch, seqlen, packed) for t in (q, k, v, out, dout, dq, dk, dv)]
+    need = int(lib.attn_bwd_workspace_size(ctypes.byref(descs[0])))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    bm = block_mask_descriptor(block_mask) if block_mask is not None else None
+    st = lib.attn_bwd(*(ctypes.byref(d) for d in descs[:5]), ctypes.c_void_p(lse.data_ptr()),
+                      ctypes.c_void_p(cu_seqlens.data_ptr()) if packed else None,
+                      int(bool(causal)), float(scale), ctypes.byref(bm) if bm is not None else None,
+                      *(ctypes.byref(d) for d in descs[5:]), ctypes.c_void_p(workspace.data_ptr()),
+                      ws_bytes, ctypes.c_void_p(_stream_handle(stream)))
+    if st != ATTN_OK:
+        raise AttnError(st, status_str(st), "attn_bwd")
+    return dq, dk, dv

@@ -1,4 +1,4 @@
-"""Build the HIP library ``libattn_fwd.so`` for gfx950 with hipcc (in-tree)."""
+"""Build the HIP library ``libattn_fwd.so`` (forward and backward kernels) for gfx950 with hipcc (in-tree)."""
 from __future__ import annotations
 
 import os
@@ -7,7 +7,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "attn_fwd.hip")
+SRCS = [os.path.join(PKG, "csrc", "attn_fwd.hip"), os.path.join(PKG, "csrc", "attn_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_fwd.so")
 
@@ -32,7 +32,7 @@ def hipcc() -> str:
 def build(extra_flags=()) -> str:
     """Compile the library; always recompiles.  Returns the path of the .so."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, *SRCS, "-o", tmp]
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
     return LIB

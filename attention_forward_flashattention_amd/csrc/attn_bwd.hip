@@ -1,0 +1,808 @@
+// attn_bwd.hip — softmax-attention backward for AMD Instinct MI355X (gfx950).
+//
+// Two kernels, launched in this order on the caller's stream:
+//
+//  1. dQ kernel: one workgroup per 128-row query tile of one (sequence, query
+//     head), four wave64s of 32 rows each, like the forward.  It first forms
+//     each row's D = dO.O and base-2 LSE and stores them to the workspace.
+//     Then, for every KV tile of 64 keys it may see (double-buffered in LDS
+//     by direct global-to-LDS loads), it recomputes the transposed tiles
+//     S^T = K Q^T and dP^T = V dO^T with 32x32x16 bf16 MFMAs (lane = query
+//     row, as in the forward), forms dS^T = P^T (dP^T - D) in registers and
+//     accumulates dQ^T += K^T dS^T, with K^T operands read by LDS transpose
+//     reads and dS^T staying in registers.
+//
+//  2. dK/dV kernel: one workgroup per 128-key block of one (sequence, KV
+//     head), four wave64s of 32 keys each, the K and V rows of its keys in
+//     registers for the whole kernel.  For every query head of the group and
+//     every 64-row query tile that may see its keys, it streams Q, dO and the
+//     two per-row workspace values into LDS and computes S = Q K^T and
+//     dP = dO V^T with lane = key.  P and dS then leave the MFMA already in
+//     the layout of the A operand of dV += P^T dO and dK += dS^T Q, whose dO
+//     and Q operands come from LDS transpose reads.
+//
+// The gradients are the chain rule of the forward (softmax Jacobian
+// dS = P (dP - D), with P recomputed from the saved LSE).  With a block
+// mask, both kernels visit only the 128 x 128 blocks whose bit is set, the
+// sparse backward navigation of the AdaSplash-2 explainer (section 2).
+// Neither kernel uses atomics: every output element is written once, by the
+// workgroup that owns it, so results are deterministic.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_bwd.h"
+#include "attn_common.h"
+
+namespace {
+
+using namespace attn_detail;
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kMaxQBlocks = 16384;  // column bitmap capacity of the dK/dV kernel (mask mode)
+
+struct BwdParams {
+  const uint16_t *q, *k, *v, *o, *g;  // g = dO
+  const float *lse;
+  uint16_t *dq, *dk, *dv;
+  float *ws_lse2, *ws_d;  // workspace: base-2 LSE (+inf for rows that see nothing), D = dO.O
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t g_sb, g_ss, g_sh;
+  int64_t dq_sb, dq_ss, dq_sh;
+  int64_t dk_sb, dk_ss, dk_sh;
+  int64_t dv_sb, dv_ss, dv_sh;
+  const int32_t *cu;
+  const uint32_t *mask;
+  int64_t mask_ss, mask_sh;
+  int mask_words;
+  int batch, seqlen, hq, hkv, group;
+  int n_tiles;    // tiles of 128 per unit (query tiles for dQ, key blocks for dK/dV)
+  int n_units;    // (sequence, head) units: batch*hq for dQ, batch*hkv for dK/dV
+  int unit_group; // consecutive units kept on one XCD (the query heads of one KV head for dQ)
+  int xcd_remap;  // 1 when n_units % (8 * unit_group) == 0
+  float c;        // scale * log2(e)
+  float scale;
+};
+
+// Workgroup id -> (tile, unit), dealing workgroups round-robin over the 8 XCDs
+// with the units of one group on one XCD (as the forward does); `reverse`
+// issues the last tiles first (the heaviest ones for causal dQ).
+__device__ __forceinline__ void decode(const BwdParams &p, bool reverse, int &tile, int &unit) {
+  const int w = blockIdx.x;
+  int rank;
+  if (p.xcd_remap) {
+    const int upx = p.n_units >> 3;
+    const int xcd = w & 7;
+    const int local = w >> 3;
+    rank = local / upx;
+    const int lu = local % upx;
+    unit = ((lu / p.unit_group) * 8 + xcd) * p.unit_group + lu % p.unit_group;
+  } else {
+    rank = w / p.n_units;
+    unit = w % p.n_units;
+  }
+  tile = reverse ? p.n_tiles - 1 - rank : rank;
+}
+
+// Index of (sequence b, query head h, row) in the caller's lse array.
+__device__ __forceinline__ int64_t lse_index(const BwdParams &p, int b, int h, int64_t tok0,
+                                             int64_t total, int row) {
+  if (p.cu) return (int64_t)h * total + tok0 + row;
+  return ((int64_t)b * p.hq + h) * p.seqlen + row;
+}
+
+// Index of (sequence b, query head h, row) in the workspace arrays: one slot of
+// seqlen rows per (sequence, head), packed or not, so every row below seqlen
+// stays inside the workspace.
+__device__ __forceinline__ int64_t ws_index(const BwdParams &p, int b, int h, int row) {
+  return ((int64_t)b * p.hq + h) * p.seqlen + row;
+}
+
+__device__ __forceinline__ float dot8(uint4_t a, uint4_t b) {
+  const bf16x8_t x = __builtin_bit_cast(bf16x8_t, a);
+  const bf16x8_t y = __builtin_bit_cast(bf16x8_t, b);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)x[e], (float)y[e], s);
+  return s;
+}
+
+// Direct global -> LDS loads of two 64-row tiles (each wave-wide load fills
+// 64 consecutive 16 B LDS slots; lane n of load i fetches the global chunk at
+// a + aoff[i] / b + boff[i]).  Rows at or beyond rows_left re-read row
+// rows_left - 1.  (A device function rather than a lambda: the LDS pointer
+// casts of the load builtin inside a lambda leave the kernel without its
+// host stub.)
+template <int kLoads>
+__device__ __forceinline__ void issue_pair(char *la, char *lb, const uint16_t *a, const uint16_t *b,
+                                           const int64_t *aoff, const int64_t *boff,
+                                           const int *lrow, int64_t a_ss, int64_t b_ss,
+                                           int rows_left) {
+#pragma unroll
+  for (int n = 0; n < kLoads; ++n) {
+    const int64_t back = min(rows_left - 1 - lrow[n], 0);
+    __builtin_amdgcn_global_load_lds(a + aoff[n] + back * a_ss, (lds_void_t *)(la + n * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(b + boff[n] + back * b_ss, (lds_void_t *)(lb + n * 1024), 16, 0, 0);
+  }
+}
+
+// One dword per lane from global to 64 consecutive LDS dwords.
+__device__ __forceinline__ void issue_dwords(char *l, const float *src) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t *)l, 4, 0, 0);
+}
+
+// ===========================================================================
+// dQ kernel
+// ===========================================================================
+template <int D, bool CAUSAL, int MODE>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
+  using LK = Dual<D>;  // K tile: row-wise reads (S^T) and transpose reads (dQ^T)
+  using LV = Lds<D>;   // V tile: row-wise reads only
+  constexpr int kNW = 4;
+  constexpr int kBM = 32 * kNW;
+  constexpr int kBN = 64;
+  constexpr int kRowBytes = D * 2;
+  constexpr int kChunks = D / 8;
+  constexpr int kDc = D / 16;
+  constexpr int kDt = D / 32;
+  constexpr int kKt = kBN / 32;
+  constexpr int kTileBytes = kBN * kRowBytes;
+  constexpr int kBufBytes = 2 * kTileBytes;  // K tile then V tile
+  constexpr int kLoads = kTileBytes / 1024 / kNW;
+  static_assert(kLoads * 1024 * kNW == kTileBytes, "tile must split evenly over waves");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes];
+
+  int tile, unit;
+  decode(p, CAUSAL || MODE != kDense, tile, unit);
+  const int b = unit / p.hq;
+  const int h = unit % p.hq;
+  const int kvh = h / p.group;
+  int64_t tok0 = 0, total = 0;
+  int len = p.seqlen;
+  if (p.cu) {
+    tok0 = p.cu[b];
+    len = min(p.cu[b + 1] - p.cu[b], p.seqlen);  // seqlen bounds every length
+    total = p.cu[p.batch];
+  }
+  const int q0 = tile * kBM;
+  if (q0 >= len) return;
+
+  const uint16_t *qg = p.q + (p.cu ? tok0 * p.q_ss : (int64_t)b * p.q_sb) + (int64_t)h * p.q_sh;
+  const uint16_t *og = p.o + (p.cu ? tok0 * p.o_ss : (int64_t)b * p.o_sb) + (int64_t)h * p.o_sh;
+  const uint16_t *gg = p.g + (p.cu ? tok0 * p.g_ss : (int64_t)b * p.g_sb) + (int64_t)h * p.g_sh;
+  const uint16_t *kg = p.k + (p.cu ? tok0 * p.k_ss : (int64_t)b * p.k_sb) + (int64_t)kvh * p.k_sh;
+  const uint16_t *vg = p.v + (p.cu ? tok0 * p.v_ss : (int64_t)b * p.v_sb) + (int64_t)kvh * p.v_sh;
+  uint16_t *dqg = p.dq + (p.cu ? tok0 * p.dq_ss : (int64_t)b * p.dq_sb) + (int64_t)h * p.dq_sh;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int j16 = lane & 15;
+
+  // ---- KV iteration space: every KV tile of 64 keys up to the causal limit,
+  // or the two tiles of every 128-key block whose mask bit is set
+  constexpr int kSub = kListBlock / kBN;
+  const int n_kvblk = (len + kListBlock - 1) / kListBlock;
+  const uint32_t *mrow = nullptr;
+  const int m_lim = CAUSAL ? min(n_kvblk, tile + 1) : n_kvblk;
+  const int m_words = (m_lim + 31) >> 5;
+  auto m_valid = [&](int w) -> uint32_t {
+    const int left = m_lim - 32 * w;
+    return left >= 32 ? 0xffffffffu : (left <= 0 ? 0u : ((1u << left) - 1u));
+  };
+  int n_iter;
+  if (MODE == kMask) {
+    mrow = p.mask + b * p.mask_ss + kvh * p.mask_sh + (int64_t)tile * p.mask_words;
+    int n_blk = 0;
+    for (int w = 0; w < m_words; ++w) n_blk += __builtin_popcount(mrow[w] & m_valid(w));
+    n_iter = n_blk * kSub;
+  } else {
+    const int kv_end = CAUSAL ? min(len, q0 + kBM) : len;
+    n_iter = (kv_end + kBN - 1) / kBN;
+  }
+  int m_w = -1;
+  uint32_t m_bits = 0;
+  int m_blk = 0;
+  auto kv_start = [&](int it) -> int {  // called for it = 0, 1, 2, ... in order
+    if (MODE == kDense) return it * kBN;
+    if (it % kSub == 0) {
+      while (m_bits == 0) {
+        if (++m_w >= m_words) return -1;
+        m_bits = mrow[m_w] & m_valid(m_w);
+      }
+      m_blk = 32 * m_w + __builtin_ctz(m_bits);
+      m_bits &= m_bits - 1u;
+    }
+    return m_blk * kListBlock + (it % kSub) * kBN;
+  };
+
+  // ---- direct global -> LDS loads of one KV tile (K in the dual layout, V in
+  // the row-read layout); rows past the end of the sequence re-read the last
+  // row (finite data; those keys are masked)
+  int64_t koff[kLoads], voff[kLoads];
+  int lrow[kLoads];
+  const int slot_byte0 = wave * kLoads * 1024;
+#pragma unroll
+  for (int n = 0; n < kLoads; ++n) {
+    const int slot = (wave * kLoads + n) * 64 + lane;
+    const int r = slot / kChunks, pc = slot % kChunks;
+    lrow[n] = r;
+    koff[n] = (int64_t)r * p.k_ss + (pc ^ LK::f(r)) * 8;
+    voff[n] = (int64_t)r * p.v_ss + (pc ^ LV::kswz(r)) * 8;
+  }
+  auto issue = [&](int buf, int kv) {
+    char *kb = smem + buf * kBufBytes + slot_byte0;
+    issue_pair<kLoads>(kb, kb + kTileBytes, kg + (int64_t)kv * p.k_ss, vg + (int64_t)kv * p.v_ss,
+                       koff, voff, lrow, p.k_ss, p.v_ss, len - kv);
+  };
+
+  int kv_cur = n_iter > 0 ? kv_start(0) : -1;
+  if (kv_cur >= 0) issue(0, kv_cur);
+
+  // ---- this lane's query row: Q and dO as MFMA B operands (head-dim values
+  // 16 dc + 8 hi .. +7), D = dO.O and the base-2 LSE; rows past the end read
+  // as zero and get P = 0 (LSE +inf)
+  const int qrow = q0 + wave * 32 + l32;
+  const int wq_last = q0 + wave * 32 + 31;
+  bf16x8_t qreg[kDc], greg[kDc];
+  float dpart = 0.f;
+#pragma unroll
+  for (int dc = 0; dc < kDc; ++dc) {
+    uint4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u}, z = {0u, 0u, 0u, 0u};
+    if (qrow < len) {
+      x = ld_global16(qg + (int64_t)qrow * p.q_ss + dc * 16 + hi * 8);
+      y = ld_global16(gg + (int64_t)qrow * p.g_ss + dc * 16 + hi * 8);
+      z = ld_global16(og + (int64_t)qrow * p.o_ss + dc * 16 + hi * 8);
+    }
+    qreg[dc] = __builtin_bit_cast(bf16x8_t, x);
+    greg[dc] = __builtin_bit_cast(bf16x8_t, y);
+    dpart += dot8(y, z);
+  }
+  const float drow = half_sum(dpart);
+  float lse2 = INFINITY;
+  if (qrow < len) {
+    const float l = p.lse[lse_index(p, b, h, tok0, total, qrow)];
+    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    if (hi == 0) {
+      const int64_t w = ws_index(p, b, h, qrow);
+      p.ws_lse2[w] = lse2;
+      p.ws_d[w] = drow;
+    }
+  }
+
+  floatx16_t acc[kDt];
+#pragma unroll
+  for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+
+  // per-lane LDS offsets: row-wise reads of K and V (row l32, chunk 2 dc + hi)
+  // and the two transpose reads of K^T (rows 4 hi + j16/4 and 8 more, the
+  // 4 columns at 32 dt + 16 (l32/16) + 4 (j16%4))
+  int kaddr[kDc], vaddr[kDc];
+  uint32_t ta[kDt], tb[kDt];
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char_t *)smem;
+#pragma unroll
+  for (int dc = 0; dc < kDc; ++dc) {
+    kaddr[dc] = LK::at(l32, 2 * dc + hi);
+    vaddr[dc] = LV::kq(l32, 2 * dc + hi);
+    asm volatile("" : "+v"(kaddr[dc]));
+    asm volatile("" : "+v"(vaddr[dc]));
+  }
+#pragma unroll
+  for (int dt = 0; dt < kDt; ++dt) {
+    const int ch = 4 * dt + 2 * (l32 >> 4) + ((j16 & 3) >> 1);
+    ta[dt] = smem_lds + LK::at(4 * hi + (j16 >> 2), ch) + (j16 & 1) * 8;
+    tb[dt] = smem_lds + LK::at(8 + 4 * hi + (j16 >> 2), ch) + (j16 & 1) * 8;
+    asm volatile("" : "+v"(ta[dt]));
+    asm volatile("" : "+v"(tb[dt]));
+  }
+
+  auto step = [&](const int it, auto buf_tag) {
+    constexpr int kBuf = decltype(buf_tag)::value;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    int kv_nxt = -1;
+    if (it + 1 < n_iter) {
+      kv_nxt = kv_start(it + 1);
+      if (kv_nxt >= 0) issue(1 - kBuf, kv_nxt);
+    }
+    const int kv0 = kv_cur;
+    kv_cur = kv_nxt;
+    if (kv0 < 0) return;
+    if (CAUSAL && kv0 > wq_last) return;
+    const char *sK = smem + kBuf * kBufBytes;
+    const char *sV = sK + kTileBytes;
+
+    const bool need_mask = (kv0 + kBN > len) || (CAUSAL && kv0 + kBN - 1 > q0 + wave * 32);
+    // one 32-key half of the tile at a time (bounds the live registers)
+    static_for<kKt>([&](auto KT) {
+      constexpr int kt = decltype(KT)::value;
+      if (CAUSAL && kv0 + kt * 32 > wq_last) return;  // this half lies above every row
+      // ---- S^T = K Q^T and dP^T = V dO^T (32 keys x 32 query rows)
+      floatx16_t s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = 0.f;
+        dp[i] = 0.f;
+      }
+#pragma unroll
+      for (int dc = 0; dc < kDc; ++dc) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(sK + kaddr[dc] + kt * 32 * kRowBytes);
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(sV + vaddr[dc] + kt * 32 * kRowBytes);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, greg[dc], dp, 0, 0, 0);
+      }
+      // ---- P^T = 2^(c s - lse2) with the causal diagonal and sequence tail
+      // masked, dS^T = P^T (dP^T - D), rounded to bf16 in the B operand
+      // layout (MFMA k index e of step c = key 32 kt + 16 c + 8 (e/4) +
+      // 4 hi + e%4)
+      bf16x8_t dsb[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -lse2));
+        if (need_mask) {
+          const int key = kv0 + kt * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+          if (key >= len || (CAUSAL && key > qrow)) pv = 0.f;
+        }
+        dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - drow));
+      }
+      // ---- dQ^T += K^T dS^T
+      static_for<kDt * 2>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int dt = i % kDt, c = i / kDt;
+        constexpr int off = kBuf * kBufBytes + (32 * kt + 16 * c) * kRowBytes;
+        bf16x8_t a = tr_pair2<off>(ta[dt], tb[dt]);
+        lgkm_wait<0>(a);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[c], acc[dt], 0, 0, 0);
+      });
+    });
+  };
+  for (int it = 0; it < n_iter; it += 2) {
+    step(it, BufTag<0>{});
+    if (it + 1 < n_iter) step(it + 1, BufTag<1>{});
+  }
+
+  // ---- epilogue: dQ = scale * acc in bf16, written through LDS so that 16
+  // consecutive lanes store one whole row with 16-byte stores
+  __syncthreads();
+  {
+    constexpr int kRowsPerStore = 1024 / kRowBytes;
+    char *so = smem + wave * 32 * kRowBytes;
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const floatx2_t f01 = {acc[dt][g4 * 4 + 0] * p.scale, acc[dt][g4 * 4 + 1] * p.scale};
+        const floatx2_t f23 = {acc[dt][g4 * 4 + 2] * p.scale, acc[dt][g4 * 4 + 3] * p.scale};
+        uint2_t w;
+        w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f01, bf16x2_t));
+        w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f23, bf16x2_t));
+        const int ch = (dt * 4 + g4) ^ (l32 % kChunks);
+        *reinterpret_cast<uint2_t *>(so + l32 * kRowBytes + ch * 16 + hi * 8) = w;
+      }
+    constexpr int kStores = 32 / kRowsPerStore;
+    const int r0 = lane / kChunks;
+    const int ch = lane % kChunks;
+    uint16_t *orow = dqg + (int64_t)(q0 + wave * 32 + r0) * p.dq_ss + ch * 8;
+    const int64_t step_rows = (int64_t)kRowsPerStore * p.dq_ss;
+#pragma unroll
+    for (int k = 0; k < kStores; ++k) {
+      const int r = k * kRowsPerStore + r0;
+      const uint4_t x = *reinterpret_cast<const uint4_t *>(so + r * kRowBytes + ((ch ^ (r % kChunks)) * 16));
+      if (q0 + wave * 32 + r < len) *reinterpret_cast<uint4_t *>(orow + k * step_rows) = x;
+    }
+  }
+}
+
+// ===========================================================================
+// dK/dV kernel
+// ===========================================================================
+template <int D, bool CAUSAL, int MODE>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+  using L = Dual<D>;  // Q and dO tiles: row-wise and transpose reads
+  constexpr int kNW = 4;
+  constexpr int kBK = 32 * kNW;  // keys per workgroup
+  constexpr int kBQ = 64;        // query rows per tile
+  constexpr int kRowBytes = D * 2;
+  constexpr int kChunks = D / 8;
+  constexpr int kDc = D / 16;
+  constexpr int kDt = D / 32;
+  constexpr int kTileBytes = kBQ * kRowBytes;
+  constexpr int kVecBytes = kBQ * 4;
+  constexpr int kBufBytes = 2 * kTileBytes + 2 * kVecBytes;  // Q, dO, lse2, D
+  constexpr int kLoads = kTileBytes / 1024 / kNW;
+  static_assert(kLoads * 1024 * kNW == kTileBytes, "tile must split evenly over waves");
+  static_assert(kBQ == 64, "one dword load per lane fills a per-row slice");
+  constexpr int kBitmapBytes = MODE == kMask ? kMaxQBlocks / 8 : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes + kBitmapBytes];
+
+  int tile, unit;
+  decode(p, false, tile, unit);  // causal: low key blocks (most query tiles) first
+  const int b = unit / p.hkv;
+  const int kvh = unit % p.hkv;
+  int64_t tok0 = 0;
+  int len = p.seqlen;
+  if (p.cu) {
+    tok0 = p.cu[b];
+    len = min(p.cu[b + 1] - p.cu[b], p.seqlen);  // seqlen bounds every length
+  }
+  const int k0 = tile * kBK;
+  if (k0 >= len) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int j16 = lane & 15;
+
+  const uint16_t *kg = p.k + (p.cu ? tok0 * p.k_ss : (int64_t)b * p.k_sb) + (int64_t)kvh * p.k_sh;
+  const uint16_t *vg = p.v + (p.cu ? tok0 * p.v_ss : (int64_t)b * p.v_sb) + (int64_t)kvh * p.v_sh;
+  const uint16_t *qbase = p.q + (p.cu ? tok0 * p.q_ss : (int64_t)b * p.q_sb);
+  const uint16_t *gbase = p.g + (p.cu ? tok0 * p.g_ss : (int64_t)b * p.g_sb);
+
+  // ---- query iteration space.  Query blocks of 128 that may see this key
+  // block: all, those at or below the diagonal (causal), or those whose mask
+  // row has this block's bit set; each is visited for every query head of the
+  // group, as two tiles of 64 rows.  Step it = (block j, head hh, half sub)
+  // with it = (j * group + hh) * 2 + sub.
+  const int n_qblk = (len + kListBlock - 1) / kListBlock;
+  const int qb_lo = CAUSAL ? tile : 0;
+  uint32_t *bitmap = reinterpret_cast<uint32_t *>(smem + 2 * kBufBytes);
+  int n_vis;
+  if (MODE == kMask) {
+    // column bitmap: bit qb set when row qb of the mask has this key block's bit
+    const uint32_t *mcol = p.mask + b * p.mask_ss + kvh * p.mask_sh + (tile >> 5);
+    for (int base = 0; base < n_qblk; base += 64 * kNW) {
+      const int qb = base + tid;
+      bool bit = false;
+      if (qb < n_qblk && qb >= qb_lo) bit = (mcol[(int64_t)qb * p.mask_words] >> (tile & 31)) & 1u;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(bit);
+      if (lane == 0 && base + wave * 64 < n_qblk) {
+        bitmap[(base + wave * 64) >> 5] = (uint32_t)bal;
+        if (base + wave * 64 + 32 < n_qblk) bitmap[((base + wave * 64) >> 5) + 1] = (uint32_t)(bal >> 32);
+      }
+    }
+    __syncthreads();
+    n_vis = 0;
+    for (int w = 0; w < (n_qblk + 31) >> 5; ++w) n_vis += __builtin_popcount(bitmap[w]);
+  } else {
+    n_vis = n_qblk - qb_lo;
+  }
+  const int n_iter = n_vis * p.group * 2;
+  int c_w = -1;         // bitmap word being walked
+  uint32_t c_bits = 0;  // its set bits not yet visited
+  int c_blk = qb_lo - 1;
+  // query row start and head of step `it` (called for it = 0, 1, 2, ... in
+  // order); -1 when the tile lies past the end of the sequence
+  auto q_start = [&](int it, int &head) -> int {
+    const int sub = it & 1;
+    const int hh = (it >> 1) % p.group;
+    if ((it >> 1) % p.group == 0 && sub == 0) {
+      if (MODE == kMask) {
+        while (c_bits == 0) c_bits = bitmap[++c_w];
+        c_blk = 32 * c_w + __builtin_ctz(c_bits);
+        c_bits &= c_bits - 1u;
+      } else {
+        ++c_blk;
+      }
+    }
+    head = kvh * p.group + hh;
+    const int q0 = c_blk * kListBlock + sub * kBQ;
+    return q0 < len ? q0 : -1;
+  };
+
+  // ---- direct global -> LDS loads of one query tile: Q and dO rows (dual
+  // layout) and the workspace's lse2 and D of the same rows (waves 0 and 1,
+  // one dword per lane); rows past the end re-read the last row
+  int64_t qoff[kLoads], goff[kLoads];
+  int lrow[kLoads];
+  const int slot_byte0 = wave * kLoads * 1024;
+#pragma unroll
+  for (int n = 0; n < kLoads; ++n) {
+    const int slot = (wave * kLoads + n) * 64 + lane;
+    const int r = slot / kChunks, pc = slot % kChunks;
+    lrow[n] = r;
+    qoff[n] = (int64_t)r * p.q_ss + (pc ^ L::f(r)) * 8;
+    goff[n] = (int64_t)r * p.g_ss + (pc ^ L::f(r)) * 8;
+  }
+  auto issue = [&](int buf, int q0, int head) {
+    char *bq = smem + buf * kBufBytes;
+    const uint16_t *qt = qbase + (int64_t)head * p.q_sh + (int64_t)q0 * p.q_ss;
+    const uint16_t *gt = gbase + (int64_t)head * p.g_sh + (int64_t)q0 * p.g_ss;
+    const int rows_left = len - q0;
+    issue_pair<kLoads>(bq + slot_byte0, bq + kTileBytes + slot_byte0, qt, gt, qoff, goff, lrow,
+                       p.q_ss, p.g_ss, rows_left);
+    if (wave < 2) {
+      const int row = q0 + min(lane, rows_left - 1);
+      const float *src = (wave == 0 ? p.ws_lse2 : p.ws_d) + ws_index(p, b, head, row);
+      issue_dwords(bq + 2 * kTileBytes + wave * kVecBytes, src);
+    }
+  };
+
+  int head_cur = 0;
+  int q_cur = n_iter > 0 ? q_start(0, head_cur) : -1;
+  if (q_cur >= 0) issue(0, q_cur, head_cur);
+
+  // ---- K and V rows of this wave's 32 keys as MFMA B operands (lane l32 =
+  // key, head-dim values 16 dc + 8 hi .. +7); keys past the end read as zero
+  const int kw0 = k0 + wave * 32;
+  const int key = kw0 + l32;
+  bf16x8_t kreg[kDc], vreg[kDc];
+#pragma unroll
+  for (int dc = 0; dc < kDc; ++dc) {
+    uint4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (key < len) {
+      x = ld_global16(kg + (int64_t)key * p.k_ss + dc * 16 + hi * 8);
+      y = ld_global16(vg + (int64_t)key * p.v_ss + dc * 16 + hi * 8);
+    }
+    kreg[dc] = __builtin_bit_cast(bf16x8_t, x);
+    vreg[dc] = __builtin_bit_cast(bf16x8_t, y);
+  }
+
+  floatx16_t dk[kDt], dv[kDt];
+#pragma unroll
+  for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dk[dt][i] = 0.f;
+      dv[dt][i] = 0.f;
+    }
+
+  // per-lane LDS offsets: row-wise reads of Q and dO (row l32, chunk
+  // 2 dc + hi) and transpose reads (rows 4 hi + j16/4 and 8 more, the 4
+  // columns at 32 dt + 16 (l32/16) + 4 (j16%4))
+  int raddr[kDc];
+  uint32_t ta[kDt], tb[kDt];
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char_t *)smem;
+#pragma unroll
+  for (int dc = 0; dc < kDc; ++dc) {
+    raddr[dc] = L::at(l32, 2 * dc + hi);
+    asm volatile("" : "+v"(raddr[dc]));
+  }
+#pragma unroll
+  for (int dt = 0; dt < kDt; ++dt) {
+    const int ch = 4 * dt + 2 * (l32 >> 4) + ((j16 & 3) >> 1);
+    ta[dt] = smem_lds + L::at(4 * hi + (j16 >> 2), ch) + (j16 & 1) * 8;
+    tb[dt] = smem_lds + L::at(8 + 4 * hi + (j16 >> 2), ch) + (j16 & 1) * 8;
+    asm volatile("" : "+v"(ta[dt]));
+    asm volatile("" : "+v"(tb[dt]));
+  }
+
+  auto step = [&](const int it, auto buf_tag) {
+    constexpr int kBuf = decltype(buf_tag)::value;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    int q_nxt = -1, head_nxt = 0;
+    if (it + 1 < n_iter) {
+      q_nxt = q_start(it + 1, head_nxt);
+      if (q_nxt >= 0) issue(1 - kBuf, q_nxt, head_nxt);
+    }
+    const int q0 = q_cur;
+    q_cur = q_nxt;
+    if (q0 < 0) return;
+    const char *sQ = smem + kBuf * kBufBytes;
+    const char *sG = sQ + kTileBytes;
+    const float *sL = reinterpret_cast<const float *>(sQ + 2 * kTileBytes);
+    const float *sD = sL + kBQ;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int qh0 = q0 + 32 * half;
+      if (qh0 >= len) continue;
+      if (CAUSAL && qh0 + 31 < kw0) continue;  // every query of the half precedes every key
+      // ---- S = Q K^T and dP = dO V^T (32 query rows x 32 keys; lane = key)
+      floatx16_t s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = 0.f;
+        dp[i] = 0.f;
+      }
+#pragma unroll
+      for (int dc = 0; dc < kDc; ++dc) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(sQ + raddr[dc] + half * 32 * kRowBytes);
+        const bf16x8_t g = *reinterpret_cast<const bf16x8_t *>(sG + raddr[dc] + half * 32 * kRowBytes);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[dc], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g, vreg[dc], dp, 0, 0, 0);
+      }
+      // ---- P = 2^(c s - lse2), dS = P (dP - D); register i holds query row
+      // 8 (i/4) + 4 hi + i%4 of the half
+      const bool need_mask = (qh0 + 32 > len) || (CAUSAL && qh0 < kw0 + 31);
+      bf16x8_t pb[2], dsb[2];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r4 = 32 * half + 8 * g4 + 4 * hi;
+        const float4 l4 = *reinterpret_cast<const float4 *>(sL + r4);
+        const float4 d4 = *reinterpret_cast<const float4 *>(sD + r4);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g4 + e;
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -lv[e]));
+          if (need_mask) {
+            const int qr = q0 + r4 + e;
+            if (qr >= len || (CAUSAL && key > qr)) pv = 0.f;
+          }
+          pb[i >> 3][i & 7] = (__bf16)pv;
+          dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dv4[e]));
+        }
+      }
+      // ---- dV += P^T dO, dK += dS^T Q (B operands by transpose reads: rows
+      // 16 c + 8 (e/4) + 4 hi + e%4 of the half, matching the k order of P)
+      static_for<kDt * 2>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int dt = i % kDt, c = i / kDt;
+        constexpr int offq = kBuf * kBufBytes + c * 16 * kRowBytes;
+        constexpr int offg = offq + kTileBytes;
+        const int hoff = half * 32 * kRowBytes;
+        bf16x8_t go = tr_pair2<offg>(ta[dt] + hoff, tb[dt] + hoff);
+        bf16x8_t qo = tr_pair2<offq>(ta[dt] + hoff, tb[dt] + hoff);
+        lgkm_wait<0>(go);
+        lgkm_wait<0>(qo);
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[c], go, dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsb[c], qo, dk[dt], 0, 0, 0);
+      });
+    }
+  };
+  for (int it = 0; it < n_iter; it += 2) {
+    step(it, BufTag<0>{});
+    if (it + 1 < n_iter) step(it + 1, BufTag<1>{});
+  }
+
+  // ---- epilogue: dK = scale * acc, dV = acc in bf16.  Register i of tile dt
+  // holds key 8 (i/4) + 4 hi + i%4 of the wave, head-dim column 32 dt + l32.
+  uint16_t *dkg = p.dk + (p.cu ? tok0 * p.dk_ss : (int64_t)b * p.dk_sb) + (int64_t)kvh * p.dk_sh;
+  uint16_t *dvg = p.dv + (p.cu ? tok0 * p.dv_ss : (int64_t)b * p.dv_sb) + (int64_t)kvh * p.dv_sh;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int kr = kw0 + (i >> 2) * 8 + hi * 4 + (i & 3);
+    if (kr < len) {
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) {
+        const __bf16 xk = (__bf16)(dk[dt][i] * p.scale);
+        const __bf16 xv = (__bf16)dv[dt][i];
+        dkg[(int64_t)kr * p.dk_ss + 32 * dt + l32] = __builtin_bit_cast(uint16_t, xk);
+        dvg[(int64_t)kr * p.dv_ss + 32 * dt + l32] = __builtin_bit_cast(uint16_t, xv);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+size_t ws_entries(const attn_tensor_t *q) {
+  return (size_t)q->heads * (size_t)q->batch * (size_t)q->seqlen;
+}
+
+int validate_bwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                 const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,
+                 const int32_t *cu, int causal, float scale, const attn_block_mask_t *mask,
+                 const attn_tensor_t *dq, const attn_tensor_t *dk, const attn_tensor_t *dv,
+                 const void *ws, size_t ws_bytes) {
+  if (!dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
+  // q, k, v, out; then dout and dq like out, dk and dv like k and v
+  int st = mask ? attn_fwd_mask_validate(q, k, v, cu, causal, scale, mask, out)
+                : attn_fwd_validate(q, k, v, cu, causal, scale, nullptr, out);
+  if (st != ATTN_OK) return st;
+  st = attn_fwd_validate(q, k, v, cu, causal, scale, nullptr, dout);
+  if (st != ATTN_OK) return st;
+  st = attn_fwd_validate(q, dk, dv, cu, causal, scale, nullptr, dq);
+  if (st != ATTN_OK) return st;
+  if (dk->heads != k->heads) return ATTN_ERR_INVALID_ARG;
+  if (q->head_dim == 256) return ATTN_ERR_UNSUPPORTED;
+  const bool empty = q->batch == 0 || q->seqlen == 0;
+  if (empty) return ATTN_OK;
+  if (!lse || !ws) return ATTN_ERR_INVALID_ARG;
+  if (ws_bytes < 2 * sizeof(float) * ws_entries(q)) return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)ws & 15u) != 0) return ATTN_ERR_UNSUPPORTED;
+  if (mask && (q->seqlen + kListBlock - 1) / kListBlock > kMaxQBlocks) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+template <int D, bool CAUSAL, int MODE>
+int launch_pair(BwdParams p, hipStream_t s) {
+  const int n_tiles = (p.seqlen + 127) / 128;
+  // dQ: one workgroup per 128-row query tile of each (sequence, query head)
+  p.n_tiles = n_tiles;
+  p.n_units = p.batch * p.hq;
+  p.unit_group = p.group;
+  p.xcd_remap = (p.n_units % (8 * p.group)) == 0 ? 1 : 0;
+  {
+    void *args[] = {&p};
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void *>(&attn_bwd_dq_kernel<D, CAUSAL, MODE>),
+        dim3((unsigned)((int64_t)n_tiles * p.n_units)), dim3(256), args, 0, s);
+    if (e != hipSuccess) return ATTN_ERR_LAUNCH;
+  }
+  // dK/dV: one workgroup per 128-key block of each (sequence, KV head)
+  p.n_units = p.batch * p.hkv;
+  p.unit_group = 1;
+  p.xcd_remap = (p.n_units % 8) == 0 ? 1 : 0;
+  {
+    void *args[] = {&p};
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void *>(&attn_bwd_dkdv_kernel<D, CAUSAL, MODE>),
+        dim3((unsigned)((int64_t)n_tiles * p.n_units)), dim3(256), args, 0, s);
+    if (e != hipSuccess) return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
+template <int D>
+int launch_d(const BwdParams &p, bool causal, bool masked, hipStream_t s) {
+  if (masked) return causal ? launch_pair<D, true, kMask>(p, s) : launch_pair<D, false, kMask>(p, s);
+  return causal ? launch_pair<D, true, kDense>(p, s) : launch_pair<D, false, kDense>(p, s);
+}
+
+}  // namespace
+
+extern "C" size_t attn_bwd_workspace_size(const attn_tensor_t *q) {
+  if (!q || q->batch <= 0 || q->seqlen <= 0 || q->heads <= 0) return 0;
+  return 2 * sizeof(float) * ws_entries(q);
+}
+
+extern "C" int attn_bwd_validate(const attn_tensor_t *q, const attn_tensor_t *k,
+                                 const attn_tensor_t *v, const attn_tensor_t *out,
+                                 const attn_tensor_t *dout, const float *lse,
+                                 const int32_t *cu_seqlens, int causal, float scale,
+                                 const attn_block_mask_t *mask, const attn_tensor_t *dq,
+                                 const attn_tensor_t *dk, const attn_tensor_t *dv,
+                                 const void *workspace, size_t workspace_bytes) {
+  return validate_bwd(q, k, v, out, dout, lse, cu_seqlens, causal, scale, mask, dq, dk, dv,
+                      workspace, workspace_bytes);
+}
+
+extern "C" int attn_bwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                        const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,
+                        const int32_t *cu_seqlens, int causal, float scale,
+                        const attn_block_mask_t *mask, attn_tensor_t *dq, attn_tensor_t *dk,
+                        attn_tensor_t *dv, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  const int st = validate_bwd(q, k, v, out, dout, lse, cu_seqlens, causal, scale, mask, dq, dk,
+                              dv, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (q->batch == 0 || q->seqlen == 0) return ATTN_OK;
+  BwdParams p;
+  p.q = static_cast<const uint16_t *>(q->data);
+  p.k = static_cast<const uint16_t *>(k->data);
+  p.v = static_cast<const uint16_t *>(v->data);
+  p.o = static_cast<const uint16_t *>(out->data);
+  p.g = static_cast<const uint16_t *>(dout->data);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t *>(dq->data);
+  p.dk = static_cast<uint16_t *>(dk->data);
+  p.dv = static_cast<uint16_t *>(dv->data);
+  p.ws_lse2 = static_cast<float *>(workspace);
+  p.ws_d = p.ws_lse2 + ws_entries(q);
+  p.q_sb = q->stride_batch; p.q_ss = q->stride_seq; p.q_sh = q->stride_head;
+  p.k_sb = k->stride_batch; p.k_ss = k->stride_seq; p.k_sh = k->stride_head;
+  p.v_sb = v->stride_batch; p.v_ss = v->stride_seq; p.v_sh = v->stride_head;
+  p.o_sb = out->stride_batch; p.o_ss = out->stride_seq; p.o_sh = out->stride_head;
+  p.g_sb = dout->stride_batch; p.g_ss = dout->stride_seq; p.g_sh = dout->stride_head;
+  p.dq_sb = dq->stride_batch; p.dq_ss = dq->stride_seq; p.dq_sh = dq->stride_head;
+  p.dk_sb = dk->stride_batch; p.dk_ss = dk->stride_seq; p.dk_sh = dk->stride_head;
+  p.dv_sb = dv->stride_batch; p.dv_ss = dv->stride_seq; p.dv_sh = dv->stride_head;
+  p.cu = cu_seqlens;
+  p.mask = mask ? mask->bits : nullptr;
+  p.mask_ss = mask ? mask->stride_seq : 0;
+  p.mask_sh = mask ? mask->stride_head : 0;
+  p.mask_words = mask ? mask->words_per_row : 0;
+  p.batch = q->batch;
+  p.seqlen = q->seqlen;
+  p.hq = q->heads;
+  p.hkv = k->heads;
+  p.group = q->heads / k->heads;
+  p.n_tiles = p.n_units = p.unit_group = p.xcd_remap = 0;  // set per kernel at launch
+  p.c = scale * kLog2e;
+  p.scale = scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (q->head_dim == 64) return launch_d<64>(p, causal != 0, mask != nullptr, s);
+  return launch_d<128>(p, causal != 0, mask != nullptr, s);
+}

@@ -24,29 +24,16 @@
 
 #include <utility>
 
+#include "attn_common.h"
 #include "attn_fwd.h"
 
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(16))) float floatx16_t;
-typedef __attribute__((ext_vector_type(4))) unsigned int uint4_t;
-typedef __attribute__((ext_vector_type(2))) unsigned int uint2_t;
-typedef __attribute__((ext_vector_type(2))) float floatx2_t;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) char lds_char_t;
+using namespace attn_detail;
 
-constexpr int kListBlock = 128;  // block-list / block-mask granularity (rows and keys)
-// KV iteration modes: every key, an ordered block list, a bit-packed block mask
-enum { kDense = 0, kList = 1, kMask = 2 };
-constexpr float kLn2 = 0.69314718055994530942f;
 // A tile's P is accepted against the running max while every row sum of the
 // tile stays at or below this (so every P is at most 2^12).
 constexpr float kFastSum = 4096.f;
-// s_waitcnt immediate that waits for vmcnt == 0 and leaves the other counters
-// free (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
-constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 
 struct Params {
   const uint16_t *q, *k, *v;
@@ -69,39 +56,6 @@ struct Params {
   float c;       // scale * log2(e)
 };
 
-// ---------------------------------------------------------------------------
-// LDS layouts (rows of D bf16 values; bank behaviour measured with the
-// SQ_LDS_BANK_CONFLICT counter on gfx950).
-//  K and Q: 16 B chunks XOR-swizzled by row, so the 16 consecutive rows that
-//    one MFMA operand read touches at one logical chunk hit 16 distinct
-//    4-bank groups (ds_read_b128, conflict-free).
-//  V: 64 B pairs of 32 B units XOR-swizzled by row, so the 4 rows x 64 B that
-//    32 lanes of one transpose read touch land in 4 distinct 64 B bank ranges
-//    (ds_read_b64_tr_b16, conflict-free).
-// ---------------------------------------------------------------------------
-template <int D>
-struct Lds {
-  static constexpr int kRowBytes = D * 2;
-  static constexpr int kChunks = D / 8;                       // 16 B chunks per row
-  static constexpr int kRowsPerWin = kRowBytes >= 256 ? 1 : 256 / kRowBytes;
-  static constexpr int kPairs = D / 32;                       // 64 B pairs per row
-  static constexpr int kPairSwz = kPairs < 4 ? kPairs : 4;
-  __device__ static __forceinline__ int kswz(int r) { return (r / kRowsPerWin) % kChunks; }
-  // byte offset of 16 B chunk `c` of row `r` (K / Q layout)
-  __device__ static __forceinline__ int kq(int r, int c) {
-    return r * kRowBytes + ((c ^ kswz(r)) << 4);
-  }
-  __device__ static __forceinline__ int vswz(int r) { return (r / kRowsPerWin) % kPairSwz; }
-  // byte offset of byte `b` (0..31) of 32 B unit `u` of row `r` (V layout)
-  __device__ static __forceinline__ int vv(int r, int u, int b) {
-    return r * kRowBytes + ((((u >> 1) ^ vswz(r)) << 6) | ((u & 1) << 5)) + b;
-  }
-  // logical 16 B chunk that the V layout stores in physical chunk `pc` of row `r`
-  __device__ static __forceinline__ int v_logical_chunk(int r, int pc) {
-    return ((((pc >> 2) ^ vswz(r))) << 2) | (pc & 3);
-  }
-};
-
 // Kernel configuration.  NW wave64s per workgroup, each owning 32 query rows
 // (BM = 32 * NW rows per workgroup); BN keys per KV tile (64, or 32 at head_dim
 // 256 to bound registers and LDS).  Dense and packed problems use 8 waves
@@ -120,76 +74,6 @@ struct Config {
   static_assert(kLoads * 1024 * NW == kTileBytes, "tile must split evenly over waves");
   static constexpr int kMinBlocks = (NW == 4 && D <= 128) ? 2 : 1;  // 2 waves per SIMD
 };
-
-// Compile-time LDS buffer index of a main-loop step.
-template <int B>
-struct BufTag {
-  static constexpr int value = B;
-};
-
-// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, so that i can be
-// used as a template argument (immediate offsets of inline assembly).
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// Byte offset (within a V tile) of the rows read by PV step i: dt = i % kDt,
-// (kt, c) = i / kDt; a step reads 16 keys starting at key 32 kt + 16 c.
-template <class L, int kDt>
-__host__ __device__ constexpr int tr_off(int i) {
-  return ((i / kDt) >> 1) * 32 * L::kRowBytes + ((i / kDt) & 1) * 16 * L::kRowBytes;
-}
-
-// Two LDS transpose reads (rows +0 and +kRow8 bytes apart: keys +0..7 and
-// +8..15 of a 16-key group) forming one MFMA A operand.  Written as inline
-// assembly: the compiler builtin for this read makes the compiler wait for every direct
-// global-to-LDS load in flight before it (the prefetch of the next tile),
-// which the double-buffered layout never needs.  The caller waits for the
-// result with lgkm_wait before using it.
-template <int kOff, int kRow8>
-__device__ __forceinline__ bf16x8_t tr_pair(uint32_t addr) {
-  uint2_t lo, hi;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(addr), "i"(kOff));
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(addr), "i"(kOff + kRow8));
-  const uint4_t packed = {lo.x, lo.y, hi.x, hi.y};
-  return __builtin_bit_cast(bf16x8_t, packed);
-}
-
-// Wait until at most N LDS operations are outstanding; `x` is tied through so
-// its uses cannot move above the wait.
-template <int N>
-__device__ __forceinline__ void lgkm_wait(bf16x8_t &x) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
-}
-
-__device__ __forceinline__ uint4_t ld_global16(const uint16_t *p) {
-  return *reinterpret_cast<const uint4_t *>(p);
-}
-
-// Exchange between the two lane halves: after v_permlane32_swap, `a` holds
-// lanes 0-31 of x in both halves and `b` lanes 32-63 of x in both halves, so
-// a (op) b is the pairwise result for lanes l and l^32 in every lane.  (Inline
-// assembly: the compiler builtin returns the same register for both results.)
-__device__ __forceinline__ void half_pair(float x, float &a, float &b) {
-  a = x;
-  b = x;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ float half_max(float x) {
-  float a, b;
-  half_pair(x, a, b);
-  return fmaxf(a, b);
-}
-__device__ __forceinline__ float half_sum(float x) {
-  float a, b;
-  half_pair(x, a, b);
-  return a + b;
-}
 
 // P = 2^(c s - m) for one tile of scores, rounded to bf16 in the MFMA
 // operand layout; returns this lane's sum of the unrounded P.

@@ -39,7 +39,7 @@ from typing import Optional
 
 import numpy as np
 
-STREAMS = ("q", "k", "v", "lengths", "block_scores", "sample_rows")
+STREAMS = ("q", "k", "v", "lengths", "block_scores", "sample_rows", "dout")
 SPARSE_BLOCK = 128
 
 
@@ -59,7 +59,8 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def streams(seed: int):
-    """The six child generators of ``seed`` in the fixed order of ``STREAMS``."""
+    """The child generators of ``seed`` in the fixed order of ``STREAMS`` (child i depends only
+    on the seed and i, so a stream appended to the tuple leaves the others unchanged)."""
     children = np.random.SeedSequence(seed).spawn(len(STREAMS))
     return {name: np.random.Generator(np.random.PCG64(c)) for name, c in zip(STREAMS, children)}
 
@@ -126,6 +127,12 @@ class Workload:
         t = self.batch * self.seqlen
         return (self.q.reshape(t, self.hq, self.d), self.k.reshape(t, self.hkv, self.d),
                 self.v.reshape(t, self.hkv, self.d))
+
+
+def make_dout(w: "Workload") -> np.ndarray:
+    """Seeded upstream gradient dO for the backward pass: i.i.d. N(0,1) in
+    bfloat16 with the shape of ``w.q`` (uint16 bits)."""
+    return normal_bf16(streams(w.seed)["dout"], w.q.shape)
 
 
 def default_scale(d: int) -> float:

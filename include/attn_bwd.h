@@ -1,0 +1,97 @@
+/*
+ * attn_bwd.h — C ABI of the softmax-attention backward pass (gradients of
+ * the forward in attn_fwd.h) for AMD Instinct MI355X (gfx950).
+ *
+ * The operation
+ * -------------
+ * With the forward's allowed set A(i), P_ij = exp(scale*q_i.k_j - lse_i) for
+ * j in A(i) (0 otherwise), and dO the gradient of a scalar loss with respect
+ * to O, the library computes
+ *
+ *   D_i    = sum_d dO[i,d] * O[i,d]                 (= sum_j P_ij dP_ij)
+ *   dP_ij  = dO_i . v_j
+ *   dS_ij  = P_ij * (dP_ij - D_i)
+ *   dQ_i   = scale * sum_j dS_ij k_j
+ *   dK_j   = scale * sum_{h in the group of j's kv head} sum_i dS_ij q_i
+ *   dV_j   = sum_{h in the group} sum_i P_ij dO_i
+ *
+ * the chain rule of the forward, recomputing P from the saved natural-log
+ * LSE rather than storing it.  The AdaSplash-2 explainer (section 2,
+ * sparsity-aware execution) names a backward pass that visits only the
+ * non-zero blocks of a bit-packed block mask, and (section 4) reports that
+ * pass as the one that gains most from skipping; with a mask, only the 128 x
+ * 128 blocks whose bit is set are loaded here, in both directions.
+ *
+ * Conventions
+ * -----------
+ * As for attn_fwd (attn_fwd.h): device pointers owned by the caller, bf16
+ * tensors with contiguous head_dim and strides in elements, fp32
+ * accumulation, asynchronous on `stream`, no host synchronisation, and the
+ * library allocates nothing: the caller passes a device workspace of at least
+ * attn_bwd_workspace_size(q) bytes (its contents on entry do not matter; the
+ * call overwrites it).  dq, dk, dv are written in bf16 (round to nearest
+ * even) at every valid position, zero where no query sees the key (dk, dv)
+ * or the query sees no key (dq).  Calls that share a workspace must not
+ * overlap.
+ */
+#ifndef ATTN_BWD_H
+#define ATTN_BWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "attn_fwd.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Bytes of workspace attn_bwd needs for query descriptor q: two float32
+ * arrays of q->heads * q->batch * q->seqlen entries (the per-row D and the
+ * base-2 LSE).  0 for an empty problem or a NULL descriptor. */
+size_t attn_bwd_workspace_size(const attn_tensor_t *q);
+
+/*
+ * attn_bwd — gradients of fused attention.
+ *
+ *   q, out, dout  [B, S, Hq, D]  (or packed [T, Hq, D] with cu_seqlens)
+ *   k, v          [B, S, Hkv, D] (or packed [T, Hkv, D])
+ *   lse           float32 [B, Hq, S] (packed: [Hq, T]), the natural-log LSE
+ *                 attn_fwd returned for these q, k, v (a row of -inf, a row
+ *                 that sees no key, gets dq = 0)
+ *   cu_seqlens, causal, scale   as for attn_fwd
+ *   mask          NULL (dense or causal), or a bit-packed block mask as for
+ *                 attn_fwd_mask; the same mask the forward used
+ *   dq            [B, S, Hq, D];  dk, dv [B, S, Hkv, D] (packed: [T, H, D])
+ *   workspace     device memory of workspace_bytes >= attn_bwd_workspace_size(q)
+ *   stream        hipStream_t to enqueue on
+ *
+ * Returns ATTN_OK, or:
+ *   ATTN_ERR_INVALID_ARG  what attn_fwd rejects for q, k, v, out (plus dout
+ *                         and dq like out, dk and dv like k); lse == NULL or
+ *                         workspace == NULL or workspace_bytes too small for
+ *                         a non-empty problem; a bad mask descriptor
+ *   ATTN_ERR_UNSUPPORTED  what attn_fwd does not support; head_dim 256; with
+ *                         a mask, more than 16384 blocks of 128 per sequence
+ *   ATTN_ERR_LAUNCH       a kernel launch failed
+ * An empty problem returns ATTN_OK and launches nothing.
+ */
+int attn_bwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+             const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,
+             const int32_t *cu_seqlens, int causal, float scale, const attn_block_mask_t *mask,
+             attn_tensor_t *dq, attn_tensor_t *dk, attn_tensor_t *dv, void *workspace,
+             size_t workspace_bytes, void *stream);
+
+/* The argument checks of attn_bwd alone: host code only, no HIP call. */
+int attn_bwd_validate(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                      const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,
+                      const int32_t *cu_seqlens, int causal, float scale,
+                      const attn_block_mask_t *mask, const attn_tensor_t *dq,
+                      const attn_tensor_t *dk, const attn_tensor_t *dv, const void *workspace,
+                      size_t workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_BWD_H */

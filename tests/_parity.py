@@ -105,3 +105,72 @@ def check_workload(w: W.Workload, rows=None, layout: str = "bshd", nthreads: int
     if rows is not None:
         o, l = o[rows], l[rows]
     return compare(o, l, o_ref, l_ref, w.name)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass
+# ---------------------------------------------------------------------------
+# Gradient tolerances, per tensor: the GPU rounds P and dS to bf16 for the
+# MFMAs and dq/dk/dv to bf16 on output (relative error 2^-9 each, random
+# sign), and forms D from the bf16 forward output; the relative RMS error of
+# a sum of such terms stays near 2^-9 ~ 2e-3.  The bounds leave a factor of
+# about 5 on that.
+G_REL_RMS = 1e-2   # ||g - g_ref||_2 / ||g_ref||_2
+G_MAX_REL = 2e-2   # max |g - g_ref| / max |g_ref|
+
+
+def bf16_tensor(a, dev, layout="bshd"):
+    import torch
+    x = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    if layout == "bhsd" and x.dim() == 4:
+        x = x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    return x
+
+
+def run_gpu_bwd(w: W.Workload, dout_bits, layout: str = "bshd", repeat: int = 1):
+    """GPU forward then backward on the workload; returns dq, dk, dv as float64
+    in packed order ([T, H, D]), one triple per repeat."""
+    import torch
+    import attention_forward_flashattention_amd as attn
+
+    q, k, v, cu, sp = to_device(w, layout)
+    if "block_list" in sp:
+        raise ValueError("the backward takes a block mask, not a block list")
+    do = bf16_tensor(dout_bits, q.device, layout)
+    ms = w.seqlen if cu is not None else None
+    out, lse = attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale, max_seqlen=ms, **sp)
+    res = []
+    for _ in range(repeat):
+        dq, dk, dv = attn.attn_bwd(q, k, v, out, do, lse, cu_seqlens=cu, causal=w.causal, scale=w.scale,
+                                   max_seqlen=ms, block_mask=sp.get("block_mask"))
+        torch.cuda.synchronize()
+        t = w.tokens
+        res.append(tuple(x.float().cpu().numpy().astype(np.float64).reshape(t, x.shape[-2], w.d)
+                         for x in (dq, dk, dv)))
+    return res if repeat > 1 else res[0]
+
+
+def oracle_bwd(w: W.Workload, dout_bits, nthreads: int = 0):
+    """fp64 oracle gradients on the same bf16 inputs, packed order."""
+    import oracle
+    from attn_workloads import bf16_bits_to_f32
+
+    q, k, v = w.packed_views()
+    f = lambda a: bf16_bits_to_f32(a).astype(np.float64)
+    do = f(dout_bits).reshape(q.shape)
+    return oracle.attn_bwd(f(q), f(k), f(v), do, w.cu_seqlens_or_fixed(), w.causal, w.scale,
+                           w.block_mask, 128, nthreads)
+
+
+def compare_grads(got, ref, label=""):
+    """Check the gradient tolerances on (dq, dk, dv); returns the error statistics."""
+    stats = {}
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        assert np.all(np.isfinite(g)), f"{label}: non-finite {name}"
+        nrm = np.linalg.norm(r)
+        err = np.abs(g - r)
+        rel_rms = float(np.linalg.norm(g - r) / nrm) if nrm > 0 else float(np.linalg.norm(g))
+        max_rel = float(err.max() / np.abs(r).max()) if np.abs(r).max() > 0 else float(err.max())
+        stats[name] = (rel_rms, max_rel)
+        assert rel_rms <= G_REL_RMS and max_rel <= G_MAX_REL, (label, name, stats[name])
+    return stats
