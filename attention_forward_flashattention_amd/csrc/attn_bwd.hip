@@ -129,6 +129,18 @@ __device__ __forceinline__ void issue_pair(char *la, char *lb, const uint16_t *a
   }
 }
 
+// issue_pair for a tile wholly inside the sequence (no row clamping).
+template <int kLoads>
+__device__ __forceinline__ void issue_pair_full(char *la, char *lb, const uint16_t *a,
+                                                const uint16_t *b, const int64_t *aoff,
+                                                const int64_t *boff) {
+#pragma unroll
+  for (int n = 0; n < kLoads; ++n) {
+    __builtin_amdgcn_global_load_lds(a + aoff[n], (lds_void_t *)(la + n * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(b + boff[n], (lds_void_t *)(lb + n * 1024), 16, 0, 0);
+  }
+}
+
 // One dword per lane from global to 64 consecutive LDS dwords.
 __device__ __forceinline__ void issue_dwords(char *l, const float *src) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t *)l, 4, 0, 0);
@@ -403,8 +415,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 // ===========================================================================
 // dK/dV kernel
 // ===========================================================================
+// Workgroups per CU: at head_dim 128 the K/V operands and the dK/dV
+// accumulators of a wave's 32 keys take ~380 registers, so one wave per SIMD;
+// at head_dim 64 half that, and two workgroups share a CU.
+template <int D>
+constexpr int dkdv_min_blocks() {
+  return D == 64 ? 2 : 1;
+}
+
 template <int D, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kernel(BwdParams p) {
   using L = Dual<D>;  // Q and dO tiles: row-wise and transpose reads
   constexpr int kNW = 4;
   constexpr int kBK = 32 * kNW;  // keys per workgroup
@@ -480,7 +500,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   uint32_t c_bits = 0;  // its set bits not yet visited
   int c_blk = qb_lo - 1;
   // query row start and head of step `it` (called for it = 0, 1, 2, ... in
-  // order); -1 when the tile lies past the end of the sequence
+  // order)
   auto q_start = [&](int it, int &head) -> int {
     const int sub = it & 1;
     const int hh = (it >> 1) % p.group;
@@ -494,8 +514,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       }
     }
     head = kvh * p.group + hh;
-    const int q0 = c_blk * kListBlock + sub * kBQ;
-    return q0 < len ? q0 : -1;
+    // a tile past the end of the sequence is loaded from the last row and
+    // computed fully masked, so the step has no branch around the
+    // accumulators (which would make the compiler copy them)
+    return c_blk * kListBlock + sub * kBQ;
   };
 
   // ---- direct global -> LDS loads of one query tile: Q and dO rows (dual
@@ -517,8 +539,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     const uint16_t *qt = qbase + (int64_t)head * p.q_sh + (int64_t)q0 * p.q_ss;
     const uint16_t *gt = gbase + (int64_t)head * p.g_sh + (int64_t)q0 * p.g_ss;
     const int rows_left = len - q0;
-    issue_pair<kLoads>(bq + slot_byte0, bq + kTileBytes + slot_byte0, qt, gt, qoff, goff, lrow,
-                       p.q_ss, p.g_ss, rows_left);
+    if (rows_left >= kBQ)
+      issue_pair_full<kLoads>(bq + slot_byte0, bq + kTileBytes + slot_byte0, qt, gt, qoff, goff);
+    else
+      issue_pair<kLoads>(bq + slot_byte0, bq + kTileBytes + slot_byte0, qt, gt, qoff, goff, lrow,
+                         p.q_ss, p.g_ss, rows_left);
     if (wave < 2) {
       const int row = q0 + min(lane, rows_left - 1);
       const float *src = (wave == 0 ? p.ws_lse2 : p.ws_d) + ws_index(p, b, head, row);
@@ -527,8 +552,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   };
 
   int head_cur = 0;
-  int q_cur = n_iter > 0 ? q_start(0, head_cur) : -1;
-  if (q_cur >= 0) issue(0, q_cur, head_cur);
+  int q_cur = 0;
+  if (n_iter > 0) {
+    q_cur = q_start(0, head_cur);
+    issue(0, q_cur, head_cur);
+  }
 
   // ---- K and V rows of this wave's 32 keys as MFMA B operands (lane l32 =
   // key, head-dim values 16 dc + 8 hi .. +7); keys past the end read as zero
@@ -575,85 +603,112 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     asm volatile("" : "+v"(tb[dt]));
   }
 
-  auto step = [&](const int it, auto buf_tag) {
-    constexpr int kBuf = decltype(buf_tag)::value;
+  // One query tile per step; the LDS buffer alternates at run time, so the
+  // loop body (and the register assignment of the accumulators) exists once.
+  auto step = [&](const int it, const int buf) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    int q_nxt = -1, head_nxt = 0;
+    int q_nxt = 0, head_nxt = 0;
     if (it + 1 < n_iter) {
       q_nxt = q_start(it + 1, head_nxt);
-      if (q_nxt >= 0) issue(1 - kBuf, q_nxt, head_nxt);
+      issue(1 - buf, q_nxt, head_nxt);
     }
     const int q0 = q_cur;
     q_cur = q_nxt;
-    if (q0 < 0) return;
-    const char *sQ = smem + kBuf * kBufBytes;
-    const char *sG = sQ + kTileBytes;
-    const float *sL = reinterpret_cast<const float *>(sQ + 2 * kTileBytes);
-    const float *sD = sL + kBQ;
-#pragma unroll
+    const int boff = buf * kBufBytes;
+#pragma unroll 1
     for (int half = 0; half < 2; ++half) {
       const int qh0 = q0 + 32 * half;
-      if (qh0 >= len) continue;
-      if (CAUSAL && qh0 + 31 < kw0) continue;  // every query of the half precedes every key
-      // ---- S = Q K^T and dP = dO V^T (32 query rows x 32 keys; lane = key)
+      const int hoff = boff + half * 32 * kRowBytes;  // row 0 of this half in the Q tile
+      const char *sQ = smem + hoff;
+      // lse2 and D of this lane's 16 rows (register i: row 8 (i/4) + 4 hi + i%4)
+      const float *sL = reinterpret_cast<const float *>(smem + boff + 2 * kTileBytes) + 32 * half;
+      float4 l4[4], d4[4];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        l4[g4] = *reinterpret_cast<const float4 *>(sL + 8 * g4 + 4 * hi);
+        d4[g4] = *reinterpret_cast<const float4 *>(sL + kBQ + 8 * g4 + 4 * hi);
+      }
+      // ---- S = Q K^T and dP = dO V^T (32 query rows x 32 keys; lane = key).
+      // Operand reads run kRing MFMAs ahead; S and dP alternate.
       floatx16_t s, dp;
+      {
+        constexpr int kRing = 4;
+        constexpr int kSteps = 2 * kDc;  // step i: dc = i / 2, Q (even) or dO (odd)
+        auto load = [&](int i) {
+          return *reinterpret_cast<const bf16x8_t *>(sQ + raddr[i >> 1] + (i & 1) * kTileBytes);
+        };
+        bf16x8_t ring[kRing];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] = 0.f;
-        dp[i] = 0.f;
-      }
+        for (int i = 0; i < kRing; ++i) ring[i] = load(i);
 #pragma unroll
-      for (int dc = 0; dc < kDc; ++dc) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(sQ + raddr[dc] + half * 32 * kRowBytes);
-        const bf16x8_t g = *reinterpret_cast<const bf16x8_t *>(sG + raddr[dc] + half * 32 * kRowBytes);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kreg[dc], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g, vreg[dc], dp, 0, 0, 0);
+        for (int i = 0; i < kSteps; ++i) {
+          const int dc = i >> 1;
+          if (i & 1)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], vreg[dc], dc == 0 ? floatx16_t{} : dp, 0, 0, 0);
+          else
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], kreg[dc], dc == 0 ? floatx16_t{} : s, 0, 0, 0);
+          if (i + kRing < kSteps) ring[i % kRing] = load(i + kRing);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      // ---- P = 2^(c s - lse2), dS = P (dP - D); register i holds query row
-      // 8 (i/4) + 4 hi + i%4 of the half
+      // ---- P = 2^(c s - lse2), dS = P (dP - D); rows past the end and keys
+      // after their query (causal) get P = 0
       const bool need_mask = (qh0 + 32 > len) || (CAUSAL && qh0 < kw0 + 31);
       bf16x8_t pb[2], dsb[2];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int r4 = 32 * half + 8 * g4 + 4 * hi;
-        const float4 l4 = *reinterpret_cast<const float4 *>(sL + r4);
-        const float4 d4 = *reinterpret_cast<const float4 *>(sD + r4);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float lv[4] = {l4[g4].x, l4[g4].y, l4[g4].z, l4[g4].w};
+        const float dv4[4] = {d4[g4].x, d4[g4].y, d4[g4].z, d4[g4].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * g4 + e;
           float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -lv[e]));
-          if (need_mask) {
-            const int qr = q0 + r4 + e;
-            if (qr >= len || (CAUSAL && key > qr)) pv = 0.f;
-          }
+          const int qr = qh0 + 8 * g4 + 4 * hi + e;
+          if (need_mask && (qr >= len || (CAUSAL && key > qr))) pv = 0.f;
           pb[i >> 3][i & 7] = (__bf16)pv;
           dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dv4[e]));
         }
       }
-      // ---- dV += P^T dO, dK += dS^T Q (B operands by transpose reads: rows
-      // 16 c + 8 (e/4) + 4 hi + e%4 of the half, matching the k order of P)
-      static_for<kDt * 2>([&](auto I) {
-        constexpr int i = decltype(I)::value;
-        constexpr int dt = i % kDt, c = i / kDt;
-        constexpr int offq = kBuf * kBufBytes + c * 16 * kRowBytes;
-        constexpr int offg = offq + kTileBytes;
-        const int hoff = half * 32 * kRowBytes;
-        bf16x8_t go = tr_pair2<offg>(ta[dt] + hoff, tb[dt] + hoff);
-        bf16x8_t qo = tr_pair2<offq>(ta[dt] + hoff, tb[dt] + hoff);
-        lgkm_wait<0>(go);
-        lgkm_wait<0>(qo);
-        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[c], go, dv[dt], 0, 0, 0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsb[c], qo, dk[dt], 0, 0, 0);
-      });
+      // ---- dV += P^T dO and dK += dS^T Q.  B operands by transpose reads of
+      // rows 16 c + 8 (e/4) + 4 hi + e%4 of the half (the k order of P); the
+      // reads run kRing MFMAs ahead
+      {
+        uint32_t ha[kDt], hb[kDt];
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt) {
+          ha[dt] = ta[dt] + hoff;
+          hb[dt] = tb[dt] + hoff;
+        }
+        constexpr int kRing = 4;
+        constexpr int kSteps = kDt * 2 * 2;  // step i: dO (even) or Q (odd); (dt, c) = i / 2
+        bf16x8_t ring[kRing];
+        static_for<kRing>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          constexpr int dt = (i >> 1) % kDt, c = (i >> 1) / kDt;
+          constexpr int off = c * 16 * kRowBytes + ((i & 1) ? 0 : kTileBytes);
+          ring[i] = tr_pair2<off>(ha[dt], hb[dt]);
+        });
+        static_for<kSteps>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          constexpr int dt = (i >> 1) % kDt, c = (i >> 1) / kDt;
+          lgkm_wait<2 * (kSteps - 1 - i < kRing - 1 ? kSteps - 1 - i : kRing - 1)>(ring[i % kRing]);
+          if constexpr (i & 1)
+            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsb[c], ring[i % kRing], dk[dt], 0, 0, 0);
+          else
+            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[c], ring[i % kRing], dv[dt], 0, 0, 0);
+          if constexpr (i + kRing < kSteps) {
+            constexpr int j = i + kRing;
+            constexpr int dtj = (j >> 1) % kDt, cj = (j >> 1) / kDt;
+            constexpr int offj = cj * 16 * kRowBytes + ((j & 1) ? 0 : kTileBytes);
+            ring[i % kRing] = tr_pair2<offj>(ha[dtj], hb[dtj]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
     }
   };
-  for (int it = 0; it < n_iter; it += 2) {
-    step(it, BufTag<0>{});
-    if (it + 1 < n_iter) step(it + 1, BufTag<1>{});
-  }
+  for (int it = 0; it < n_iter; ++it) step(it, it & 1);
 
   // ---- epilogue: dK = scale * acc, dV = acc in bf16.  Register i of tile dt
   // holds key 8 (i/4) + 4 hi + i%4 of the wave, head-dim column 32 dt + l32.

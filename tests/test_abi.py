@@ -1,4 +1,4 @@
-"""The C-ABI library: loads, exports what include/attn_fwd.h declares, and
+"""The C-ABI library: loads, exports what include/*.h declare, and
 rejects bad arguments with the documented status codes (host-only checks; no
 kernel is launched, so these run without a GPU)."""
 import ctypes
@@ -12,17 +12,22 @@ import attention_forward_flashattention_amd as attn
 from attention_forward_flashattention_amd import AttnBlockList, AttnBlockMask, AttnTensor
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+    names = set()
+    for f in sorted(os.listdir(INCLUDE)):
+        if f.endswith(".h"):
+            text = open(os.path.join(INCLUDE, f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_mask", "attn_fwd_mask_validate", "attn_fwd_validate",
+    assert declared_functions() == ["attn_bwd", "attn_bwd_validate", "attn_bwd_workspace_size", "attn_fwd",
+                                    "attn_fwd_mask", "attn_fwd_mask_validate", "attn_fwd_validate",
                                     "attn_status_str", "attn_version"]
 
 
@@ -149,3 +154,67 @@ def test_block_mask_validation():
     # shared checks still apply
     k.heads = 3
     assert validate_mask(q, k, v, mask_desc()) == -1
+
+
+# ---------------------------------------------------------------------------
+# attn_bwd argument checks (host only)
+# ---------------------------------------------------------------------------
+def bwd_validate(q, k, v, out=None, dout=None, dq=None, dk=None, dv=None, lse=FAKE, ws=FAKE,
+                 ws_bytes=None, mask=None, causal=1, scale=0.125, cu=None):
+    lib = attn.load_library()
+    out = out if out is not None else q
+    dout = dout if dout is not None else q
+    dq = dq if dq is not None else q
+    dk = dk if dk is not None else k
+    dv = dv if dv is not None else v
+    if ws_bytes is None:
+        ws_bytes = lib.attn_bwd_workspace_size(ctypes.byref(q))
+    r = lambda t: ctypes.byref(t)
+    return lib.attn_bwd_validate(r(q), r(k), r(v), r(out), r(dout), lse, cu, causal, scale,
+                                 r(mask) if mask is not None else None, r(dq), r(dk), r(dv), ws, ws_bytes)
+
+
+def test_bwd_workspace_size():
+    lib = attn.load_library()
+    assert lib.attn_bwd_workspace_size(ctypes.byref(desc(b=2, s=256, h=8))) == 2 * 4 * 2 * 256 * 8
+    assert lib.attn_bwd_workspace_size(ctypes.byref(desc(b=0))) == 0
+    assert lib.attn_bwd_workspace_size(None) == 0
+
+
+def test_bwd_valid_arguments_pass():
+    assert bwd_validate(desc(), desc(h=2), desc(h=2)) == 0
+    assert bwd_validate(desc(d=64), desc(h=8, d=64), desc(h=8, d=64), causal=0) == 0
+    m = AttnBlockMask(FAKE, 128, 128, 2, 1, 2, 0)
+    assert bwd_validate(desc(), desc(h=2), desc(h=2), mask=m) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lse=None), -1),                                   # no LSE
+    (dict(ws=None), -1),                                    # no workspace
+    (dict(ws_bytes=1024), -1),                              # workspace too small
+    (dict(dq=desc(h=4)), -1),                               # dq heads differ from q
+    (dict(dk=desc(h=4), dv=desc(h=4)), -1),                 # dk/dv heads differ from k
+    (dict(dout=desc(s=128)), -1),                           # dout seqlen differs
+    (dict(dv=desc(h=2, d=64)), -1),                         # dv head_dim differs
+    (dict(ws=FAKE + 4), -2),                                # misaligned workspace
+    (dict(causal=2), -1),
+    (dict(mask=AttnBlockMask(FAKE, 64, 128, 2, 1, 0, 0)), -2),  # block size 64
+])
+def test_bwd_invalid_arguments(kw, code):
+    assert bwd_validate(desc(), desc(h=2), desc(h=2), **kw) == code
+
+
+def test_bwd_unsupported_head_dim_and_long_masked_sequences():
+    assert bwd_validate(desc(d=256), desc(h=2, d=256), desc(h=2, d=256)) == -2
+    s = 128 * 16385  # more query blocks than the key kernel's column bitmap holds
+    q, kv = desc(b=1, s=s, h=1), desc(b=1, s=s, h=1)
+    m = AttnBlockMask(FAKE, 128, 128, 16385, 513, 0, 0)
+    assert bwd_validate(q, kv, desc(b=1, s=s, h=1), mask=m) == -2
+    m2 = AttnBlockMask(FAKE, 128, 128, 16384, 512, 0, 0)
+    s2 = 128 * 16384
+    assert bwd_validate(desc(b=1, s=s2, h=1), desc(b=1, s=s2, h=1), desc(b=1, s=s2, h=1), mask=m2) == 0
+
+
+def test_bwd_empty_problem_needs_no_buffers():
+    q, k = desc(b=0), desc(b=0, h=2)
+    assert bwd_validate(q, k, desc(b=0, h=2), lse=None, ws=None, ws_bytes=0) == 0
