@@ -4,7 +4,8 @@ A step is one forward pass (one ``attn_fwd`` launch) over the dense causal
 multi-head workload B=4, H=16, S=2048, D=128 (bf16, inputs resident in HBM).
 Prints ONE JSON line with causal-adjusted TFLOP/s, the roofline fraction of
 the kernel against the bf16 dense MFMA peak, and the fp64 CPU oracle timed on
-a bounded sample of the same workload.
+a bounded sample of the same workload.  A secondary ``backward`` object times
+``attn_bwd`` (dq, dk, dv from the saved LSE) on the same inputs.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload mha]
 """
@@ -90,6 +91,45 @@ def cpu_baseline(w: W.Workload, budget_s: float = 20.0):
             "kind": "oracle", "sample": sample}
 
 
+def time_backward(attn, torch, w, q, k, v, cu, sp, out, lse, flops, n):
+    """Average time of one attn_bwd call (its dQ and dK/dV kernels) over n
+    back-to-back calls on the launch stream, after the forward filled out/lse.
+
+    TFLOP/s use the usual backward count: 2.5 x the forward's counted FLOPs
+    (five matrix products of the forward's size: S, dP, dV, dK, dQ); the
+    kernels recompute S and dP once more for dQ, which that count leaves out."""
+    g = torch.from_numpy(W.make_dout(w).view(np.int16)).view(torch.bfloat16).to(q.device)
+    ms = w.seqlen if cu is not None else None
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(16, 8 * w.hq * w.batch * w.seqlen), dtype=torch.uint8, device=q.device)
+
+    def run():
+        attn.attn_bwd(q, k, v, out, g, lse, cu_seqlens=cu, causal=w.causal, scale=w.scale, max_seqlen=ms,
+                      block_mask=sp.get("block_mask"), dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    # settle the clock again (the cold-cache launches before this leave it low)
+    t0 = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t0 < 0.1 or n_settle < 3:
+        run()
+        n_settle += 1
+        if n_settle % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_b = e0.elapsed_time(e1) / n
+    tf = 2.5 * flops / (ms_b * 1e-3) / 1e12
+    return {"ms_per_call": round(ms_b, 5), "calls": n, "tflops": round(tf, 3),
+            "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "flop_convention": "2.5 x forward counted FLOPs (S, dP, dV, dK, dQ products)",
+            "kernels": "attn_bwd_dq_kernel then attn_bwd_dkdv_kernel"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +142,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="launches timed one by one after evicting the caches (secondary figure)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the secondary timing of the backward pass")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -227,6 +269,11 @@ def main():
         log(f"dense causal on the same inputs: {dense_ms:.2f} ms/step; block-sparse speedup "
             f"{dense_ms / ms_per_step:.2f}x (ideal {ideal:.2f}x)")
 
+    bwd = None
+    if not args.no_backward and "block_list" not in sp:
+        bwd = time_backward(attn, torch, w, q, k, v, cu, sp, out, lse, flops, max(10, args.steps // 4))
+        log(f"backward: {bwd}")
+
     cpu = None
     if not args.no_cpu_baseline and not w.packed and not sp:
         cpu = cpu_baseline(w)
@@ -254,6 +301,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic()},
         "cpu_baseline": cpu,
+        "backward": bwd,
     }
     print(json.dumps(rec), flush=True)
 
