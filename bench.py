@@ -27,7 +27,8 @@ import attn_workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA peak
 METRIC = "attention fwd TFLOPS (bf16, causal-adjusted) and % of MFMA bf16 peak, 1 GPU"
-KERNEL_SRC = os.path.join(ROOT, "attention_forward_flashattention_amd", "csrc", "attn_fwd.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "attention_forward_flashattention_amd", "csrc", f)
+               for f in ("attn_fwd.hip", "attn_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_mha.json")
 
 
@@ -36,7 +37,11 @@ def log(msg):
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """sha256[:16] of the forward kernel's sources (attn_fwd.hip, then attn_common.h)."""
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -91,7 +96,7 @@ def cpu_baseline(w: W.Workload, budget_s: float = 20.0):
             "kind": "oracle", "sample": sample}
 
 
-def time_backward(attn, torch, w, q, k, v, cu, sp, out, lse, flops, n):
+def time_backward(attn, torch, w, q, k, v, cu, sp, out, lse, flops, n, settle_s):
     """Average time of one attn_bwd call (its dQ and dK/dV kernels) over n
     back-to-back calls on the launch stream, after the forward filled out/lse.
 
@@ -110,7 +115,7 @@ def time_backward(attn, torch, w, q, k, v, cu, sp, out, lse, flops, n):
     # settle the clock again (the cold-cache launches before this leave it low)
     t0 = time.perf_counter()
     n_settle = 0
-    while time.perf_counter() - t0 < 0.1 or n_settle < 3:
+    while time.perf_counter() - t0 < settle_s or n_settle < 3:
         run()
         n_settle += 1
         if n_settle % 4 == 0:
@@ -271,7 +276,8 @@ def main():
 
     bwd = None
     if not args.no_backward and "block_list" not in sp:
-        bwd = time_backward(attn, torch, w, q, k, v, cu, sp, out, lse, flops, max(10, args.steps // 4))
+        bwd = time_backward(attn, torch, w, q, k, v, cu, sp, out, lse, flops, max(10, args.steps // 4),
+                            args.settle_ms / 2e3)
         log(f"backward: {bwd}")
 
     cpu = None
