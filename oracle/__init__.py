@@ -1,6 +1,6 @@
-"""fp64 CPU oracle for softmax attention, forward and backward (test infrastructure only).
+"""fp64 CPU oracle for softmax attention: forward, backward, ordered skipping (test infrastructure only).
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package; the product path must not.
 """
-from .oracle import attn_bwd, attn_fwd, build, default_threads, run_workload  # noqa: F401
+from .oracle import attn_bwd, attn_fwd, attn_fwd_osk, build, default_threads, run_workload  # noqa: F401

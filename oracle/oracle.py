@@ -7,7 +7,8 @@ module, and this module never imports the product package.
 ``attn_fwd`` computes exact softmax attention forward in float64 from the
 definition (see the header of ``oracle_attn.c`` for the formula and the
 passages of the pages it follows); ``attn_bwd`` its exact gradients (header
-of ``oracle_bwd.c``).  Every function's parity status is "pinned":
+of ``oracle_bwd.c``); ``attn_fwd_osk`` ordered skipping along a block list
+with the stopping rule stated in the header of ``oracle_osk.c``.  Every function's parity status is "pinned":
 ``tests/test_oracle_pins.py``, ``test_oracle_mask_pins.py`` and
 ``test_oracle_bwd_pins.py`` tie them to brute force, finite differences,
 closed forms and invariants that do not go through this code.
@@ -22,7 +23,8 @@ from typing import Optional
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRCS = [os.path.join(HERE, "oracle_attn.c"), os.path.join(HERE, "oracle_bwd.c")]
+SRCS = [os.path.join(HERE, "oracle_attn.c"), os.path.join(HERE, "oracle_bwd.c"),
+        os.path.join(HERE, "oracle_osk.c")]
 LIB = os.path.join(HERE, "liboracle_attn.so")
 
 _lib = None
@@ -61,6 +63,11 @@ def _load():
                                         ctypes.c_int, ctypes.c_int, ctypes.c_double, P,
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                         P, P, P, ctypes.c_int]
+        lib.oracle_attn_fwd_osk.restype = ctypes.c_int
+        lib.oracle_attn_fwd_osk.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_double, P, P, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_double, ctypes.c_int, P, ctypes.c_int, P, P, P, P,
+                                            ctypes.c_int]
         lib.oracle_default_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -172,6 +179,43 @@ def attn_bwd(q, k, v, dout, cu_seqlens, causal: bool, scale: float, block_mask=N
     if rc != 0:
         raise RuntimeError(f"oracle_attn_bwd failed with code {rc}")
     return dq, dk, dv
+
+
+def attn_fwd_osk(q, k, v, causal: bool, scale: float, row_ptr, col_idx, tau: float, min_visit: int,
+                 qblocks=None, block: int = 128, nthreads: int = 0):
+    """Ordered skipping along a block list (rule in the header of ``oracle_osk.c``).
+
+    q: float64 [T, Hq, D]; k, v: float64 [T, Hkv, D] (one sequence)
+    row_ptr, col_idx: the ordered block list; tau, min_visit: the stopping rule
+    qblocks: query blocks to compute (None: all)
+    Returns (O [rows, Hq, D], LSE [rows, Hq], visited int32 [Hq, n_sel],
+    ratio [Hq, nnz]) where rows are those of the selected blocks in order and
+    ratio holds max_i d_i/L_i after each visited entry (NaN for entries after
+    the stop).
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    t, hq, d = q.shape
+    hkv = k.shape[1]
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    if len(ci) == 0:
+        ci = np.zeros(1, dtype=np.int32)
+    n_qblk = len(rp) - 1
+    sel = np.arange(n_qblk, dtype=np.int32) if qblocks is None else np.ascontiguousarray(qblocks, dtype=np.int32)
+    rows = sum(min(block, t - int(b) * block) for b in sel)
+    out = np.zeros((rows, hq, d))
+    lse = np.zeros((rows, hq))
+    visited = np.zeros((hq, len(sel)), dtype=np.int32)
+    ratio = np.full((hq, max(1, int(rp[-1]))), np.nan)
+    rc = _load().oracle_attn_fwd_osk(_ptr(q), _ptr(k), _ptr(v), t, hq, hkv, d, int(bool(causal)), float(scale),
+                                     _ptr(rp), _ptr(ci), n_qblk, int(block), float(tau), int(min_visit),
+                                     _ptr(sel), len(sel), _ptr(out), _ptr(lse), _ptr(visited), _ptr(ratio),
+                                     int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_fwd_osk failed with code {rc}")
+    return out, lse, visited, ratio
 
 
 def run_workload(w, rows=None, nthreads: int = 0, with_psum: bool = False):
