@@ -190,8 +190,8 @@ def attn_fwd_osk(q, k, v, causal: bool, scale: float, row_ptr, col_idx, tau: flo
     qblocks: query blocks to compute (None: all)
     Returns (O [rows, Hq, D], LSE [rows, Hq], visited int32 [Hq, n_sel],
     ratio [Hq, nnz]) where rows are those of the selected blocks in order and
-    ratio holds max_i d_i/L_i after each visited entry (NaN for entries after
-    the stop).
+    ratio holds the test value max_i (n - e) d_i / L_i after each visited entry
+    e of an n-entry list (NaN for entries after the stop).
     """
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)

@@ -11,13 +11,17 @@
  * longer needs.  The page states no rule for when to stop; the rule here is
  * the builder's reading of "cumulative score":
  *
- *   Walk the entries e = 1, 2, ... of query block qb's list in order.  For
- *   each row i of the block let L_i(e) = sum of exp(s_ij) over the allowed
- *   keys of entries 1..e (its cumulative softmax mass) and d_i(e) the part of
- *   it that entry e added.  After entry e, if e >= min_visit and
- *   d_i(e) <= tau * L_i(e) for every row i of the block, stop: the visited
- *   prefix is entries 1..e.  Otherwise go on; a list that runs out is visited
- *   whole.  (A row that has seen no key yet has L = d = 0 and meets the test.)
+ *   Walk the entries e = 1, 2, ... of query block qb's list (n entries) in
+ *   order.  For each row i of the block let L_i(e) = sum of exp(s_ij) over
+ *   the allowed keys of entries 1..e (its cumulative softmax mass) and d_i(e)
+ *   the part of it that entry e added.  If the list ranks blocks by their
+ *   mass, each of the n - e entries still to come adds at most d_i(e), so
+ *   (n - e) d_i(e) bounds the mass the row would still gain.  After entry e,
+ *   if e >= min_visit and (n - e) d_i(e) <= tau * L_i(e) for every row i of
+ *   the block, stop: the visited prefix is entries 1..e, and tau bounds the
+ *   fraction of each row's mass left out when the ranking holds.  Otherwise
+ *   go on; a list that runs out is visited whole.  (A row that has seen no key
+ *   yet has L = d = 0 and meets the test.)
  *   The result is exact softmax attention over the keys of the visited
  *   prefix (the allowed set of the block-list definition in oracle_attn.c,
  *   with the list cut at the prefix).
@@ -102,7 +106,7 @@ static void one_unit(ojob_t *J, int h, int si, double *m, double *L, double *sro
           m[i - r0] = m_new;
         }
       }
-      const double r = L[i - r0] > 0.0 ? delta / L[i - r0] : 0.0;
+      const double r = L[i - r0] > 0.0 ? (double)(e1 - e - 1) * delta / L[i - r0] : 0.0;
       if (r > worst) worst = r;
     }
     if (J->ratio) J->ratio[(size_t)h * J->row_ptr[J->n_qblk] + e] = worst;
@@ -185,7 +189,7 @@ static void *oworker(void *arg) {
  *   qblocks [n_sel] int32: the query blocks to compute (NULL: all, n_sel = n_qblk)
  *   out [rows][hq][d], lse [rows][hq]: rows of the selected blocks in order
  *   visited [hq][n_sel] int32: entries visited per (head, selected block)
- *   ratio [hq][nnz] or NULL: the test value max_i d_i/L_i after each visited entry
+ *   ratio [hq][nnz] or NULL: the test value max_i (n-e) d_i/L_i after each visited entry
  *     (entries after the stop are left as they were)
  * Returns 0, or a negative code.
  */

@@ -17,9 +17,12 @@ AssertionError when it disagrees with what the pin fixes:
   followed by exactly one more entry (the first entry is all the mass seen so
   far, so the test can only pass at the second), and O is the softmax over
   that block alone to within exp(-40).
+* the last entry of a list always passes (nothing remains), so a list whose
+  entries all carry equal mass is cut only at its end.
 A numpy copy of the rule with one planted mistake each (stop one entry late
 or early, ratio taken before adding the entry, min_visit ignored, any row
-instead of every row, causal mask ignored in the mass) fails at least one pin.
+instead of every row, causal mask ignored in the mass, the remaining-entry
+count dropped) fails at least one pin.
 """
 import math
 
@@ -113,11 +116,12 @@ def brute(q, k, v, causal, scale, rp, ci, tau, min_visit, block):
             n_vis = len(ents)
             for e, kb in enumerate(ents):
                 ok = True
+                left = len(ents) - (e + 1)
                 for i in rows:
                     keys = [j for j in range(kb * block, min(T, (kb + 1) * block)) if not causal or j <= i]
                     add = math.fsum(math.exp(s[i, j]) for j in keys)
                     cum[i] += add
-                    if add > tau * cum[i]:
+                    if left * add > tau * cum[i]:
                         ok = False
                 if e + 1 >= min_visit and ok:
                     n_vis = e + 1
@@ -138,7 +142,7 @@ def brute(q, k, v, causal, scale, rp, ci, tau, min_visit, block):
 def pin_brute_force(impl):
     for c in CASES:
         q, k, v, causal, scale, rp, ci, block = case(*c)
-        for tau in (0.02, 0.1, 0.3, 0.7):
+        for tau in (0.05, 0.3, 1.1, 2.7):  # away from the exact ratios (n - 1) of a first entry
             for mv in (1, 2):
                 o, l, vis = impl(q, k, v, causal, scale, rp, ci, tau, mv, block)
                 o_b, l_b, vis_b = brute(q, k, v, causal, scale, rp, ci, tau, mv, block)
@@ -151,7 +155,7 @@ def pin_monotone_in_tau(impl):
     for c in CASES:
         q, k, v, causal, scale, rp, ci, block = case(*c)
         prev = None
-        for tau in (0.0, 0.01, 0.05, 0.2, 0.5, 1.0):
+        for tau in (0.0, 0.03, 0.2, 1.0, 3.0, 10.0):
             _, _, vis = impl(q, k, v, causal, scale, rp, ci, tau, 1, block)
             if prev is not None:
                 assert np.all(vis <= prev), (c, tau)
@@ -177,8 +181,24 @@ def pin_dominant_block(impl):
     assert np.abs(o[:, 0] - p @ v[8:12, 0]).max() < 1e-12
 
 
+def pin_equal_mass_runs_to_the_end(impl):
+    """Keys of equal score everywhere: every entry adds the same mass, so
+    (n - e) d / L = (n - e) / e stays above tau = 0.5 until the last entry."""
+    T, d, block = 32, 4, 4
+    q = np.zeros((T, 2, d))
+    k = np.zeros((T, 1, d))
+    v = np.random.default_rng(8).standard_normal((T, 1, d))
+    n_qblk = T // block
+    rp = np.arange(n_qblk + 1, dtype=np.int32) * n_qblk
+    ci = np.array([b for _ in range(n_qblk) for b in np.random.default_rng(9).permutation(n_qblk)], np.int32)
+    _, _, vis = impl(q, k, v, False, 1.0, rp, ci, 0.5, 1, block)
+    # (n - e) / e <= 0.5  <=>  e >= 2n/3
+    want = int(np.ceil(2 * n_qblk / 3))
+    assert np.all(vis == want), vis
+
+
 PINS = [pin_tau_zero_is_exact_list, pin_huge_tau_stops_at_min_visit, pin_brute_force, pin_monotone_in_tau,
-        pin_dominant_block]
+        pin_dominant_block, pin_equal_mass_runs_to_the_end]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -232,6 +252,7 @@ def mutant(bug):
                 cum = np.zeros(r1 - r0)
                 n_vis = len(ents)
                 for e, kb in enumerate(ents):
+                    left = 1 if bug == "no_remaining_count" else len(ents) - (e + 1)
                     jj = np.arange(kb * block, min(T, (kb + 1) * block))
                     ii = np.arange(r0, r1)[:, None]
                     allowed = np.ones((r1 - r0, len(jj)), bool)
@@ -241,7 +262,7 @@ def mutant(bug):
                     before = cum.copy()
                     cum = cum + add
                     base = before if bug == "ratio_before_add" else cum
-                    sat = add <= tau * base
+                    sat = left * add <= tau * base
                     ok = sat.any() if bug == "any_row" else sat.all()
                     if (bug == "min_visit_ignored" or e + 1 >= min_visit) and ok:
                         n_vis = e + 1 + (1 if bug == "stop_late" else 0) - (1 if bug == "stop_early" else 0)
@@ -260,7 +281,8 @@ def mutant(bug):
     return impl
 
 
-OSK_MUTANTS = ["stop_late", "stop_early", "ratio_before_add", "min_visit_ignored", "any_row", "mass_no_causal"]
+OSK_MUTANTS = ["stop_late", "stop_early", "ratio_before_add", "min_visit_ignored", "any_row", "mass_no_causal",
+               "no_remaining_count"]
 
 
 def test_clean_numpy_copy_passes_osk_pins():
