@@ -72,6 +72,12 @@ def load_library(path: str = LIB_PATH):
         lib.attn_fwd_mask.argtypes = [T, T, T, P, ctypes.c_int, ctypes.c_float, BM, T, P, P]
         lib.attn_fwd_mask_validate.restype = ctypes.c_int
         lib.attn_fwd_mask_validate.argtypes = [T, T, T, P, ctypes.c_int, ctypes.c_float, BM, T]
+        lib.attn_fwd_osk.restype = ctypes.c_int
+        lib.attn_fwd_osk.argtypes = [T, T, T, ctypes.c_int, ctypes.c_float, BL, ctypes.c_float, ctypes.c_int,
+                                     T, P, P, P]
+        lib.attn_fwd_osk_validate.restype = ctypes.c_int
+        lib.attn_fwd_osk_validate.argtypes = [T, T, T, ctypes.c_int, ctypes.c_float, BL, ctypes.c_float,
+                                              ctypes.c_int, T]
         lib.attn_bwd.restype = ctypes.c_int
         lib.attn_bwd.argtypes = [T, T, T, T, T, P, P, ctypes.c_int, ctypes.c_float, BM, T, T, T, P,
                                  ctypes.c_size_t, P]
@@ -205,6 +211,49 @@ def attn_fwd(q, k, v, cu_seqlens=None, causal: bool = False, scale: Optional[flo
     if st != ATTN_OK:
         raise AttnError(st, status_str(st))
     return out, lse
+
+
+def attn_fwd_osk(q, k, v, block_list: Tuple, tau: float, min_visit: int = 2, causal: bool = True,
+                 scale: Optional[float] = None, out=None, lse=None, visited=None, stream=None):
+    """Block-list forward with ordered skipping (the stopping rule of
+    ``attn_fwd_osk`` in include/attn_fwd.h): each (query head, query block)
+    walks its list in order and stops once (entries left) x the newest entry's
+    mass is at most ``tau`` of every row's mass, after ``min_visit`` entries.
+
+    q: bf16 [1, S, Hq, D]; k, v: bf16 [1, S, Hkv, D]; block_list: (row_ptr, col_idx)
+    Returns (out, lse, visited) with visited int32 [Hq, num_q_blocks].
+    """
+    import torch
+
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [1, S, H, D]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError(f"{name} must be a bfloat16 device tensor")
+    batch, seqlen, hq, d = (int(x) for x in q.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((batch, hq, seqlen), dtype=torch.float32, device=q.device)
+    row_ptr, col_idx = block_list
+    for t in (row_ptr, col_idx):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("block list tensors must be contiguous int32 device tensors")
+    n_qblk = int(row_ptr.numel()) - 1
+    if visited is None:
+        visited = torch.empty((hq, n_qblk), dtype=torch.int32, device=q.device)
+    bl = AttnBlockList(row_ptr.data_ptr(), col_idx.data_ptr() if col_idx.numel() else row_ptr.data_ptr(),
+                       128, 128, n_qblk)
+    dq, dk, dv, do = (describe(t, batch, seqlen, False) for t in (q, k, v, out))
+    st = lib.attn_fwd_osk(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(bool(causal)), float(scale),
+                          ctypes.byref(bl), float(tau), int(min_visit), ctypes.byref(do),
+                          ctypes.c_void_p(lse.data_ptr()), ctypes.c_void_p(visited.data_ptr()),
+                          ctypes.c_void_p(_stream_handle(stream)))
+    if st != ATTN_OK:
+        raise AttnError(st, status_str(st), "attn_fwd_osk")
+    return out, lse, visited
 
 
 def attn_bwd(q, k, v, out, dout, lse, cu_seqlens=None, causal: bool = False,

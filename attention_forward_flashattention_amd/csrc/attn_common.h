@@ -19,8 +19,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
 constexpr int kListBlock = 128;  // block-list / block-mask granularity (rows and keys)
-// KV iteration modes: every key, an ordered block list, a bit-packed block mask
-enum { kDense = 0, kList = 1, kMask = 2 };
+// KV iteration modes: every key, an ordered block list, a bit-packed block
+// mask, an ordered block list walked with ordered skipping
+enum { kDense = 0, kList = 1, kMask = 2, kOsk = 3 };
 constexpr float kLn2 = 0.69314718055994530942f;
 // s_waitcnt immediate that waits for vmcnt == 0 and leaves the other counters
 // free (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])

@@ -17,7 +17,9 @@
 // The computation is the softmax attention that FlashAttention-style kernels
 // evaluate tile by tile in on-chip memory (AdaSplash-2 explainer, technical
 // summary section 1); block skipping follows the ordered per-query-block KV
-// list of the CoSA explainer (lay summary): unlisted blocks are never loaded.
+// list of the CoSA explainer (lay summary): unlisted blocks are never loaded,
+// and in the ordered-skipping mode the walk along the list also stops once the
+// blocks still listed can add little to what the first ones gathered.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -49,6 +51,9 @@ struct Params {
   const uint32_t *mask;    // bit-packed block mask, or null
   int64_t mask_ss, mask_sh; // words between masks of consecutive sequences / kv heads
   int mask_words;          // words per query-block row of a mask
+  float osk_tau;           // ordered skipping: stop when (entries left) x every row's newest-entry mass <= tau x its mass
+  int osk_min_visit;       // ... but never before this many entries
+  int32_t *visited;        // ordered skipping: entries visited per (query head, query block), or null
   int batch, seqlen, hq, group;
   int n_tiles;   // query tiles per (sequence, head) = ceil(seqlen / BM)
   int n_units;   // batch * hq
@@ -150,6 +155,7 @@ template <class C, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Params p) {
   constexpr int D = C::D;
   constexpr bool LIST = MODE != kDense;  // block-sparse: one 128-row query block per workgroup
+  constexpr bool OSK = MODE == kOsk;     // block list with ordered skipping
   using L = Lds<D>;
   constexpr int kBM = C::kBM;
   constexpr int kBN = C::kBN;
@@ -162,7 +168,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   // own, so a wave can write out its rows while others still read K/V.
   constexpr bool kOwnStage = C::kMinBlocks == 1;
   constexpr int kStageBytes = C::NW * 32 * D * 2;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes + (kOwnStage ? kStageBytes : 0)];
+  constexpr int kFlagBytes = OSK ? 16 : 0;  // one stop flag per wave
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes + (kOwnStage ? kStageBytes : 0) + kFlagBytes];
+  uint32_t *osk_flag = reinterpret_cast<uint32_t *>(smem + 2 * kBufBytes + (kOwnStage ? kStageBytes : 0));
 
   int tile, unit;
   decode_tile(p, CAUSAL || LIST, tile, unit);
@@ -193,6 +201,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
 
   // ---- KV iteration space
   constexpr int kSub = kListBlock / kBN;  // KV tiles per 128-key block
+  // (the stop flags of an entry are written after its last tile and read after
+  // the barrier that starts the next entry: two tiles per entry keep a write
+  // from racing a read of the previous flags)
+  static_assert(!OSK || kSub >= 2, "ordered skipping needs two or more tiles per list entry");
   int n_iter;
   int e0 = 0;
   const int n_kvblk = (len + kListBlock - 1) / kListBlock;
@@ -205,7 +217,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     const int left = m_lim - 32 * w;
     return left >= 32 ? 0xffffffffu : (left <= 0 ? 0u : ((1u << left) - 1u));
   };
-  if (MODE == kList) {
+  if (MODE == kList || MODE == kOsk) {
     e0 = p.row_ptr[tile];
     n_iter = (p.row_ptr[tile + 1] - e0) * kSub;
   } else if (MODE == kMask) {
@@ -272,6 +284,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   // tile's max nor rescale O.
   float m_run = -INFINITY;
   float l_run = 0.f;  // running sum over this lane's half of the keys
+  float d_run = 0.f;  // ordered skipping: the current list entry's part of l_run
 
   const int qrow = q0 + wave * 32 + l32;  // this lane's query row (sequence position)
   const int wq_last = q0 + wave * 32 + 31;
@@ -317,12 +330,18 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   }
 
   bool first = true;  // no tile processed yet by this wave
-  auto step = [&](const int it, auto buf_tag) {
+  // Returns true (ordered skipping only) when the walk stops before tile `it`.
+  auto step = [&](const int it, auto buf_tag) -> bool {
     constexpr int kBuf = decltype(buf_tag)::value;  // LDS buffer of tile `it` (= it % 2)
     // tile `it` has landed (every wave waited for its own loads); every wave is
     // done reading the other buffer
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+    // ordered skipping: at the start of a list entry, stop when every wave found
+    // all its rows' share of the previous entry at most tau of their mass
+    if (OSK && it > 0 && it % kSub == 0 && it / kSub >= p.osk_min_visit &&
+        (osk_flag[0] & osk_flag[1] & osk_flag[2] & osk_flag[3]))
+      return true;
     int kv_nxt = -1;
     if (it + 1 < n_iter) {
       kv_nxt = kv_start(it + 1);
@@ -334,8 +353,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     }
     const int kv0 = kv_cur;
     kv_cur = kv_nxt;
-    if (kv0 < 0) return;
-    if (CAUSAL && kv0 > wq_last) return;  // whole tile above this wave's rows
+    if (kv0 < 0) return false;
+    if (CAUSAL && kv0 > wq_last) return false;  // whole tile above this wave's rows
     const char *sK = smem + kBuf * kBufBytes;
     const char *sV = sK + kTileBytes;
 
@@ -404,12 +423,14 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
         m_run = m_new;
         l_run *= alpha;
+        if (OSK) d_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < kDt; ++dt) oacc[dt] = oacc[dt] * alpha;
       }
       rs = exp_tile(s, p.c, m_run == -INFINITY ? 0.f : m_run, pb);
     }
     l_run += rs;
+    if (OSK) d_run += rs;
 
     // ---- O^T += V^T P^T.  MFMA k index (8 per lane half) maps to keys
     // 16c + 8(e/4) + 4*hi + (e%4) of a 32-key tile, matching where the score
@@ -437,14 +458,40 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         __builtin_amdgcn_sched_barrier(0);
       });
     }
+    return false;
   };
+  // ordered skipping: after the last tile of a list entry, each wave records
+  // whether all its rows passed the test -- the entries still to come, if
+  // each adds at most what this one added, would add at most tau of the
+  // row's mass -- and starts the next entry's share
+  auto osk_mark = [&](const int it) {
+    if (!OSK || it % kSub != kSub - 1) return;
+    const float share = half_sum(d_run);
+    const float mass = half_sum(l_run);
+    const float left = (float)(n_iter / kSub - (it / kSub + 1));  // entries not yet visited
+    const bool fail = __builtin_amdgcn_ballot_w64(left * share > p.osk_tau * mass) != 0;
+    if (lane == 0) osk_flag[wave] = fail ? 0u : 1u;
+    d_run = 0.f;
+  };
+  int n_done = n_iter;  // tiles walked (ordered skipping may stop early)
   // two tiles per trip so that each step's LDS buffer is a compile-time constant
   // (every LDS operand address is then a loop-invariant lane offset plus an
   // immediate)
   for (int it = 0; it < n_iter; it += 2) {
-    step(it, BufTag<0>{});
-    if (it + 1 < n_iter) step(it + 1, BufTag<1>{});
+    if (step(it, BufTag<0>{})) {
+      n_done = it;
+      break;
+    }
+    osk_mark(it);
+    if (it + 1 < n_iter) {
+      if (step(it + 1, BufTag<1>{})) {
+        n_done = it + 1;
+        break;
+      }
+      osk_mark(it + 1);
+    }
   }
+  if (OSK && p.visited && tid == 0) p.visited[(int64_t)h * p.n_tiles + tile] = n_done / kSub;
 
   // ---- epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log.
   // O goes out through LDS: each wave writes its 32 x D tile there (16 B
@@ -576,6 +623,8 @@ int launch_d(const Params &p, bool causal, int mode, hipStream_t s) {
     return causal ? launch<Listed, true, kList>(p, s) : launch<Listed, false, kList>(p, s);
   if (mode == kMask)
     return causal ? launch<Listed, true, kMask>(p, s) : launch<Listed, false, kMask>(p, s);
+  if (mode == kOsk)
+    return causal ? launch<Listed, true, kOsk>(p, s) : launch<Listed, false, kOsk>(p, s);
   return causal ? launch<Dense, true, kDense>(p, s) : launch<Dense, false, kDense>(p, s);
 }
 
@@ -609,6 +658,9 @@ Params make_params(const attn_tensor_t *q, const attn_tensor_t *k, const attn_te
   p.mask = nullptr;
   p.mask_ss = p.mask_sh = 0;
   p.mask_words = 0;
+  p.osk_tau = 0.f;
+  p.osk_min_visit = 1;
+  p.visited = nullptr;
   p.batch = q->batch;
   p.seqlen = q->seqlen;
   p.hq = q->heads;
@@ -677,6 +729,33 @@ extern "C" int attn_fwd_mask(const attn_tensor_t *q, const attn_tensor_t *k,
   return launch_any(p, q->head_dim, causal, kMask, static_cast<hipStream_t>(stream));
 }
 
+extern "C" int attn_fwd_osk_validate(const attn_tensor_t *q, const attn_tensor_t *k,
+                                     const attn_tensor_t *v, int causal, float scale,
+                                     const attn_block_list_t *block_list, float tau,
+                                     int min_visit, const attn_tensor_t *out) {
+  if (!block_list) return ATTN_ERR_INVALID_ARG;
+  const int st = validate(q, k, v, nullptr, causal, scale, block_list, out);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(tau) || tau < 0.f || min_visit < 1) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+extern "C" int attn_fwd_osk(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                            int causal, float scale, const attn_block_list_t *block_list,
+                            float tau, int min_visit, attn_tensor_t *out, float *lse,
+                            int32_t *visited, void *stream) {
+  const int st = attn_fwd_osk_validate(q, k, v, causal, scale, block_list, tau, min_visit, out);
+  if (st != ATTN_OK) return st;
+  if (q->batch == 0 || q->seqlen == 0) return ATTN_OK;
+  Params p = make_params(q, k, v, nullptr, scale, out, lse);
+  p.row_ptr = block_list->row_ptr;
+  p.col_idx = block_list->col_idx;
+  p.osk_tau = tau;
+  p.osk_min_visit = min_visit;
+  p.visited = visited;
+  return launch_any(p, q->head_dim, causal, kOsk, static_cast<hipStream_t>(stream));
+}
+
 extern "C" const char *attn_status_str(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
@@ -687,4 +766,4 @@ extern "C" const char *attn_status_str(int status) {
   }
 }
 
-extern "C" int attn_version(void) { return 200; }
+extern "C" int attn_version(void) { return 300; }

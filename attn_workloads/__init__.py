@@ -288,13 +288,62 @@ def make_sparse_mask(name, seed, s, hq, hkv, d, budget=0.10, n_sample=256) -> Wo
                     sample_rows=sample_positions(g["sample_rows"], s, n_sample))
 
 
+def osk_list(n_qblk: int, proxy: np.ndarray, budget: float):
+    """Ordered list for ordered skipping: query block i visits its own block
+    first, then the ceil(budget * i) blocks of 0..i-1 with the highest proxy
+    score, highest first (ties to the lower index)."""
+    row_ptr = np.zeros(n_qblk + 1, dtype=np.int32)
+    cols = []
+    for i in range(n_qblk):
+        k = int(math.ceil(budget * i))
+        order = np.argsort(-proxy[:i], kind="stable")[:k]
+        cols.append(np.concatenate([[i], order]).astype(np.int32))
+        row_ptr[i + 1] = row_ptr[i] + len(cols[-1])
+    return row_ptr, np.concatenate(cols) if cols else np.zeros(0, np.int32)
+
+
+def make_osk(name, seed, s, hq, hkv, d, budget=0.25, mu=5.0, proxy_noise=0.5, n_sample=256) -> Workload:
+    """Causal block-list workload with planted block relevance, for ordered skipping.
+
+    Every 128-key block kb gets a relevance a_kb = 4 * Exp(1); KV head c has a
+    unit direction e_c.  Keys are k_j = z_j + a_kb(j) * e_c and queries
+    q_i = z_i' + mu * e_c (z i.i.d. N(0,1); z_i' is z_i with its component
+    along e_c removed), so every key of block kb carries the same score boost
+    scale * mu * a_kb for every query row of the head, on top of per-pair
+    noise: a few blocks hold most of a row's softmax mass, and the rows of a
+    query block agree on which, as in long-context attention.  A proxy scores blocks by
+    a_kb plus N(0, proxy_noise) noise (an imperfect ranking); the list
+    (``osk_list``) visits the diagonal block, then the top ``budget`` share of
+    the earlier blocks by proxy score.  All draws come from the seed's
+    streams; the values are rounded to bf16."""
+    g = streams(seed)
+    n_qblk = (s + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    gb = g["block_scores"]
+    a = (4.0 * gb.exponential(size=n_qblk)).astype(np.float32)
+    proxy = a.astype(np.float64) + proxy_noise * gb.standard_normal(n_qblk)
+    e = gb.standard_normal((hkv, d)).astype(np.float32)
+    e /= np.linalg.norm(e, axis=1, keepdims=True)
+    group = hq // hkv
+    eh = np.repeat(e, group, axis=0)                      # e of each query head's KV head
+    zq = g["q"].standard_normal(size=(1, s, hq, d), dtype=np.float32)
+    zq -= np.einsum("bshd,hd->bsh", zq, eh)[..., None] * eh[None, None]  # noise orthogonal to e
+    zq += mu * eh[None, None]
+    zk = g["k"].standard_normal(size=(1, s, hkv, d), dtype=np.float32)
+    zk += np.repeat(a, SPARSE_BLOCK)[:s][None, :, None, None] * e[None, None]
+    row_ptr, col_idx = osk_list(n_qblk, proxy, budget)
+    return Workload(name=name, seed=seed, batch=1, seqlen=s, hq=hq, hkv=hkv, d=d, causal=True,
+                    scale=default_scale(d), q=f32_to_bf16_bits(zq), k=f32_to_bf16_bits(zk),
+                    v=normal_bf16(g["v"], (1, s, hkv, d)), row_ptr=row_ptr, col_idx=col_idx,
+                    sample_rows=sample_positions(g["sample_rows"], s, n_sample))
+
+
 CONFIG_NAMES = ("tiny", "mha", "gqa", "varlen_d64", "varlen_d128", "varlen_d256", "sparse",
-                "sparse_mask")
+                "sparse_mask", "sparse_osk")
 
 
 def make(name: str) -> Workload:
     """Build one of the named workloads (seed 1..6 in the order tiny, mha, gqa, varlen, sparse,
-    sparse_mask)."""
+    sparse_mask; seed 8 for sparse_osk)."""
     if name == "tiny":
         return make_dense("tiny", 1, 1, 128, 2, 2, 64, False)
     if name == "mha":
@@ -308,6 +357,8 @@ def make(name: str) -> Workload:
         return make_sparse("sparse", 5, 131072, 32, 8, 128)
     if name == "sparse_mask":
         return make_sparse_mask("sparse_mask", 6, 131072, 32, 8, 128)
+    if name == "sparse_osk":
+        return make_osk("sparse_osk", 8, 131072, 32, 8, 128)
     raise KeyError(name)
 
 

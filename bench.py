@@ -96,6 +96,23 @@ def cpu_baseline(w: W.Workload, budget_s: float = 20.0):
             "kind": "oracle", "sample": sample}
 
 
+def osk_flops(w: W.Workload, visited: np.ndarray):
+    """FLOPs of the visited prefixes (4*D per counted pair, the diagonal block
+    counted half under causal masking) and the fraction of listed entries skipped."""
+    n_qblk = len(w.row_ptr) - 1
+    pairs = 0.0
+    listed = 0
+    for qb in range(n_qblk):
+        e0, e1 = int(w.row_ptr[qb]), int(w.row_ptr[qb + 1])
+        ents = w.col_idx[e0:e1]
+        wgt = np.where(ents == qb, 0.5, 1.0) if w.causal else np.ones(len(ents))
+        cum = np.concatenate([[0.0], np.cumsum(wgt)])
+        pairs += float(cum[visited[:, qb]].sum())
+        listed += (e1 - e0) * w.hq
+    flops = 4.0 * w.d * W.SPARSE_BLOCK * W.SPARSE_BLOCK * pairs
+    return flops, 1.0 - float(visited.sum()) / listed
+
+
 def time_backward(attn, torch, w, q, k, v, cu, sp, out, lse, flops, n, settle_s):
     """Average time of one attn_bwd call (its dQ and dK/dV kernels) over n
     back-to-back calls on the launch stream, after the forward filled out/lse.
@@ -147,6 +164,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="launches timed one by one after evicting the caches (secondary figure)")
+    ap.add_argument("--osk-tau", type=float, default=1e-2,
+                    help="sparse_osk workload: the ordered-skipping stop threshold tau")
+    ap.add_argument("--osk-min-visit", type=int, default=2,
+                    help="sparse_osk workload: entries visited before the stop test applies")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the secondary timing of the backward pass")
     ap.add_argument("--copy-probe", action="store_true",
@@ -184,9 +205,22 @@ def main():
     else:
         lse = torch.empty((w.hq, q.shape[0]), dtype=torch.float32, device=q.device)
 
-    def step():
-        attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale, out=out, lse=lse,
-                      max_seqlen=w.seqlen if cu is not None else None, **sp)
+    osk = w.name == "sparse_osk"
+    if osk:
+        visited = torch.empty((w.hq, len(w.row_ptr) - 1), dtype=torch.int32, device=q.device)
+
+        def step():
+            attn.attn_fwd_osk(q, k, v, sp["block_list"], args.osk_tau, args.osk_min_visit, causal=w.causal,
+                              scale=w.scale, out=out, lse=lse, visited=visited)
+
+        # the FLOPs of ordered skipping are those of the entries it visits
+        step()
+        torch.cuda.synchronize()
+        flops, skip_rate = osk_flops(w, visited.cpu().numpy())
+    else:
+        def step():
+            attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale, out=out, lse=lse,
+                          max_seqlen=w.seqlen if cu is not None else None, **sp)
 
     # Settle the clock: the GPU ramps its engine clock over the first tens of
     # milliseconds of load; without this the timed steps of a short kernel run
@@ -251,7 +285,38 @@ def main():
         log(f"cold cache (L2 and Infinity Cache evicted before each launch): median {np.median(cold) * 1e3:.1f} us, "
             f"min {min(cold) * 1e3:.1f} us over {len(cold)} launches")
 
-    if sp:
+    if osk:
+        # ordered skipping against the static list on the same inputs: speedup,
+        # and the error it makes against the static list's exact result
+        o_osk = out.float().clone()
+        out_s = torch.empty_like(out)
+
+        def static():
+            attn.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=out_s, lse=lse, **sp)
+        static()
+        torch.cuda.synchronize()
+        n_s = max(2, args.steps // 20)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_s):
+            static()
+        e1.record()
+        torch.cuda.synchronize()
+        static_ms = e0.elapsed_time(e1) / n_s
+        ref = out_s.float()
+        diff = o_osk - ref
+        extra["osk"] = {"tau": args.osk_tau, "min_visit": args.osk_min_visit,
+                        "skipped_entry_fraction": round(skip_rate, 4),
+                        "static_list_ms_per_step": round(static_ms, 4),
+                        "speedup_vs_static_list": round(static_ms / ms_per_step, 3),
+                        "o_rel_rms_vs_static_list": float(diff.norm() / ref.norm()),
+                        "o_max_abs_vs_static_list": float(diff.abs().max()),
+                        "flops_convention": "4*D per visited (query, key) pair x Hq"}
+        log(f"ordered skipping tau={args.osk_tau}: skipped {skip_rate:.3f} of the listed entries; static list "
+            f"{static_ms:.2f} ms/step -> speedup {static_ms / ms_per_step:.2f}x; O vs static list: rel RMS "
+            f"{extra['osk']['o_rel_rms_vs_static_list']:.2e}, max abs {extra['osk']['o_max_abs_vs_static_list']:.2e}")
+
+    if sp and not osk:
         # block-sparse speedup: the dense causal launch on the same inputs
         def dense():
             attn.attn_fwd(q, k, v, cu_seqlens=cu, causal=w.causal, scale=w.scale, out=out, lse=lse,
@@ -275,7 +340,7 @@ def main():
             f"{dense_ms / ms_per_step:.2f}x (ideal {ideal:.2f}x)")
 
     bwd = None
-    if not args.no_backward and "block_list" not in sp:
+    if not args.no_backward and "block_list" not in sp and not osk:
         bwd = time_backward(attn, torch, w, q, k, v, cu, sp, out, lse, flops, max(10, args.steps // 4),
                             args.settle_ms / 2e3)
         log(f"backward: {bwd}")

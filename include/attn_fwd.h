@@ -171,6 +171,45 @@ int attn_fwd_mask_validate(const attn_tensor_t *q, const attn_tensor_t *k,
                            float scale, const attn_block_mask_t *mask,
                            const attn_tensor_t *out);
 
+/*
+ * attn_fwd_osk — block-list forward with ordered skipping.
+ *
+ * The CoSA explainer (lay summary) has the kernel read a query block's KV
+ * blocks in the proxy's priority order, gather a cumulative score from the
+ * most important ones first, and then skip later blocks it no longer needs;
+ * the page states no rule for when to stop.  The rule here: walk the n
+ * entries of query block qb's list in order; for each row i of the block let
+ * L_i be its softmax mass (sum of exp(scale q_i.k_j) over the keys visited so
+ * far) and d_i the part the newest entry e added.  After entry e, if
+ * e >= min_visit and (n - e) * d_i <= tau * L_i for every row of the block
+ * (for the query head at hand), the walk stops; otherwise it goes on to the
+ * end of the list.  If the list ranks blocks by their mass, (n - e) * d_i
+ * bounds the mass a row would still gain, so tau bounds the fraction left
+ * out.  The result is exact softmax attention (as attn_fwd with the list)
+ * over the visited prefix of each (query head, query block); it is an
+ * approximation of attn_fwd with the whole list.  The sums are formed in
+ * fp32 as the kernel meets them, so a walk whose test value lands within
+ * rounding of tau may stop one entry earlier or later than an exact
+ * evaluation would.
+ *
+ *   block_list  required (same rules as for attn_fwd: batch 1, no cu_seqlens)
+ *   tau         finite, >= 0 (0: stop only where the rest can add nothing)
+ *   min_visit   >= 1: entries always visited before the test applies
+ *   visited     NULL, or device int32 [Hq, num_q_blocks]: entries visited per
+ *               (query head, query block), written by the call
+ * Other arguments and returns as for attn_fwd; additionally
+ * ATTN_ERR_INVALID_ARG for a NULL list, a negative or non-finite tau, or
+ * min_visit < 1.
+ */
+int attn_fwd_osk(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                 int causal, float scale, const attn_block_list_t *block_list, float tau,
+                 int min_visit, attn_tensor_t *out, float *lse, int32_t *visited, void *stream);
+
+/* The argument checks of attn_fwd_osk alone (host code only). */
+int attn_fwd_osk_validate(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                          int causal, float scale, const attn_block_list_t *block_list, float tau,
+                          int min_visit, const attn_tensor_t *out);
+
 /* Static description of a status code (never NULL). */
 const char *attn_status_str(int status);
 

@@ -174,3 +174,79 @@ def compare_grads(got, ref, label=""):
         stats[name] = (rel_rms, max_rel)
         assert rel_rms <= G_REL_RMS and max_rel <= G_MAX_REL, (label, name, stats[name])
     return stats
+
+
+# ---------------------------------------------------------------------------
+# Ordered skipping
+# ---------------------------------------------------------------------------
+OSK_BAND = 1e-3   # relative band around tau where fp32 and fp64 test values may disagree
+
+
+def run_gpu_osk(w: W.Workload, tau: float, min_visit: int, tensors=None):
+    """GPU ordered-skipping forward: O float64 [T, Hq, D], LSE [T, Hq], visited int [Hq, n_qblk]."""
+    import torch
+    import attention_forward_flashattention_amd as attn
+
+    q, k, v, cu, sp = tensors if tensors is not None else to_device(w)
+    out, lse, vis = attn.attn_fwd_osk(q, k, v, sp["block_list"], tau, min_visit, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64).reshape(w.seqlen, w.hq, w.d)
+    l = lse.cpu().numpy().astype(np.float64)[0].T
+    return o, l, vis.cpu().numpy()
+
+
+def osk_trace(w: W.Workload, qblocks, nthreads: int = 0):
+    """The oracle's test value after every entry of the selected query blocks'
+    lists (tau = 0 walks each list to its end): [Hq, nnz] (NaN elsewhere)."""
+    import oracle
+    from attn_workloads import bf16_bits_to_f32
+
+    q, k, v = (bf16_bits_to_f32(x).astype(np.float64).reshape(w.seqlen, -1, w.d) for x in (w.q, w.k, w.v))
+    _, _, _, ratio = oracle.attn_fwd_osk(q, k, v, w.causal, w.scale, w.row_ptr, w.col_idx, 0.0, 1,
+                                         qblocks=qblocks, nthreads=nthreads)
+    return ratio
+
+
+def check_visited(w: W.Workload, visited, ratio, tau: float, min_visit: int, qblocks):
+    """Every GPU stop is a valid stop of the rule within the band: the test value
+    at the stop is <= tau (unless the list ran out) and every earlier value from
+    min_visit on is > tau, each up to OSK_BAND relative."""
+    n_bad = 0
+    for h in range(w.hq):
+        for qb in qblocks:
+            e0, e1 = int(w.row_ptr[qb]), int(w.row_ptr[qb + 1])
+            vis = int(visited[h, qb])
+            r = ratio[h, e0:e1]
+            assert 1 <= vis <= e1 - e0, (h, qb, vis)
+            if vis < e1 - e0:
+                assert vis >= min_visit and r[vis - 1] <= tau * (1 + OSK_BAND), (h, qb, vis, r[vis - 1])
+            early = r[min_visit - 1:vis - 1]
+            assert np.all(early > tau * (1 - OSK_BAND)), (h, qb, vis, early.min() if len(early) else None)
+            n_bad += 0
+    return True
+
+
+def oracle_prefix_rows(w: W.Workload, visited, rows, nthreads: int = 0):
+    """Exact attention of the given rows over each (head, query block)'s visited
+    prefix of the list: O [len(rows), Hq, D], LSE [len(rows), Hq]."""
+    import oracle
+    from attn_workloads import bf16_bits_to_f32
+
+    q, k, v = (bf16_bits_to_f32(x).astype(np.float64).reshape(w.seqlen, -1, w.d) for x in (w.q, w.k, w.v))
+    g = w.hq // w.hkv
+    n_qblk = len(w.row_ptr) - 1
+    O = np.zeros((len(rows), w.hq, w.d))
+    L = np.zeros((len(rows), w.hq))
+    for h in range(w.hq):
+        rp = np.zeros(n_qblk + 1, np.int32)
+        ci = []
+        for qb in range(n_qblk):
+            e0 = int(w.row_ptr[qb])
+            ci.extend(w.col_idx[e0:e0 + int(visited[h, qb])])
+            rp[qb + 1] = len(ci)
+        o, l = oracle.attn_fwd(q[rows][:, h:h + 1], k[:, h // g:h // g + 1], v[:, h // g:h // g + 1],
+                               np.array([0, w.seqlen], np.int32), w.causal, w.scale, rp,
+                               np.array(ci, np.int32), 128, rows=rows, nthreads=nthreads)
+        O[:, h] = o[:, 0]
+        L[:, h] = l[:, 0]
+    return O, L

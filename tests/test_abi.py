@@ -27,8 +27,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_validate", "attn_bwd_workspace_size", "attn_fwd",
-                                    "attn_fwd_mask", "attn_fwd_mask_validate", "attn_fwd_validate",
-                                    "attn_status_str", "attn_version"]
+                                    "attn_fwd_mask", "attn_fwd_mask_validate", "attn_fwd_osk",
+                                    "attn_fwd_osk_validate", "attn_fwd_validate", "attn_status_str",
+                                    "attn_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.attn_version() == 200
+    assert lib.attn_version() == 300
     assert attn.status_str(0) == "ok" and attn.status_str(-3) == "kernel launch failed"
 
 
@@ -218,3 +219,27 @@ def test_bwd_unsupported_head_dim_and_long_masked_sequences():
 def test_bwd_empty_problem_needs_no_buffers():
     q, k = desc(b=0), desc(b=0, h=2)
     assert bwd_validate(q, k, desc(b=0, h=2), lse=None, ws=None, ws_bytes=0) == 0
+
+
+# ---------------------------------------------------------------------------
+# attn_fwd_osk argument checks (host only)
+# ---------------------------------------------------------------------------
+def osk_validate(q, k, v, bl, tau=0.01, min_visit=2, causal=1, scale=0.125):
+    lib = attn.load_library()
+    return lib.attn_fwd_osk_validate(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), causal, scale,
+                                     ctypes.byref(bl) if bl is not None else None, tau, min_visit,
+                                     ctypes.byref(q))
+
+
+def test_osk_argument_checks():
+    q, kv = desc(b=1, s=256, h=4), desc(b=1, s=256, h=2)
+    bl = AttnBlockList(FAKE, FAKE, 128, 128, 2)
+    assert osk_validate(q, kv, kv, bl) == 0
+    assert osk_validate(q, kv, kv, bl, tau=0.0, min_visit=1) == 0
+    assert osk_validate(q, kv, kv, None) == -1                      # the list is required
+    assert osk_validate(q, kv, kv, bl, tau=-0.1) == -1
+    assert osk_validate(q, kv, kv, bl, tau=float("inf")) == -1
+    assert osk_validate(q, kv, kv, bl, tau=float("nan")) == -1
+    assert osk_validate(q, kv, kv, bl, min_visit=0) == -1
+    assert osk_validate(desc(b=2, s=256, h=4), desc(b=2, s=256, h=2), desc(b=2, s=256, h=2), bl) == -2  # batch > 1
+    assert osk_validate(q, kv, kv, AttnBlockList(FAKE, FAKE, 64, 128, 4)) == -2                          # block size
