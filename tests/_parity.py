@@ -211,7 +211,6 @@ def check_visited(w: W.Workload, visited, ratio, tau: float, min_visit: int, qbl
     """Every GPU stop is a valid stop of the rule within the band: the test value
     at the stop is <= tau (unless the list ran out) and every earlier value from
     min_visit on is > tau, each up to OSK_BAND relative."""
-    n_bad = 0
     for h in range(w.hq):
         for qb in qblocks:
             e0, e1 = int(w.row_ptr[qb]), int(w.row_ptr[qb + 1])
@@ -222,7 +221,6 @@ def check_visited(w: W.Workload, visited, ratio, tau: float, min_visit: int, qbl
                 assert vis >= min_visit and r[vis - 1] <= tau * (1 + OSK_BAND), (h, qb, vis, r[vis - 1])
             early = r[min_visit - 1:vis - 1]
             assert np.all(early > tau * (1 - OSK_BAND)), (h, qb, vis, early.min() if len(early) else None)
-            n_bad += 0
     return True
 
 

@@ -132,3 +132,34 @@ def test_block_mask_generator():
     # counted flops: 128x128 pairs per visible off-diagonal block, half for the diagonal, g heads each
     per_head = sum(W.sparse_budget(i) - 0.5 for i in range(32))
     assert W.counted_flops(w) == 4 * 64 * 2 * 128 * 128 * 2 * per_head
+
+
+def test_osk_generator():
+    """Planted-relevance workload: deterministic bytes; each query block's list is its
+    own block, then the top ceil(budget * i) earlier blocks by proxy score, highest
+    first; keys of a block share one boost along the head's direction, which the
+    query rows all see alike (query noise is orthogonal to it)."""
+    w = W.make_osk("o", 8, 4096, 4, 2, 64)
+    assert sha(w.q) == "605d8d9b73d51d542557d74b5439b3e94216953ee6e9f99d14c0278ae2481bde"
+    assert sha(w.k) == "11437e094208718a741a9527f40b86be287a58ca5cb07b5d3d18d2f294392b9f"
+    assert sha(w.col_idx) == "8eb6b0fbf3d64e5b8caa7ed17d0a2639ed00b6312ed6c15de4a2b74eef9e28a3"
+    g = W.streams(8)["block_scores"]
+    a = 4.0 * g.exponential(size=32)
+    proxy = a + 0.5 * g.standard_normal(32)
+    e = g.standard_normal((2, 64))
+    e /= np.linalg.norm(e, axis=1, keepdims=True)
+    for i in range(32):
+        ents = w.col_idx[w.row_ptr[i]:w.row_ptr[i + 1]]
+        assert ents[0] == i and len(ents) == 1 + int(np.ceil(0.25 * i))
+        assert np.all(ents[1:] < i) and len(set(ents)) == len(ents)
+        assert np.all(np.diff(proxy[ents[1:]]) <= 0)
+    q = W.bf16_bits_to_f32(w.q).reshape(4096, 4, 64).astype(np.float64)
+    k = W.bf16_bits_to_f32(w.k).reshape(4096, 2, 64).astype(np.float64)
+    # every query of head h has component ~mu along e of its KV head (bf16 rounding aside)
+    for h in range(4):
+        comp = q[:, h] @ e[h // 2]
+        assert np.abs(comp - 5.0).max() < 0.1
+    # a key's component along e is its block's relevance plus N(0,1) noise
+    kcomp = k[:, 0] @ e[0]
+    blk_mean = kcomp.reshape(32, 128).mean(1)
+    assert np.corrcoef(blk_mean, a)[0, 1] > 0.99
