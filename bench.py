@@ -362,7 +362,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: i.i.d. N(0,1) inputs rounded to bf16, seeded",
+        "data": ("synthetic: seeded N(0,1) noise plus planted block relevance, rounded to bf16" if osk else
+                 "synthetic: i.i.d. N(0,1) inputs rounded to bf16, seeded"),
         "config": {"workload": f"{w.name}: dense causal MHA B={w.batch} H={w.hq} S={w.seqlen} D={w.d}"
                    if w.name == "mha" else w.name,
                    "batch": w.batch, "seq_len": w.seqlen, "heads_q": w.hq, "heads_kv": w.hkv,
