@@ -8,7 +8,8 @@ module, and this module never imports the product package.
 definition (see the header of ``oracle_attn.c`` for the formula and the
 passages of the pages it follows); ``attn_bwd`` its exact gradients (header
 of ``oracle_bwd.c``); ``attn_fwd_osk`` ordered skipping along a block list
-with the stopping rule stated in the header of ``oracle_osk.c``.  Every function's parity status is "pinned":
+with the stopping rule stated in the header of ``oracle_osk.c``;
+``entmax_fwd`` alpha-entmax attention (header of ``oracle_entmax.c``).  Every function's parity status is "pinned":
 ``tests/test_oracle_pins.py``, ``test_oracle_mask_pins.py`` and
 ``test_oracle_bwd_pins.py`` tie them to brute force, finite differences,
 closed forms and invariants that do not go through this code.
@@ -24,7 +25,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRCS = [os.path.join(HERE, "oracle_attn.c"), os.path.join(HERE, "oracle_bwd.c"),
-        os.path.join(HERE, "oracle_osk.c")]
+        os.path.join(HERE, "oracle_osk.c"), os.path.join(HERE, "oracle_entmax.c")]
 LIB = os.path.join(HERE, "liboracle_attn.so")
 
 _lib = None
@@ -68,6 +69,10 @@ def _load():
                                             ctypes.c_int, ctypes.c_double, P, P, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_double, ctypes.c_int, P, ctypes.c_int, P, P, P, P,
                                             ctypes.c_int]
+        lib.oracle_entmax_fwd.restype = ctypes.c_int
+        lib.oracle_entmax_fwd.argtypes = [P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_int, P, P, P,
+                                          P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.oracle_default_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -216,6 +221,42 @@ def attn_fwd_osk(q, k, v, causal: bool, scale: float, row_ptr, col_idx, tau: flo
     if rc != 0:
         raise RuntimeError(f"oracle_attn_fwd_osk failed with code {rc}")
     return out, lse, visited, ratio
+
+
+def entmax_fwd(q, k, v, cu_seqlens, causal: bool, scale: float, alpha: float, bins: int = 32,
+               with_mask: bool = False, block: int = 128, nthreads: int = 0):
+    """Exact alpha-entmax attention forward (header of ``oracle_entmax.c``).
+
+    q: float64 [T, Hq, D]; k, v: float64 [T, Hkv, D]; cu_seqlens: int [n+1]
+    Returns (O [T, Hq, D], tau [T, Hq], tau_hist [T, Hq]) and, with
+    ``with_mask``, the block mask uint32 [n, Hq, n_qblk, words] (n_qblk from
+    the longest sequence).
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    n_seqs = len(cu) - 1
+    t, hq, d = q.shape
+    hkv = k.shape[1]
+    out = np.zeros((t, hq, d))
+    tau = np.zeros((t, hq))
+    tau_h = np.zeros((t, hq))
+    mask = None
+    n_qblk = words = 1
+    if with_mask:
+        lmax = int(np.diff(cu).max()) if n_seqs else 0
+        n_qblk = max(1, -(-lmax // block))
+        words = max(1, -(-n_qblk // 32))
+        mask = np.zeros((n_seqs, hq, n_qblk, words), dtype=np.uint32)
+    rc = _load().oracle_entmax_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), n_seqs, hq, hkv, d, int(bool(causal)),
+                                   float(scale), float(alpha), int(bins), _ptr(out), _ptr(tau), _ptr(tau_h),
+                                   _ptr(mask), int(block), n_qblk, words, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_entmax_fwd failed with code {rc}")
+    if with_mask:
+        return out, tau, tau_h, mask
+    return out, tau, tau_h
 
 
 def run_workload(w, rows=None, nthreads: int = 0, with_psum: bool = False):
