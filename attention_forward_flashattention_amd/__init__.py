@@ -78,6 +78,12 @@ def load_library(path: str = LIB_PATH):
         lib.attn_fwd_osk_validate.restype = ctypes.c_int
         lib.attn_fwd_osk_validate.argtypes = [T, T, T, ctypes.c_int, ctypes.c_float, BL, ctypes.c_float,
                                               ctypes.c_int, T]
+        lib.attn_entmax_fwd.restype = ctypes.c_int
+        lib.attn_entmax_fwd.argtypes = [T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_int, T,
+                                        P, P, ctypes.c_int, P, P]
+        lib.attn_entmax_fwd_validate.restype = ctypes.c_int
+        lib.attn_entmax_fwd_validate.argtypes = [T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                                 ctypes.c_int, T, ctypes.c_int]
         lib.attn_bwd.restype = ctypes.c_int
         lib.attn_bwd.argtypes = [T, T, T, T, T, P, P, ctypes.c_int, ctypes.c_float, BM, T, T, T, P,
                                  ctypes.c_size_t, P]
@@ -254,6 +260,49 @@ def attn_fwd_osk(q, k, v, block_list: Tuple, tau: float, min_visit: int = 2, cau
     if st != ATTN_OK:
         raise AttnError(st, status_str(st), "attn_fwd_osk")
     return out, lse, visited
+
+
+def attn_entmax_fwd(q, k, v, alpha: float, causal: bool = False, scale: Optional[float] = None,
+                    n_iter: int = 16, out=None, return_mask: bool = False, return_tau_init: bool = False,
+                    stream=None):
+    """alpha-entmax attention forward (``attn_entmax_fwd`` in include/attn_fwd.h).
+
+    q: bf16 [B, S, Hq, D]; k, v: bf16 [B, S, Hkv, D]
+    Returns (out, tau) plus the block mask int32 [B, Hq, n_qblk, words] with
+    ``return_mask`` and the histogram bound [B, Hq, S] with ``return_tau_init``.
+    """
+    import torch
+
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, S, H, D]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError(f"{name} must be a bfloat16 device tensor")
+    batch, seqlen, hq, d = (int(x) for x in q.shape)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    tau = torch.empty((batch, hq, seqlen), dtype=torch.float32, device=q.device)
+    n_qblk = (seqlen + 127) // 128
+    words = max(1, (n_qblk + 31) // 32)
+    mask = torch.zeros((batch, hq, n_qblk, words), dtype=torch.int32, device=q.device) if return_mask else None
+    tau0 = torch.empty_like(tau) if return_tau_init else None
+    dq, dk, dv, do = (describe(t, batch, seqlen, False) for t in (q, k, v, out))
+    st = lib.attn_entmax_fwd(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(bool(causal)),
+                             float(scale), float(alpha), int(n_iter), ctypes.byref(do),
+                             ctypes.c_void_p(tau.data_ptr()),
+                             ctypes.c_void_p(mask.data_ptr()) if mask is not None else None, words,
+                             ctypes.c_void_p(tau0.data_ptr()) if tau0 is not None else None,
+                             ctypes.c_void_p(_stream_handle(stream)))
+    if st != ATTN_OK:
+        raise AttnError(st, status_str(st), "attn_entmax_fwd")
+    res = (out, tau)
+    if return_mask:
+        res += (mask,)
+    if return_tau_init:
+        res += (tau0,)
+    return res
 
 
 def attn_bwd(q, k, v, out, dout, lse, cu_seqlens=None, causal: bool = False,

@@ -1,4 +1,5 @@
-"""Build the HIP library ``libattn_fwd.so`` (forward and backward kernels) for gfx950 with hipcc (in-tree)."""
+"""Build the HIP library ``libattn_fwd.so`` (forward, backward and alpha-entmax kernels) for gfx950
+with hipcc (in-tree)."""
 from __future__ import annotations
 
 import os
@@ -7,7 +8,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "attn_fwd.hip"), os.path.join(PKG, "csrc", "attn_bwd.hip")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip", "attn_entmax.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_fwd.so")
 

@@ -1,0 +1,477 @@
+// attn_entmax.hip — alpha-entmax attention forward for AMD Instinct MI355X (gfx950).
+//
+// alpha-entmax replaces the softmax normaliser by a threshold tau found by
+// root finding (AdaSplash-2 explainer, technical summary section 1):
+//   p_j = [(alpha-1) z_j - tau]_+^(1/(alpha-1)),  sum_j p_j = 1,  O = sum_j p_j v_j.
+// Following the explainer's section 2, one workgroup (128 query rows of one
+// (sequence, query head), four wave64s of 32 rows) makes these passes over
+// the keys it may see, each streaming 64-key K tiles through double-buffered
+// LDS with direct global-to-LDS loads and forming the transposed score tile
+// S^T = K Q^T with 32x32x16 bf16 MFMAs (lane = query row, as in the softmax
+// kernel):
+//   1. the row maximum m;
+//   2. a histogram of the scores in the window [m - W, m], W = 1/(alpha-1)
+//      (only those can carry weight), kBins bins per row in LDS; each score
+//      counts at its bin's lower edge, so the root tau_h of the histogram's
+//      mass equation is a lower bound of the true tau; each lane solves it
+//      by bisection over the bins;
+//   3. up to n_iter refinement passes (fewer once every row of the workgroup
+//      has |sum p - 1| <= 4e-6), each forming the power sums the update needs
+//      at the current tau and taking one step of the hybrid solver (Halley
+//      for alpha <= 1.5, Newton for alpha <= 2, a secant through the bracket
+//      ends (regula falsi, Illinois rule) above), with a
+//      bisection step whenever the update leaves the bracket [lo, hi] kept
+//      from the signs seen so far; every pass also marks, in an LDS
+//      bit-packed block mask, each 128-key block whose scores can clear the
+//      bracket's lower end at the start of the pass (so every block with a
+//      non-zero weight at the final tau is marked);
+//   4. the output pass, which visits only the marked blocks (walking the
+//      mask's set bits), forms p in registers and accumulates O^T += V^T P^T
+//      with V^T from LDS transpose reads; O is divided by sum p.
+// tau (fp32) and the bit-packed block mask can be written out.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_common.h"
+#include "attn_fwd.h"
+
+namespace {
+
+using namespace attn_detail;
+
+constexpr int kBins = 32;       // histogram bins per row
+constexpr int kMaxKBlocks = 16384;  // key blocks a mask row holds in LDS
+
+struct EntParams {
+  const uint16_t *q, *k, *v;
+  uint16_t *o;
+  float *tau;          // [B, Hq, S] or null
+  float *tau_init;     // [B, Hq, S] or null: the histogram bound tau_h
+  uint32_t *mask;      // [B, Hq, n_qblk, mask_words] or null
+  int mask_words;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int batch, seqlen, hq, group, n_tiles, n_iter, causal;
+  float scale, alpha;
+};
+
+// u^e for u > 0 (0 otherwise)
+__device__ __forceinline__ float powpos(float u, float e) {
+  return u > 0.f ? __builtin_amdgcn_exp2f(e * __builtin_amdgcn_logf(u)) : 0.f;
+}
+
+template <int kLoads>
+__device__ __forceinline__ void issue_rows(char *l, const uint16_t *g, const int64_t *off,
+                                           const int *lrow, int64_t ss, int rows_left) {
+#pragma unroll
+  for (int n = 0; n < kLoads; ++n) {
+    const int64_t back = min(rows_left - 1 - lrow[n], 0);
+    __builtin_amdgcn_global_load_lds(g + off[n] + back * ss, (lds_void_t *)(l + n * 1024), 16, 0, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
+  using L = Lds<D>;
+  constexpr int kNW = 4;
+  constexpr int kBM = 128;
+  constexpr int kBN = 64;
+  constexpr int kRowBytes = D * 2;
+  constexpr int kChunks = D / 8;
+  constexpr int kDc = D / 16;
+  constexpr int kDt = D / 32;
+  constexpr int kKt = kBN / 32;
+  constexpr int kTileBytes = kBN * kRowBytes;
+  constexpr int kBufBytes = 2 * kTileBytes;  // K then V
+  constexpr int kLoads = kTileBytes / 1024 / kNW;
+  constexpr int kHistBytes = kBM * kBins * 4;
+  constexpr int kMaskBytes = kMaxKBlocks / 8;
+  // The passes before the output pass load K only, so the histogram can live
+  // in the V half of buffer 0 when it fits there (it is read into registers
+  // before the output pass loads V).
+  constexpr bool kHistInV = kTileBytes >= kHistBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes + kMaskBytes + 16 + (kHistInV ? 0 : kHistBytes)];
+  uint32_t *mbits = reinterpret_cast<uint32_t *>(smem + 2 * kBufBytes);
+  uint32_t *done_flag = mbits + kMaxKBlocks / 32;  // one per wave
+  uint32_t *hist = reinterpret_cast<uint32_t *>(kHistInV ? smem + kTileBytes : smem + 2 * kBufBytes + kMaskBytes + 16);
+
+  const int n_units = p.batch * p.hq;
+  const int rank = blockIdx.x / n_units;
+  const int unit = blockIdx.x % n_units;
+  const int tile = p.causal ? p.n_tiles - 1 - rank : rank;  // causal: heaviest first
+  const int b = unit / p.hq, h = unit % p.hq, kvh = h / p.group;
+  const int len = p.seqlen;
+  const int q0 = tile * kBM;
+  const uint16_t *qg = p.q + (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+  const uint16_t *kg = p.k + (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+  const uint16_t *vg = p.v + (int64_t)b * p.v_sb + (int64_t)kvh * p.v_sh;
+  uint16_t *og = p.o + (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int j16 = lane & 15;
+  const int row = wave * 32 + l32;  // row within the workgroup
+  const int qrow = q0 + row;
+  const bool live = qrow < len;
+
+  const int kv_end = p.causal ? min(len, q0 + kBM) : len;
+  const int n_kv = (kv_end + kBN - 1) / kBN;
+  const int n_kblk = (kv_end + kListBlock - 1) / kListBlock;
+  const float a1 = p.alpha - 1.f;
+  const float e = 1.f / a1;
+  const float W = e;  // window width 1/(alpha-1)
+
+  // ---- K / V tile loads
+  int64_t koff[kLoads], voff[kLoads];
+  int lrow[kLoads];
+  const int slot_byte0 = wave * kLoads * 1024;
+#pragma unroll
+  for (int n = 0; n < kLoads; ++n) {
+    const int slot = (wave * kLoads + n) * 64 + lane;
+    const int r = slot / kChunks, pc = slot % kChunks;
+    lrow[n] = r;
+    koff[n] = (int64_t)r * p.k_ss + (pc ^ L::kswz(r)) * 8;
+    voff[n] = (int64_t)r * p.v_ss + L::v_logical_chunk(r, pc) * 8;
+  }
+  auto issue = [&](int buf, int kv, bool with_v) {
+    char *kb = smem + buf * kBufBytes + slot_byte0;
+    issue_rows<kLoads>(kb, kg + (int64_t)kv * p.k_ss, koff, lrow, p.k_ss, len - kv);
+    if (with_v) issue_rows<kLoads>(kb + kTileBytes, vg + (int64_t)kv * p.v_ss, voff, lrow, p.v_ss, len - kv);
+  };
+
+  // ---- Q rows (MFMA B operand), zero past the end
+  bf16x8_t qreg[kDc];
+#pragma unroll
+  for (int dc = 0; dc < kDc; ++dc) {
+    uint4_t x = {0u, 0u, 0u, 0u};
+    if (live) x = ld_global16(qg + (int64_t)qrow * p.q_ss + dc * 16 + hi * 8);
+    qreg[dc] = __builtin_bit_cast(bf16x8_t, x);
+  }
+  int kaddr[kDc];
+#pragma unroll
+  for (int dc = 0; dc < kDc; ++dc) kaddr[dc] = L::kq(l32, dc * 2 + hi);
+
+  // S^T of one K tile: s[kt][i] is the score of key kv0 + 32 kt + 8 (i/4) +
+  // 4 hi + i%4 for this lane's row; keys past kv_end, after the row (causal)
+  // or rows past the end get -inf
+  auto scores = [&](const char *sK, int kv0, floatx16_t (&s)[kKt]) {
+#pragma unroll
+    for (int kt = 0; kt < kKt; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+#pragma unroll
+      for (int dc = 0; dc < kDc; ++dc) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(sK + kaddr[dc] + kt * 32 * kRowBytes);
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], s[kt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < kKt; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kv0 + kt * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+        s[kt][i] = (key >= kv_end || (p.causal && key > qrow) || !live) ? -INFINITY : s[kt][i] * p.scale;
+      }
+  };
+
+  // One dense pass over the KV tiles: f(kv0, s) for each.
+  auto dense_pass = [&](auto f) {
+    issue(0, 0, false);
+    for (int it = 0; it < n_kv; ++it) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      if (it + 1 < n_kv) issue((it + 1) & 1, (it + 1) * kBN, false);
+      floatx16_t s[kKt];
+      scores(smem + (it & 1) * kBufBytes, it * kBN, s);
+      f(it * kBN, s);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  };
+
+  // ---- pass 1: row maximum
+  float m = -INFINITY;
+  dense_pass([&](int, floatx16_t(&s)[kKt]) {
+#pragma unroll
+    for (int kt = 0; kt < kKt; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, s[kt][i]);
+  });
+  m = half_max(m);
+  const int n_allowed = p.causal ? qrow + 1 : len;
+
+  // ---- pass 2: histogram of the window [m - W, m]
+  for (int i = tid; i < kBM * kBins; i += 256) hist[i] = 0u;
+  for (int i = tid; i < (n_kblk + 31) / 32; i += 256) mbits[i] = 0u;
+  __syncthreads();
+  const float base = m - W;
+  const float inv_bw = kBins / W;
+  dense_pass([&](int, floatx16_t(&s)[kKt]) {
+#pragma unroll
+    for (int kt = 0; kt < kKt; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float t = (s[kt][i] - base) * inv_bw;  // -inf for masked scores
+        if (t >= 0.f) {
+          const int bin = min((int)t, kBins - 1);
+          atomicAdd(&hist[row * kBins + bin], 1u);
+        }
+      }
+  });
+  // the histogram's root by bisection (both lane halves hold the same row and
+  // the same counts, so both compute the same tau_h)
+  float cnt[kBins];
+#pragma unroll
+  for (int bb = 0; bb < kBins; ++bb) cnt[bb] = (float)hist[row * kBins + bb];
+  float lo = a1 * base - 1.f, hi_t = a1 * m;
+  for (int it = 0; it < 30; ++it) {
+    const float mid = 0.5f * (lo + hi_t);
+    float sum = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < kBins; ++bb) sum += cnt[bb] * powpos(a1 * (base + bb * (W / kBins)) - mid, e);
+    if (sum >= 1.f)
+      lo = mid;
+    else
+      hi_t = mid;
+  }
+  const float tau_h = lo;  // lo keeps sum >= 1: a lower bound of the histogram's root
+  // ---- pass 3: refinement.  Bracket [blo, bhi] of the true tau: tau_h is
+  // below it; counting every score at its bin's upper edge instead would
+  // raise every score by at most W/B and the root by at most (alpha-1) W/B =
+  // 1/B, so tau_h + 1/B is above it (with a little room for fp32 rounding);
+  // and at (alpha-1) m - n^(1-alpha) every weight is at most 1/n.
+  float blo = tau_h;
+  float bhi = fminf(a1 * m - __builtin_amdgcn_exp2f((1.f - p.alpha) *
+                                                     __builtin_amdgcn_logf((float)max(n_allowed, 1))),
+                    tau_h + (1.f / kBins) * (1.f + 1e-4f) + 1e-6f * fabsf(tau_h));
+  if (!(bhi > blo)) bhi = blo + 1e-6f * fmaxf(1.f, fabsf(blo));
+  float t = tau_h;
+  // regula falsi state (alpha > 2): g at the bracket ends, and which end moved last
+  float glo = 0.f, ghi = 0.f;
+  int side = 0;
+  const float kTol = 4e-6f;  // |sum p - 1| at which a row counts as converged (fp32 sums)
+  const int m_words = (n_kblk + 31) / 32;
+  for (int r = 0; r < p.n_iter; ++r) {
+    const bool first = r == 0;
+    const float t_mask = blo;  // <= every later tau
+    // every pass rebuilds the block mask, so the mask of the pass the loop
+    // ends after covers the final tau
+    for (int w = tid; w < m_words; w += 256) mbits[w] = 0u;
+    __syncthreads();
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, shi = 0.f;
+    dense_pass([&](int kv0, floatx16_t(&s)[kKt]) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < kKt; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float u = a1 * s[kt][i] - t;
+          tmax = fmaxf(tmax, s[kt][i]);
+          if (u > 0.f) {
+            const float pu = powpos(u, e);
+            s0 += pu;
+            if (p.alpha <= 2.f) {
+              const float r1 = pu / u;
+              s1 += r1;
+              if (p.alpha <= 1.5f) s2 += r1 / u;
+            }
+          }
+          if (p.alpha > 2.f && first) shi += powpos(a1 * s[kt][i] - bhi, e);  // g at the upper end
+        }
+      // mark the 128-key block if some live row's scores clear t_mask
+      const bool any = __builtin_amdgcn_ballot_w64(live && a1 * tmax > t_mask) != 0;
+      if (any && lane == 0) atomicOr(&mbits[kv0 / kListBlock / 32], 1u << ((kv0 / kListBlock) % 32));
+    });
+    s0 = half_sum(s0);
+    s1 = half_sum(s1);
+    s2 = half_sum(s2);
+    const float g = s0 - 1.f;
+    if (p.alpha > 2.f && first) ghi = half_sum(shi) - 1.f;
+    const bool conv = fabsf(g) <= kTol;  // converged: keep t (the bracket may have closed on it)
+    // the workgroup stops once every live row has converged
+    const bool wave_done = __builtin_amdgcn_ballot_w64(live && !conv) == 0;
+    if (lane == 0) done_flag[wave] = wave_done ? 1u : 0u;
+    __syncthreads();
+    const bool all_done = done_flag[0] & done_flag[1] & done_flag[2] & done_flag[3];
+    if (all_done) break;
+    if (conv) continue;
+    if (g > 0.f) {
+      blo = t;
+      glo = g;
+      if (side == 1) ghi *= 0.5f;  // Illinois: the other end stayed twice
+      side = 1;
+    } else {
+      bhi = t;
+      ghi = g;
+      if (side == -1) glo *= 0.5f;
+      side = -1;
+    }
+    float t_new;
+    if (p.alpha <= 1.5f) {  // Halley
+      const float g1 = -e * s1, g2 = e * (e - 1.f) * s2;
+      t_new = t - 2.f * g * g1 / (2.f * g1 * g1 - g * g2);
+    } else if (p.alpha <= 2.f) {  // Newton
+      t_new = t - g / (-e * s1);
+    } else {  // secant through the bracket ends (regula falsi)
+      t_new = ghi < glo ? blo - glo * (bhi - blo) / (ghi - glo) : 0.5f * (blo + bhi);
+    }
+    if (!(t_new >= blo && t_new <= bhi)) t_new = 0.5f * (blo + bhi);  // bisection fallback
+    t = t_new;
+  }
+  __syncthreads();  // the mask is complete
+
+  // ---- pass 4: output over the marked blocks
+  floatx16_t oacc[kDt];
+#pragma unroll
+  for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+  float l = 0.f;
+  int n_blk = 0;
+  for (int w = 0; w < m_words; ++w) n_blk += __builtin_popcount(mbits[w]);
+  const int n_out = 2 * n_blk;  // two 64-key tiles per block
+  int c_w = -1;
+  uint32_t c_bits = 0;
+  int c_blk = 0;
+  auto out_kv = [&](int it) -> int {  // in order
+    if ((it & 1) == 0) {
+      while (c_bits == 0) c_bits = mbits[++c_w];
+      c_blk = 32 * c_w + __builtin_ctz(c_bits);
+      c_bits &= c_bits - 1u;
+    }
+    return c_blk * kListBlock + (it & 1) * kBN;
+  };
+  uint32_t vlds[kDt];
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char_t *)smem;
+#pragma unroll
+  for (int dt = 0; dt < kDt; ++dt)
+    vlds[dt] = smem_lds + (uint32_t)L::vv(4 * hi + (j16 >> 2), 2 * dt + (l32 >> 4), (j16 & 3) * 8);
+  int kv_cur = n_out > 0 ? out_kv(0) : 0;
+  if (n_out > 0) issue(0, kv_cur, true);
+  for (int it = 0; it < n_out; ++it) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    int kv_nxt = 0;
+    if (it + 1 < n_out) {
+      kv_nxt = out_kv(it + 1);
+      issue((it + 1) & 1, kv_nxt, true);
+    }
+    const int kv0 = kv_cur;
+    kv_cur = kv_nxt;
+    const int boff = (it & 1) * kBufBytes;
+    floatx16_t s[kKt];
+    scores(smem + boff, kv0, s);
+    bf16x8_t pb[kKt][2];
+#pragma unroll
+    for (int kt = 0; kt < kKt; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = powpos(a1 * s[kt][i] - t, e);
+        l += pv;
+        pb[kt][i >> 3][i & 7] = (__bf16)pv;
+      }
+#pragma unroll
+    for (int kt = 0; kt < kKt; ++kt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt) {
+          const uint32_t addr = vlds[dt] + boff + kTileBytes + (kt * 32 + c * 16) * kRowBytes;
+          bf16x8_t a = tr_pair<0, 8 * kRowBytes>(addr);
+          lgkm_wait<0>(a);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][c], oacc[dt], 0, 0, 0);
+        }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  const float l_tot = half_sum(l);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // ---- epilogue: O (bf16), tau, tau_h, the mask row
+  if (live) {
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int dcol = dt * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
+        og[(int64_t)qrow * p.o_ss + dcol] = __builtin_bit_cast(uint16_t, (__bf16)(oacc[dt][i] * inv));
+      }
+    if (hi == 0) {
+      const int64_t idx = ((int64_t)b * p.hq + h) * p.seqlen + qrow;
+      if (p.tau) p.tau[idx] = t;
+      if (p.tau_init) p.tau_init[idx] = tau_h;
+    }
+  }
+  if (p.mask) {
+    uint32_t *mrow = p.mask + (((int64_t)b * p.hq + h) * p.n_tiles + tile) * p.mask_words;
+    for (int w = tid; w < p.mask_words; w += 256) mrow[w] = w < m_words ? mbits[w] : 0u;
+  }
+}
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+bool stride_ok(int64_t s) { return ((s * 2) % 16) == 0; }
+
+}  // namespace
+
+extern "C" int attn_entmax_fwd_validate(const attn_tensor_t *q, const attn_tensor_t *k,
+                                        const attn_tensor_t *v, int causal, float scale,
+                                        float alpha, int n_iter, const attn_tensor_t *out,
+                                        int mask_words) {
+  const int st = attn_fwd_validate(q, k, v, nullptr, causal, scale, nullptr, out);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(alpha) || !(alpha > 1.f) || n_iter < 1 || n_iter > 32) return ATTN_ERR_INVALID_ARG;
+  // Above alpha = 3 the weights u^(1/(alpha-1)) rise so steeply from the
+  // support edge that fp32 scores cannot reproduce exact weights to the
+  // forward's tolerances (a key 1e-6 above the edge already weighs 0.03 at
+  // alpha = 5); below 1.05 the window 1/(alpha-1) outgrows fp32 range use.
+  if (alpha > 3.f || alpha < 1.05f) return ATTN_ERR_UNSUPPORTED;
+  if (q->head_dim == 256) return ATTN_ERR_UNSUPPORTED;
+  const int64_t n_blk = (q->seqlen + kListBlock - 1) / kListBlock;
+  if (n_blk > kMaxKBlocks) return ATTN_ERR_UNSUPPORTED;
+  if (mask_words < 0) return ATTN_ERR_INVALID_ARG;
+  if (mask_words > 0 && (int64_t)mask_words * 32 < n_blk) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+extern "C" int attn_entmax_fwd(const attn_tensor_t *q, const attn_tensor_t *k,
+                               const attn_tensor_t *v, int causal, float scale, float alpha,
+                               int n_iter, attn_tensor_t *out, float *tau, uint32_t *block_mask,
+                               int mask_words, float *tau_init, void *stream) {
+  const int st = attn_entmax_fwd_validate(q, k, v, causal, scale, alpha, n_iter, out,
+                                          block_mask ? mask_words : 0);
+  if (st != ATTN_OK) return st;
+  if (q->batch == 0 || q->seqlen == 0) return ATTN_OK;
+  EntParams p;
+  p.q = static_cast<const uint16_t *>(q->data);
+  p.k = static_cast<const uint16_t *>(k->data);
+  p.v = static_cast<const uint16_t *>(v->data);
+  p.o = static_cast<uint16_t *>(out->data);
+  p.tau = tau;
+  p.tau_init = tau_init;
+  p.mask = block_mask;
+  p.mask_words = mask_words;
+  p.q_sb = q->stride_batch; p.q_ss = q->stride_seq; p.q_sh = q->stride_head;
+  p.k_sb = k->stride_batch; p.k_ss = k->stride_seq; p.k_sh = k->stride_head;
+  p.v_sb = v->stride_batch; p.v_ss = v->stride_seq; p.v_sh = v->stride_head;
+  p.o_sb = out->stride_batch; p.o_ss = out->stride_seq; p.o_sh = out->stride_head;
+  p.batch = q->batch;
+  p.seqlen = q->seqlen;
+  p.hq = q->heads;
+  p.group = q->heads / k->heads;
+  p.n_tiles = (q->seqlen + 127) / 128;
+  p.n_iter = n_iter;
+  p.causal = causal;
+  p.scale = scale;
+  p.alpha = alpha;
+  const int64_t grid = (int64_t)p.n_tiles * p.batch * p.hq;
+  void *args[] = {&p};
+  const void *fn = q->head_dim == 64 ? reinterpret_cast<const void *>(&attn_entmax_kernel<64>)
+                                     : reinterpret_cast<const void *>(&attn_entmax_kernel<128>);
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}

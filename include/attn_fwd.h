@@ -210,6 +210,51 @@ int attn_fwd_osk_validate(const attn_tensor_t *q, const attn_tensor_t *k, const 
                           int causal, float scale, const attn_block_list_t *block_list, float tau,
                           int min_visit, const attn_tensor_t *out);
 
+/*
+ * attn_entmax_fwd — alpha-entmax attention forward.
+ *
+ * The AdaSplash-2 explainer (technical summary sections 1-2) replaces softmax
+ * by alpha-entmax: for each query row, with scores z_j = scale * q.k_j over
+ * the allowed keys (all keys of the sequence, or j <= i under causal
+ * masking),
+ *     p_j = [(alpha - 1) z_j - tau]_+ ^ (1 / (alpha - 1)),   sum_j p_j = 1,
+ *     O = sum_j p_j v_j,
+ * so most weights are exactly zero.  tau has no closed form: the kernel bins
+ * the scores of the window [m - 1/(alpha-1), m] (m the row max) into a
+ * histogram whose root is a lower bound of tau, then takes steps of a hybrid
+ * root finder (Halley for alpha <= 1.5, Newton for alpha <= 2, a secant
+ * through the bracket ends above) with a bisection fallback -- until every
+ * row of a 128-row tile has |sum p - 1| <= 4e-6 or n_iter steps are done --
+ * and finally visits only the 128 x 128 blocks that can hold a non-zero
+ * weight.  O is divided by sum p at the final tau (1 when tau has converged).
+ *
+ *   q [B, S, Hq, D], k, v [B, S, Hkv, D] bf16 (fixed-length batches)
+ *   alpha        in [1.05, 3] (above 3 the weights rise too steeply from the
+ *                support edge for fp32 scores to reproduce exact weights)
+ *   n_iter       at most this many refinement steps after the histogram start, 1..32
+ *   out          [B, S, Hq, D] bf16
+ *   tau          NULL, or float32 [B, Hq, S]: the final threshold per row
+ *   block_mask   NULL, or uint32 [B, Hq, ceil(S/128), mask_words]: bit kb % 32
+ *                of word kb / 32 of query block qb's row is set when block kb
+ *                was visited (a superset of the blocks with a non-zero weight)
+ *   mask_words   words per mask row, >= ceil(ceil(S/128) / 32) (with a mask)
+ *   tau_init     NULL, or float32 [B, Hq, S]: the histogram lower bound
+ * Returns what attn_fwd returns for q, k, v, out (no cu_seqlens, no list), or
+ * ATTN_ERR_INVALID_ARG for alpha <= 1 or not finite, n_iter outside 1..32, or
+ * too few mask words; ATTN_ERR_UNSUPPORTED for alpha outside [1.05, 3],
+ * head_dim 256, or more than 16384 blocks of 128 per sequence.
+ */
+int attn_entmax_fwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                    int causal, float scale, float alpha, int n_iter, attn_tensor_t *out,
+                    float *tau, uint32_t *block_mask, int mask_words, float *tau_init,
+                    void *stream);
+
+/* The argument checks of attn_entmax_fwd alone (host code only); mask_words
+ * is 0 when no mask is written. */
+int attn_entmax_fwd_validate(const attn_tensor_t *q, const attn_tensor_t *k,
+                             const attn_tensor_t *v, int causal, float scale, float alpha,
+                             int n_iter, const attn_tensor_t *out, int mask_words);
+
 /* Static description of a status code (never NULL). */
 const char *attn_status_str(int status);
 

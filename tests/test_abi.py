@@ -26,7 +26,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_validate", "attn_bwd_workspace_size", "attn_fwd",
+    assert declared_functions() == ["attn_bwd", "attn_bwd_validate", "attn_bwd_workspace_size",
+                                    "attn_entmax_fwd", "attn_entmax_fwd_validate", "attn_fwd",
                                     "attn_fwd_mask", "attn_fwd_mask_validate", "attn_fwd_osk",
                                     "attn_fwd_osk_validate", "attn_fwd_validate", "attn_status_str",
                                     "attn_version"]
@@ -243,3 +244,23 @@ def test_osk_argument_checks():
     assert osk_validate(q, kv, kv, bl, min_visit=0) == -1
     assert osk_validate(desc(b=2, s=256, h=4), desc(b=2, s=256, h=2), desc(b=2, s=256, h=2), bl) == -2  # batch > 1
     assert osk_validate(q, kv, kv, AttnBlockList(FAKE, FAKE, 64, 128, 4)) == -2                          # block size
+
+
+# ---------------------------------------------------------------------------
+# attn_entmax_fwd argument checks (host only)
+# ---------------------------------------------------------------------------
+def test_entmax_argument_checks():
+    lib = attn.load_library()
+    q, kv = desc(b=2, s=256, h=4), desc(b=2, s=256, h=2)
+
+    def val(alpha=1.5, n_iter=2, words=0, qd=q, kd=kv):
+        return lib.attn_entmax_fwd_validate(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(kd), 1, 0.125,
+                                            alpha, n_iter, ctypes.byref(qd), words)
+    assert val() == 0 and val(alpha=2.0, words=1) == 0 and val(alpha=3.0, n_iter=32) == 0
+    assert val(alpha=1.0) == -1 and val(alpha=float("nan")) == -1 and val(alpha=float("inf")) == -1
+    assert val(n_iter=0) == -1 and val(n_iter=33) == -1
+    assert val(alpha=1.01) == -2 and val(alpha=3.5) == -2
+    assert val(qd=desc(b=2, s=256, h=4, d=256), kd=desc(b=2, s=256, h=2, d=256)) == -2
+    s = 128 * 33                                        # 33 blocks need 2 mask words
+    assert val(words=1, qd=desc(b=1, s=s, h=4), kd=desc(b=1, s=s, h=2)) == -1
+    assert val(words=2, qd=desc(b=1, s=s, h=4), kd=desc(b=1, s=s, h=2)) == 0
