@@ -113,6 +113,39 @@ def osk_flops(w: W.Workload, visited: np.ndarray):
     return flops, 1.0 - float(visited.sum()) / listed
 
 
+def time_entmax(attn, torch, w, q, k, v, softmax_ms, n, settle_s, alpha=1.5):
+    """Average time of one attn_entmax_fwd call (alpha-entmax forward, solver
+    run to convergence) on the same inputs, against the softmax forward's
+    time, and the share of causal blocks its output pass visits."""
+    out = torch.empty_like(q)
+
+    def run():
+        return attn.attn_entmax_fwd(q, k, v, alpha, causal=w.causal, scale=w.scale, n_iter=16, out=out,
+                                    return_mask=True)
+    t0 = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t0 < settle_s or n_settle < 3:
+        run()
+        n_settle += 1
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_e = e0.elapsed_time(e1) / n
+    _, _, mask = run()
+    torch.cuda.synchronize()
+    visited = int(np.unpackbits(mask.cpu().numpy().view(np.uint8)).sum())
+    nq = (w.seqlen + 127) // 128
+    blocks = w.batch * w.hq * (nq * (nq + 1) // 2 if w.causal else nq * nq)
+    return {"alpha": alpha, "ms_per_call": round(ms_e, 5), "calls": n,
+            "time_vs_softmax_forward": round(ms_e / softmax_ms, 3),
+            "output_pass_block_fraction": round(visited / blocks, 4),
+            "kernel": "attn_entmax_kernel (max, histogram, refinement passes to convergence, sparse output pass)"}
+
+
 def time_backward(attn, torch, w, q, k, v, cu, sp, out, lse, flops, n, settle_s):
     """Average time of one attn_bwd call (its dQ and dK/dV kernels) over n
     back-to-back calls on the launch stream, after the forward filled out/lse.
@@ -168,6 +201,8 @@ def main():
                     help="sparse_osk workload: the ordered-skipping stop threshold tau")
     ap.add_argument("--osk-min-visit", type=int, default=2,
                     help="sparse_osk workload: entries visited before the stop test applies")
+    ap.add_argument("--no-entmax", action="store_true",
+                    help="skip the secondary timing of the alpha-entmax forward")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the secondary timing of the backward pass")
     ap.add_argument("--copy-probe", action="store_true",
@@ -345,6 +380,11 @@ def main():
                             args.settle_ms / 2e3)
         log(f"backward: {bwd}")
 
+    ent = None
+    if not args.no_entmax and not w.packed and not sp:
+        ent = time_entmax(attn, torch, w, q, k, v, ms_per_step, max(10, args.steps // 10), args.settle_ms / 2e3)
+        log(f"entmax: {ent}")
+
     cpu = None
     if not args.no_cpu_baseline and not w.packed and not sp:
         cpu = cpu_baseline(w)
@@ -374,6 +414,7 @@ def main():
                      "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "backward": bwd,
+        "entmax": ent,
     }
     print(json.dumps(rec), flush=True)
 
