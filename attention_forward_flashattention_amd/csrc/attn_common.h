@@ -134,6 +134,16 @@ __device__ __forceinline__ bf16x8_t tr_pair2(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(bf16x8_t, packed);
 }
 
+// One 16 B LDS read (an MFMA operand) at a per-lane address plus an immediate
+// offset.  Inline assembly for the same reason as tr_pair; the caller waits
+// for the result with lgkm_wait.
+template <int kOff>
+__device__ __forceinline__ bf16x8_t ld_b128(uint32_t addr) {
+  uint4_t x;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(x) : "v"(addr), "i"(kOff));
+  return __builtin_bit_cast(bf16x8_t, x);
+}
+
 // Wait until at most N LDS operations are outstanding; `x` is tied through so
 // its uses cannot move above the wait.
 template <int N>

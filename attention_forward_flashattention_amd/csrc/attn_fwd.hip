@@ -122,33 +122,54 @@ __device__ __forceinline__ void decode_tile(const Params &p, bool heavy_first, i
   tile = heavy_first ? p.n_tiles - 1 - rank : rank;
 }
 
-// Direct global -> LDS loads of one KV tile (K then V) into one LDS buffer.
-// Each wave-wide load writes 64 consecutive 16 B LDS slots; each lane fetches
-// the global chunk that the swizzled layout places in its slot.  The per-lane
-// part of the global offset (koff, voff: row lrow of the tile) is fixed for
-// the whole kernel; only the tile's start row changes.  In a tile that runs
-// past the end of the sequence the missing rows re-read the last row (finite
-// data; those keys are masked).
+// Direct global -> LDS loads of the rows of one K or V tile.  Each wave-wide
+// load writes 64 consecutive 16 B LDS slots; each lane fetches the global
+// chunk that the swizzled layout places in its slot.  The per-lane part of the
+// global offset (off: row lrow of the tile) is fixed for the whole kernel; only
+// the tile's start row changes.  In a tile that runs past the end of the
+// sequence the missing rows re-read the last row (finite data; those keys are
+// masked).
+template <class C>
+__device__ __forceinline__ void issue_rows(char *dst, const uint16_t *t0, const int64_t *off,
+                                           const int *lrow, int64_t ss, int rows_left) {
+  constexpr int kLoads = C::kLoads;
+  if (rows_left >= C::kBN) {
+#pragma unroll
+    for (int n = 0; n < kLoads; ++n)
+      __builtin_amdgcn_global_load_lds(t0 + off[n], (lds_void_t *)(dst + n * 1024), 16, 0, 0);
+  } else {
+#pragma unroll
+    for (int n = 0; n < kLoads; ++n) {
+      const int64_t back = min(rows_left - 1 - lrow[n], 0);  // rows to step back
+      __builtin_amdgcn_global_load_lds(t0 + off[n] + back * ss, (lds_void_t *)(dst + n * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// One KV tile (K then V) into one LDS buffer.
 template <class C>
 __device__ __forceinline__ void issue_tile(char *kb, char *vb, const uint16_t *kt0,
                                            const uint16_t *vt0, const int64_t *koff,
                                            const int64_t *voff, const int *lrow, int64_t k_ss,
                                            int64_t v_ss, int rows_left) {
-  constexpr int kLoads = C::kLoads;
-  if (rows_left >= C::kBN) {
-#pragma unroll
-    for (int n = 0; n < kLoads; ++n) {
-      __builtin_amdgcn_global_load_lds(kt0 + koff[n], (lds_void_t *)(kb + n * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vt0 + voff[n], (lds_void_t *)(vb + n * 1024), 16, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int n = 0; n < kLoads; ++n) {
-      const int64_t back = min(rows_left - 1 - lrow[n], 0);  // rows to step back
-      __builtin_amdgcn_global_load_lds(kt0 + koff[n] + back * k_ss, (lds_void_t *)(kb + n * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vt0 + voff[n] + back * v_ss, (lds_void_t *)(vb + n * 1024), 16, 0, 0);
-    }
-  }
+  issue_rows<C>(kb, kt0, koff, lrow, k_ss, rows_left);
+  issue_rows<C>(vb, vt0, voff, lrow, v_ss, rows_left);
+}
+
+// Operand steps of one MFMA phase of the pipelined dense loop: scores of one
+// tile and PV of the previous one interleaved (kBoth), or one of them alone.
+// Step t is a score MFMA (kind 0, one 16 B K read) or a PV MFMA (kind 1, two
+// transpose reads of V), with index x among the steps of its kind.
+enum { kBoth = 0, kOnlyS = 1, kOnlyPV = 2 };
+__host__ __device__ constexpr int step_kind(int w, int t) { return w == kBoth ? (t & 1) : (w == kOnlyS ? 0 : 1); }
+__host__ __device__ constexpr int step_idx(int w, int t) { return w == kBoth ? (t >> 1) : t; }
+__host__ __device__ constexpr int step_reads(int w, int t) { return step_kind(w, t) == 0 ? 1 : 2; }
+// LDS reads still allowed in flight when step i needs its operand: those of
+// the steps after it that a ring of r operands has already issued.
+__host__ __device__ constexpr int step_wait(int w, int n, int r, int i) {
+  int c = 0;
+  for (int t = i + 1; t < n && t < i + r; ++t) c += step_reads(w, t);
+  return c;
 }
 
 template <class C, bool CAUSAL, int MODE>
@@ -289,10 +310,17 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   const int qrow = q0 + wave * 32 + l32;  // this lane's query row (sequence position)
   const int wq_last = q0 + wave * 32 + 31;
 
+  // Dense problems with two waves per SIMD from one workgroup run the
+  // software-pipelined loop below; the other kernels the plain one.
+  constexpr bool kPipe = MODE == kDense && C::NW == 8;
   int kv_cur = n_iter > 0 ? kv_start(0) : -1;
-  if (kv_cur >= 0)
-    issue_tile<C>(smem + slot_byte0, smem + kTileBytes + slot_byte0, kg + (int64_t)kv_cur * p.k_ss,
-                       vg + (int64_t)kv_cur * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_cur);
+  if (kv_cur >= 0) {
+    if constexpr (kPipe)
+      issue_rows<C>(smem + slot_byte0, kg + (int64_t)kv_cur * p.k_ss, koff, lrow, p.k_ss, len - kv_cur);
+    else
+      issue_tile<C>(smem + slot_byte0, smem + kTileBytes + slot_byte0, kg + (int64_t)kv_cur * p.k_ss,
+                    vg + (int64_t)kv_cur * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_cur);
+  }
 
   // ---- Q rows of this wave straight into registers (MFMA B operand: lane
   // l32 holds head-dim values 16*dc + 8*hi .. +7 of its row); rows past the
@@ -315,12 +343,13 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   // offset.  The empty asm keeps each offset in one register (otherwise the
   // compiler re-splits it into row and chunk parts and re-adds them per read).
   int kaddr[kDc], vaddr[kDt];
-  uint32_t vlds[kDt];
+  uint32_t klds[kDc], vlds[kDt];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char_t *)smem;
 #pragma unroll
   for (int dc = 0; dc < kDc; ++dc) {
     kaddr[dc] = L::kq(l32, dc * 2 + hi);
     asm volatile("" : "+v"(kaddr[dc]));
+    klds[dc] = smem_lds + (uint32_t)kaddr[dc];
   }
 #pragma unroll
   for (int dt = 0; dt < kDt; ++dt) {
@@ -329,62 +358,16 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     vlds[dt] = smem_lds + (uint32_t)vaddr[dt];
   }
 
+  // ---- online softmax of one score tile whose first key is kv0 (base 2,
+  // scale folded into c): masks the causal diagonal and the sequence tail
+  // where the tile needs it, forms P in bf16 in the MFMA operand layout and
+  // adds the tile's row sums to l_run.  P is first computed against the
+  // running max as it stands; the tile's own max is taken only on the wave's
+  // first tile or when some row sum exceeds kFastSum (a score well above the
+  // running max).  Then the max is raised to the tile's, O and l are
+  // rescaled and P is computed again.
   bool first = true;  // no tile processed yet by this wave
-  // Returns true (ordered skipping only) when the walk stops before tile `it`.
-  auto step = [&](const int it, auto buf_tag) -> bool {
-    constexpr int kBuf = decltype(buf_tag)::value;  // LDS buffer of tile `it` (= it % 2)
-    // tile `it` has landed (every wave waited for its own loads); every wave is
-    // done reading the other buffer
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    // ordered skipping: at the start of a list entry, stop when every wave found
-    // all its rows' share of the previous entry at most tau of their mass
-    if (OSK && it > 0 && it % kSub == 0 && it / kSub >= p.osk_min_visit &&
-        (osk_flag[0] & osk_flag[1] & osk_flag[2] & osk_flag[3]))
-      return true;
-    int kv_nxt = -1;
-    if (it + 1 < n_iter) {
-      kv_nxt = kv_start(it + 1);
-      if (kv_nxt >= 0) {
-        char *buf = smem + (1 - kBuf) * kBufBytes;
-        issue_tile<C>(buf + slot_byte0, buf + kTileBytes + slot_byte0, kg + (int64_t)kv_nxt * p.k_ss,
-                           vg + (int64_t)kv_nxt * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_nxt);
-      }
-    }
-    const int kv0 = kv_cur;
-    kv_cur = kv_nxt;
-    if (kv0 < 0) return false;
-    if (CAUSAL && kv0 > wq_last) return false;  // whole tile above this wave's rows
-    const char *sK = smem + kBuf * kBufBytes;
-    const char *sV = sK + kTileBytes;
-
-    // ---- S^T = K Q^T : kKt tiles of 32 keys x 32 query rows
-    floatx16_t s[kKt];
-    {
-      // LDS operand reads run kRing MFMAs ahead of their use, and consecutive
-      // MFMAs alternate between the kKt independent accumulators, so neither
-      // the LDS latency nor the MFMA dependency latency is exposed
-      constexpr int kRing = 4;
-      constexpr int kSteps = kKt * kDc;  // step i: kt = i % kKt, dc = i / kKt
-      auto load = [&](int i) {
-        return *reinterpret_cast<const bf16x8_t *>(sK + kaddr[i / kKt] + (i % kKt) * 32 * L::kRowBytes);
-      };
-      bf16x8_t ring[kRing];
-#pragma unroll
-      for (int i = 0; i < kRing; ++i) ring[i] = load(i);
-#pragma unroll
-      for (int i = 0; i < kSteps; ++i) {
-        const int kt = i % kKt, dc = i / kKt;
-        if (dc == 0)
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], floatx16_t{}, 0, 0, 0);
-        else
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], s[kt], 0, 0, 0);
-        if (i + kRing < kSteps) ring[i % kRing] = load(i + kRing);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-
-    // ---- mask (causal diagonal and sequence tail only)
+  auto softmax = [&](floatx16_t (&s)[kKt], const int kv0, bf16x8_t (&pb)[kKt][2]) __attribute__((always_inline)) {
     const bool need_mask = (kv0 + kBN > len) || (CAUSAL && kv0 + kBN - 1 > q0 + wave * 32);
     if (need_mask) {
 #pragma unroll
@@ -396,13 +379,6 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
           if (bad) s[kt][i] = -INFINITY;
         }
     }
-
-    // ---- online softmax (base 2, scale folded into c).  P is first computed
-    // against the running max as it stands; the tile's own max is taken only
-    // on the wave's first tile or when some row sum exceeds kFastSum (a score
-    // well above the running max).  Then the max is raised to the tile's,
-    // O and l are rescaled and P is computed again.
-    bf16x8_t pb[kKt][2];
     float rs = 0.f;
     bool slow = first;
     if (!first) {
@@ -431,64 +407,233 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     }
     l_run += rs;
     if (OSK) d_run += rs;
+  };
 
-    // ---- O^T += V^T P^T.  MFMA k index (8 per lane half) maps to keys
-    // 16c + 8(e/4) + 4*hi + (e%4) of a 32-key tile, matching where the score
-    // layout left P; V^T operands are read with the LDS transpose.
-    {
-      // same operand ring as for S; consecutive MFMAs alternate between the
-      // kDt output accumulators
+  int n_done = n_iter;  // tiles walked (ordered skipping may stop early)
+  if constexpr (kPipe) {
+    // ---- software-pipelined dense loop.  Iteration j (one barrier each,
+    // j = 0 .. n_iter) issues the loads of K(j+1) and V(j), and each wave
+    // runs one MFMA phase with the scores S(j) = K(j) Q^T interleaved with
+    // the PV product of the tile before, O^T += V(j-1)^T P(j-1)^T, and the
+    // online softmax of one tile.  K buffer j % 2 holds K(j), V buffer j % 2
+    // holds V(j); a buffer is rewritten one barrier after its last read.
+    // The two waves that share a SIMD (wave w and w + 4) run the iteration
+    // rotated against each other: the first does [MFMA phase][softmax of
+    // S(j)], the second [softmax of S(j-1)][MFMA phase], so that while one
+    // wave works through the exp2 and VALU work of the softmax the other one
+    // keeps the matrix core busy.
+    const bool lagged = ((wave >> 2) & 1) != 0;
+    // tiles this wave needs (under causal masking, those not wholly above its rows)
+    const int n_own = CAUSAL ? min(n_iter, wq_last / kBN + 1) : n_iter;
+    floatx16_t s[kKt];
+    bf16x8_t pb[kKt][2];
+    auto sync = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    };
+    auto issue = [&](const int j) __attribute__((always_inline)) {
+      if (j + 1 < n_iter) {
+        const int kv = (j + 1) * kBN;
+        issue_rows<C>(smem + ((j + 1) & 1) * kBufBytes + slot_byte0, kg + (int64_t)kv * p.k_ss, koff,
+                      lrow, p.k_ss, len - kv);
+      }
+      if (j < n_iter) {
+        const int kv = j * kBN;
+        issue_rows<C>(smem + (j & 1) * kBufBytes + kTileBytes + slot_byte0, vg + (int64_t)kv * p.v_ss,
+                      voff, lrow, p.v_ss, len - kv);
+      }
+    };
+    // One MFMA phase: K from buffer kKb, V from buffer kVb.  Operand reads run
+    // kRing steps ahead of their MFMA; consecutive MFMAs alternate between
+    // independent accumulators.
+    auto phase = [&](auto kb_tag, auto vb_tag, auto what_tag) __attribute__((always_inline)) {
+      constexpr int kKb = decltype(kb_tag)::value;
+      constexpr int kVb = decltype(vb_tag)::value;
+      constexpr int kW = decltype(what_tag)::value;
+      constexpr int kNs = kKt * kDc, kNp = kDt * kKt * 2;
+      static_assert(kW != kBoth || kNs == kNp, "score and PV steps must pair up");
+      constexpr int kN = kW == kBoth ? kNs + kNp : (kW == kOnlyS ? kNs : kNp);
       constexpr int kRing = 4;
-      constexpr int kSteps = kDt * kKt * 2;  // step i: dt = i % kDt, (kt, c) = i / kDt
-      constexpr int kVOff = kBuf * kBufBytes + kTileBytes;  // V tile of this buffer
+      auto load = [&](auto T) __attribute__((always_inline)) -> bf16x8_t {
+        constexpr int t = decltype(T)::value;
+        constexpr int x = step_idx(kW, t);
+        if constexpr (step_kind(kW, t) == 0)
+          return ld_b128<kKb * kBufBytes + (x % kKt) * 32 * L::kRowBytes>(klds[x / kKt]);
+        else
+          return tr_pair<kVb * kBufBytes + kTileBytes + tr_off<L, kDt>(x), 8 * L::kRowBytes>(vlds[x % kDt]);
+      };
       bf16x8_t ring[kRing];
-      static_for<kRing>([&](auto I) {
-        constexpr int i = decltype(I)::value;
-        ring[i] = tr_pair<kVOff + tr_off<L, kDt>(i), 8 * L::kRowBytes>(vlds[i % kDt]);
+      static_for<kRing>([&](auto T) {
+        constexpr int t = decltype(T)::value;
+        if constexpr (t < kN) ring[t] = load(T);
       });
-      static_for<kSteps>([&](auto I) {
+      static_for<kN>([&](auto I) {
         constexpr int i = decltype(I)::value;
-        constexpr int dt = i % kDt, kc = i / kDt, kt = kc >> 1, c = kc & 1;
-        // the reads of step i are done once at most the reads issued after
-        // them are outstanding (LDS reads complete in order)
-        lgkm_wait<2 * (kSteps - 1 - i < kRing - 1 ? kSteps - 1 - i : kRing - 1)>(ring[i % kRing]);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], pb[kt][c], oacc[dt], 0, 0, 0);
-        if constexpr (i + kRing < kSteps)
-          ring[i % kRing] = tr_pair<kVOff + tr_off<L, kDt>(i + kRing), 8 * L::kRowBytes>(vlds[(i + kRing) % kDt]);
+        constexpr int x = step_idx(kW, i);
+        lgkm_wait<step_wait(kW, kN, kRing, i)>(ring[i % kRing]);
+        if constexpr (step_kind(kW, i) == 0) {
+          constexpr int kt = x % kKt, dc = x / kKt;
+          if constexpr (dc == 0)
+            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], floatx16_t{}, 0, 0, 0);
+          else
+            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], s[kt], 0, 0, 0);
+        } else {
+          constexpr int dt = x % kDt, kc = x / kDt;
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], pb[kc >> 1][kc & 1], oacc[dt], 0, 0, 0);
+        }
+        if constexpr (i + kRing < kN) ring[i % kRing] = load(std::integral_constant<int, i + kRing>{});
         __builtin_amdgcn_sched_barrier(0);
       });
+    };
+    // iteration 0: scores of tile 0
+    sync();
+    issue(0);
+    phase(BufTag<0>{}, BufTag<0>{}, std::integral_constant<int, kOnlyS>{});
+    if (!lagged) softmax(s, 0, pb);
+    // iterations 1 .. n_own - 1, two per trip so that the buffers of each
+    // are compile-time constants
+    int j = 1;
+    auto body = [&](auto kb_tag) __attribute__((always_inline)) {
+      constexpr int kKb = decltype(kb_tag)::value;  // = j % 2
+      sync();
+      issue(j);
+      if (lagged) softmax(s, (j - 1) * kBN, pb);
+      phase(kb_tag, BufTag<1 - kKb>{}, std::integral_constant<int, kBoth>{});
+      if (!lagged) softmax(s, j * kBN, pb);
+      ++j;
+    };
+    while (j + 1 < n_own) {
+      body(BufTag<1>{});
+      body(BufTag<0>{});
     }
-    return false;
-  };
-  // ordered skipping: after the last tile of a list entry, each wave records
-  // whether all its rows passed the test -- the entries still to come, if
-  // each adds at most what this one added, would add at most tau of the
-  // row's mass -- and starts the next entry's share
-  auto osk_mark = [&](const int it) {
-    if (!OSK || it % kSub != kSub - 1) return;
-    const float share = half_sum(d_run);
-    const float mass = half_sum(l_run);
-    const float left = (float)(n_iter / kSub - (it / kSub + 1));  // entries not yet visited
-    const bool fail = __builtin_amdgcn_ballot_w64(left * share > p.osk_tau * mass) != 0;
-    if (lane == 0) osk_flag[wave] = fail ? 0u : 1u;
-    d_run = 0.f;
-  };
-  int n_done = n_iter;  // tiles walked (ordered skipping may stop early)
-  // two tiles per trip so that each step's LDS buffer is a compile-time constant
-  // (every LDS operand address is then a loop-invariant lane offset plus an
-  // immediate)
-  for (int it = 0; it < n_iter; it += 2) {
-    if (step(it, BufTag<0>{})) {
-      n_done = it;
-      break;
+    if (j < n_own) body(BufTag<1>{});
+    // iteration n_own: PV of the wave's last tile
+    sync();
+    issue(n_own);
+    if (lagged) softmax(s, (n_own - 1) * kBN, pb);
+    if ((n_own - 1) & 1)
+      phase(BufTag<0>{}, BufTag<1>{}, std::integral_constant<int, kOnlyPV>{});
+    else
+      phase(BufTag<0>{}, BufTag<0>{}, std::integral_constant<int, kOnlyPV>{});
+    // the other waves' remaining iterations: barriers and loads only
+    for (int jj = n_own + 1; jj <= n_iter; ++jj) {
+      sync();
+      issue(jj);
     }
-    osk_mark(it);
-    if (it + 1 < n_iter) {
-      if (step(it + 1, BufTag<1>{})) {
-        n_done = it + 1;
+  } else {
+    // Returns true (ordered skipping only) when the walk stops before tile `it`.
+    auto step = [&](const int it, auto buf_tag) -> bool {
+      constexpr int kBuf = decltype(buf_tag)::value;  // LDS buffer of tile `it` (= it % 2)
+      // tile `it` has landed (every wave waited for its own loads); every wave is
+      // done reading the other buffer
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      // ordered skipping: at the start of a list entry, stop when every wave found
+      // all its rows' share of the previous entry at most tau of their mass
+      if (OSK && it > 0 && it % kSub == 0 && it / kSub >= p.osk_min_visit &&
+          (osk_flag[0] & osk_flag[1] & osk_flag[2] & osk_flag[3]))
+        return true;
+      int kv_nxt = -1;
+      if (it + 1 < n_iter) {
+        kv_nxt = kv_start(it + 1);
+        if (kv_nxt >= 0) {
+          char *buf = smem + (1 - kBuf) * kBufBytes;
+          issue_tile<C>(buf + slot_byte0, buf + kTileBytes + slot_byte0, kg + (int64_t)kv_nxt * p.k_ss,
+                        vg + (int64_t)kv_nxt * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_nxt);
+        }
+      }
+      const int kv0 = kv_cur;
+      kv_cur = kv_nxt;
+      if (kv0 < 0) return false;
+      if (CAUSAL && kv0 > wq_last) return false;  // whole tile above this wave's rows
+      const char *sK = smem + kBuf * kBufBytes;
+
+      // ---- S^T = K Q^T : kKt tiles of 32 keys x 32 query rows
+      floatx16_t s[kKt];
+      {
+        // LDS operand reads run kRing MFMAs ahead of their use, and consecutive
+        // MFMAs alternate between the kKt independent accumulators, so neither
+        // the LDS latency nor the MFMA dependency latency is exposed
+        constexpr int kRing = 4;
+        constexpr int kSteps = kKt * kDc;  // step i: kt = i % kKt, dc = i / kKt
+        auto load = [&](int i) {
+          return *reinterpret_cast<const bf16x8_t *>(sK + kaddr[i / kKt] + (i % kKt) * 32 * L::kRowBytes);
+        };
+        bf16x8_t ring[kRing];
+#pragma unroll
+        for (int i = 0; i < kRing; ++i) ring[i] = load(i);
+#pragma unroll
+        for (int i = 0; i < kSteps; ++i) {
+          const int kt = i % kKt, dc = i / kKt;
+          if (dc == 0)
+            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], floatx16_t{}, 0, 0, 0);
+          else
+            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], s[kt], 0, 0, 0);
+          if (i + kRing < kSteps) ring[i % kRing] = load(i + kRing);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      bf16x8_t pb[kKt][2];
+      softmax(s, kv0, pb);
+
+      // ---- O^T += V^T P^T.  MFMA k index (8 per lane half) maps to keys
+      // 16c + 8(e/4) + 4*hi + (e%4) of a 32-key tile, matching where the score
+      // layout left P; V^T operands are read with the LDS transpose.
+      {
+        // same operand ring as for S; consecutive MFMAs alternate between the
+        // kDt output accumulators
+        constexpr int kRing = 4;
+        constexpr int kSteps = kDt * kKt * 2;  // step i: dt = i % kDt, (kt, c) = i / kDt
+        constexpr int kVOff = kBuf * kBufBytes + kTileBytes;  // V tile of this buffer
+        bf16x8_t ring[kRing];
+        static_for<kRing>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          ring[i] = tr_pair<kVOff + tr_off<L, kDt>(i), 8 * L::kRowBytes>(vlds[i % kDt]);
+        });
+        static_for<kSteps>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          constexpr int dt = i % kDt, kc = i / kDt, kt = kc >> 1, c = kc & 1;
+          // the reads of step i are done once at most the reads issued after
+          // them are outstanding (LDS reads complete in order)
+          lgkm_wait<2 * (kSteps - 1 - i < kRing - 1 ? kSteps - 1 - i : kRing - 1)>(ring[i % kRing]);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], pb[kt][c], oacc[dt], 0, 0, 0);
+          if constexpr (i + kRing < kSteps)
+            ring[i % kRing] = tr_pair<kVOff + tr_off<L, kDt>(i + kRing), 8 * L::kRowBytes>(vlds[(i + kRing) % kDt]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+      return false;
+    };
+    // ordered skipping: after the last tile of a list entry, each wave records
+    // whether all its rows passed the test -- the entries still to come, if
+    // each adds at most what this one added, would add at most tau of the
+    // row's mass -- and starts the next entry's share
+    auto osk_mark = [&](const int it) {
+      if (!OSK || it % kSub != kSub - 1) return;
+      const float share = half_sum(d_run);
+      const float mass = half_sum(l_run);
+      const float left = (float)(n_iter / kSub - (it / kSub + 1));  // entries not yet visited
+      const bool fail = __builtin_amdgcn_ballot_w64(left * share > p.osk_tau * mass) != 0;
+      if (lane == 0) osk_flag[wave] = fail ? 0u : 1u;
+      d_run = 0.f;
+    };
+    // two tiles per trip so that each step's LDS buffer is a compile-time constant
+    // (every LDS operand address is then a loop-invariant lane offset plus an
+    // immediate)
+    for (int it = 0; it < n_iter; it += 2) {
+      if (step(it, BufTag<0>{})) {
+        n_done = it;
         break;
       }
-      osk_mark(it + 1);
+      osk_mark(it);
+      if (it + 1 < n_iter) {
+        if (step(it + 1, BufTag<1>{})) {
+          n_done = it + 1;
+          break;
+        }
+        osk_mark(it + 1);
+      }
     }
   }
   if (OSK && p.visited && tid == 0) p.visited[(int64_t)h * p.n_tiles + tile] = n_done / kSub;
