@@ -1,9 +1,10 @@
 // attn_fwd.hip — fused softmax-attention forward for AMD Instinct MI355X (gfx950).
 //
 // One workgroup computes a tile of query rows of one (sequence, query head):
-// 256 rows in eight wave64s for dense and packed problems, 128 rows in four
-// wave64s for the block-list kernel (one query block of the list).  Each wave
-// owns 32 rows and keeps them in registers for the whole kernel.  KV tiles of
+// for dense and packed problems 256 rows in eight wave64s (head_dim 128), 384
+// rows in twelve (head_dim 64) or 128 rows in four (head_dim 256); 128 rows in
+// four wave64s for the block-list kernel (one query block of the list).  Each
+// wave owns 32 rows and keeps them in registers for the whole kernel.  KV tiles of
 // BN keys (64; 32 at head_dim 256) are streamed into double-buffered LDS with
 // direct global-to-LDS loads; for each tile a wave computes the transposed
 // score tile S^T = K Q^T with 32x32x16 bf16 MFMAs, so that every lane holds
@@ -63,10 +64,13 @@ struct Params {
 
 // Kernel configuration.  NW wave64s per workgroup, each owning 32 query rows
 // (BM = 32 * NW rows per workgroup); BN keys per KV tile (64, or 32 at head_dim
-// 256 to bound registers and LDS).  Dense and packed problems use 8 waves
-// (256-row tiles: every K/V tile staged in LDS serves 256 query rows); the
-// block-list kernel uses 4 waves so a workgroup covers exactly one 128-row
-// query block of the list.
+// 256 to bound registers and LDS).  Dense and packed problems use 8 waves at
+// head_dim 128 (two per SIMD, 256-row tiles: every K/V tile staged in LDS
+// serves 256 query rows) and 12 at head_dim 64 (three per SIMD: the
+// pipelined loop needs under 168 VGPRs there, so a third wave fits and hides
+// more of each wave's serial barrier and load-issue time); the block-list
+// kernel uses 4 waves so a workgroup covers exactly one 128-row query block
+// of the list.
 template <int D_, int NW_>
 struct Config {
   static constexpr int D = D_;
@@ -75,8 +79,11 @@ struct Config {
   static constexpr int kBM = 32 * NW;
   static constexpr int kBN = D == 256 ? 32 : 64;
   static constexpr int kTileBytes = kBN * D * 2;
-  static constexpr int kLoads = kTileBytes / 1024 / NW;  // wave-wide 16 B loads per wave per tile
-  static_assert(kLoads * 1024 * NW == kTileBytes, "tile must split evenly over waves");
+  // waves that load K/V tiles (the first kLoadWaves) and their wave-wide 16 B
+  // loads per tile each
+  static constexpr int kLoadWaves = NW < 8 ? NW : 8;
+  static constexpr int kLoads = kTileBytes / 1024 / kLoadWaves;
+  static_assert(kLoads * 1024 * kLoadWaves == kTileBytes, "tile must split evenly over the loading waves");
   static constexpr int kMinBlocks = (NW == 4 && D <= 128) ? 2 : 1;  // 2 waves per SIMD
 };
 
@@ -285,10 +292,13 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   constexpr int kLoads = C::kLoads;
   int64_t koff[kLoads], voff[kLoads];
   int lrow[kLoads];
-  const int slot_byte0 = wave * kLoads * 1024;  // this wave's first LDS slot in a tile
+  // waves past the loading ones issue no loads (their offsets are unused)
+  const bool loader = C::NW <= C::kLoadWaves || wave < C::kLoadWaves;
+  const int lwave = wave % C::kLoadWaves;
+  const int slot_byte0 = lwave * kLoads * 1024;  // this wave's first LDS slot in a tile
 #pragma unroll
   for (int n = 0; n < kLoads; ++n) {
-    const int slot = (wave * kLoads + n) * 64 + lane;
+    const int slot = (lwave * kLoads + n) * 64 + lane;
     const int r = slot / L::kChunks, pc = slot % L::kChunks;
     lrow[n] = r;
     koff[n] = (int64_t)r * p.k_ss + (pc ^ L::kswz(r)) * 8;
@@ -312,9 +322,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
 
   // Dense problems with two waves per SIMD from one workgroup run the
   // software-pipelined loop below; the other kernels the plain one.
-  constexpr bool kPipe = MODE == kDense && C::NW == 8;
+  constexpr bool kPipe = MODE == kDense && C::NW >= 8;
   int kv_cur = n_iter > 0 ? kv_start(0) : -1;
-  if (kv_cur >= 0) {
+  if (kv_cur >= 0 && loader) {
     if constexpr (kPipe)
       issue_rows<C>(smem + slot_byte0, kg + (int64_t)kv_cur * p.k_ss, koff, lrow, p.k_ss, len - kv_cur);
     else
@@ -370,14 +380,13 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   auto softmax = [&](floatx16_t (&s)[kKt], const int kv0, bf16x8_t (&pb)[kKt][2]) __attribute__((always_inline)) {
     const bool need_mask = (kv0 + kBN > len) || (CAUSAL && kv0 + kBN - 1 > q0 + wave * 32);
     if (need_mask) {
+      // key kv0 + hi*4 + o (o a compile-time offset) is masked when o > lim
+      const int lim = (CAUSAL ? min(qrow, len - 1) : len - 1) - kv0 - hi * 4;
 #pragma unroll
       for (int kt = 0; kt < kKt; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kv0 + kt * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-          const bool bad = key >= len || (CAUSAL && key > qrow);
-          if (bad) s[kt][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (kt * 32 + (i >> 2) * 8 + (i & 3) > lim) s[kt][i] = -INFINITY;
     }
     float rs = 0.f;
     bool slow = first;
@@ -417,11 +426,11 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     // the PV product of the tile before, O^T += V(j-1)^T P(j-1)^T, and the
     // online softmax of one tile.  K buffer j % 2 holds K(j), V buffer j % 2
     // holds V(j); a buffer is rewritten one barrier after its last read.
-    // The two waves that share a SIMD (wave w and w + 4) run the iteration
-    // rotated against each other: the first does [MFMA phase][softmax of
-    // S(j)], the second [softmax of S(j-1)][MFMA phase], so that while one
-    // wave works through the exp2 and VALU work of the softmax the other one
-    // keeps the matrix core busy.
+    // Waves w, w + 4 (and w + 8) share a SIMD; waves 4-7 run the iteration
+    // rotated against the others: waves 0-3 (and 8-11) do [MFMA phase]
+    // [softmax of S(j)], waves 4-7 [softmax of S(j-1)][MFMA phase], so that
+    // while one wave works through the exp2 and VALU work of the softmax
+    // another keeps the matrix core busy.
     const bool lagged = ((wave >> 2) & 1) != 0;
     // tiles this wave needs (under causal masking, those not wholly above its rows)
     const int n_own = CAUSAL ? min(n_iter, wq_last / kBN + 1) : n_iter;
@@ -432,6 +441,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       __syncthreads();
     };
     auto issue = [&](const int j) __attribute__((always_inline)) {
+      if (!loader) return;
       if (j + 1 < n_iter) {
         const int kv = (j + 1) * kBN;
         issue_rows<C>(smem + ((j + 1) & 1) * kBufBytes + slot_byte0, kg + (int64_t)kv * p.k_ss, koff,
@@ -762,7 +772,7 @@ int launch(Params p, hipStream_t stream) {
 
 template <int D>
 int launch_d(const Params &p, bool causal, int mode, hipStream_t s) {
-  using Dense = Config<D, D == 256 ? 4 : 8>;
+  using Dense = Config<D, D == 64 ? 12 : (D == 128 ? 8 : 4)>;
   using Listed = Config<D, 4>;
   if (mode == kList)
     return causal ? launch<Listed, true, kList>(p, s) : launch<Listed, false, kList>(p, s);
