@@ -616,97 +616,127 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
     const int q0 = q_cur;
     q_cur = q_nxt;
     const int boff = buf * kBufBytes;
-#pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
-      const int qh0 = q0 + 32 * half;
-      const int hoff = boff + half * 32 * kRowBytes;  // row 0 of this half in the Q tile
-      const char *sQ = smem + hoff;
-      // lse2 and D of this lane's 16 rows (register i: row 8 (i/4) + 4 hi + i%4)
-      const float *sL = reinterpret_cast<const float *>(smem + boff + 2 * kTileBytes) + 32 * half;
-      float4 l4[4], d4[4];
+    // The tile's two halves of 32 query rows are software-pipelined so that
+    // the exp2 / dS VALU work of one half runs between the MFMAs of the other
+    // (one wave per SIMD: nothing else would fill the matrix core meanwhile):
+    //   S, dP of half 0 | S, dP of half 1 + VALU of half 0 |
+    //   dV, dK of half 0 + VALU of half 1 | dV, dK of half 1.
+    floatx16_t s[2], dp[2];
+    bf16x8_t pb[2][2], dsb[2][2];
+    float4 l4[4], d4[4];
+    // lse2 and D of this lane's 16 rows of half h (register i: row 8 (i/4) +
+    // 4 hi + i%4), waited for at once (the phases' own LDS reads are counted
+    // by explicit waits)
+    auto load_ld = [&](const int h) __attribute__((always_inline)) {
+      const float *sL = reinterpret_cast<const float *>(smem + boff + 2 * kTileBytes) + 32 * h;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         l4[g4] = *reinterpret_cast<const float4 *>(sL + 8 * g4 + 4 * hi);
         d4[g4] = *reinterpret_cast<const float4 *>(sL + kBQ + 8 * g4 + 4 * hi);
       }
-      // ---- S = Q K^T and dP = dO V^T (32 query rows x 32 keys; lane = key).
-      // Operand reads run kRing MFMAs ahead; S and dP alternate.
-      floatx16_t s, dp;
-      {
-        constexpr int kRing = 4;
-        constexpr int kSteps = 2 * kDc;  // step i: dc = i / 2, Q (even) or dO (odd)
-        auto load = [&](int i) {
-          return *reinterpret_cast<const bf16x8_t *>(sQ + raddr[i >> 1] + (i & 1) * kTileBytes);
-        };
-        bf16x8_t ring[kRing];
-#pragma unroll
-        for (int i = 0; i < kRing; ++i) ring[i] = load(i);
-#pragma unroll
-        for (int i = 0; i < kSteps; ++i) {
-          const int dc = i >> 1;
-          if (i & 1)
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], vreg[dc], dc == 0 ? floatx16_t{} : dp, 0, 0, 0);
-          else
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], kreg[dc], dc == 0 ? floatx16_t{} : s, 0, 0, 0);
-          if (i + kRing < kSteps) ring[i % kRing] = load(i + kRing);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      // ---- P = 2^(c s - lse2), dS = P (dP - D); rows past the end and keys
-      // after their query (causal) get P = 0
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    };
+    // VALU of element i (of 16) of half h: P = 2^(c s - lse2), dS = P (dP - D);
+    // rows past the end and keys after their query (causal) get P = 0
+    auto valu = [&](auto H, auto I) __attribute__((always_inline)) {
+      constexpr int h = decltype(H)::value, i = decltype(I)::value;
+      constexpr int g4 = i / 4, e = i % 4;
+      const float lv = e == 0 ? l4[g4].x : e == 1 ? l4[g4].y : e == 2 ? l4[g4].z : l4[g4].w;
+      const float dv4 = e == 0 ? d4[g4].x : e == 1 ? d4[g4].y : e == 2 ? d4[g4].z : d4[g4].w;
+      const int qh0 = q0 + 32 * h;
       const bool need_mask = (qh0 + 32 > len) || (CAUSAL && qh0 < kw0 + 31);
-      bf16x8_t pb[2], dsb[2];
+      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][i], p.c, -lv));
+      const int qr = qh0 + 8 * g4 + 4 * hi + e;
+      if (need_mask && (qr >= len || (CAUSAL && key > qr))) pv = 0.f;
+      pb[h][i >> 3][i & 7] = (__bf16)pv;
+      dsb[h][i >> 3][i & 7] = (__bf16)(pv * (dp[h][i] - dv4));
+    };
+    // S = Q K^T and dP = dO V^T of half h (32 query rows x 32 keys; lane =
+    // key), operand reads kRing MFMAs ahead, S and dP alternating; the VALU
+    // of half hv (if hv >= 0) spread over the steps
+    auto sdp = [&](auto H, auto HV) __attribute__((always_inline)) {
+      constexpr int h = decltype(H)::value, hv = decltype(HV)::value;
+      const char *sQ = smem + boff + h * 32 * kRowBytes;
+      constexpr int kRing = 4;
+      constexpr int kSteps = 2 * kDc;  // step i: dc = i / 2, Q (even) or dO (odd)
+      constexpr int kPer = 16 / kSteps;  // VALU elements per step
+      auto load = [&](int i) {
+        return *reinterpret_cast<const bf16x8_t *>(sQ + raddr[i >> 1] + (i & 1) * kTileBytes);
+      };
+      bf16x8_t ring[kRing];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float lv[4] = {l4[g4].x, l4[g4].y, l4[g4].z, l4[g4].w};
-        const float dv4[4] = {d4[g4].x, d4[g4].y, d4[g4].z, d4[g4].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g4 + e;
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -lv[e]));
-          const int qr = qh0 + 8 * g4 + 4 * hi + e;
-          if (need_mask && (qr >= len || (CAUSAL && key > qr))) pv = 0.f;
-          pb[i >> 3][i & 7] = (__bf16)pv;
-          dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dv4[e]));
-        }
-      }
-      // ---- dV += P^T dO and dK += dS^T Q.  B operands by transpose reads of
-      // rows 16 c + 8 (e/4) + 4 hi + e%4 of the half (the k order of P); the
-      // reads run kRing MFMAs ahead
-      {
-        uint32_t ha[kDt], hb[kDt];
-#pragma unroll
-        for (int dt = 0; dt < kDt; ++dt) {
-          ha[dt] = ta[dt] + hoff;
-          hb[dt] = tb[dt] + hoff;
-        }
-        constexpr int kRing = 4;
-        constexpr int kSteps = kDt * 2 * 2;  // step i: dO (even) or Q (odd); (dt, c) = i / 2
-        bf16x8_t ring[kRing];
-        static_for<kRing>([&](auto I) {
-          constexpr int i = decltype(I)::value;
-          constexpr int dt = (i >> 1) % kDt, c = (i >> 1) / kDt;
-          constexpr int off = c * 16 * kRowBytes + ((i & 1) ? 0 : kTileBytes);
-          ring[i] = tr_pair2<off>(ha[dt], hb[dt]);
-        });
-        static_for<kSteps>([&](auto I) {
-          constexpr int i = decltype(I)::value;
-          constexpr int dt = (i >> 1) % kDt, c = (i >> 1) / kDt;
-          lgkm_wait<2 * (kSteps - 1 - i < kRing - 1 ? kSteps - 1 - i : kRing - 1)>(ring[i % kRing]);
-          if constexpr (i & 1)
-            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsb[c], ring[i % kRing], dk[dt], 0, 0, 0);
+      for (int i = 0; i < kRing; ++i) ring[i] = load(i);
+      static_for<kSteps>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int dc = i >> 1;
+        if constexpr (i & 1) {
+          if constexpr (dc == 0)
+            dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], vreg[dc], floatx16_t{}, 0, 0, 0);
           else
-            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[c], ring[i % kRing], dv[dt], 0, 0, 0);
-          if constexpr (i + kRing < kSteps) {
-            constexpr int j = i + kRing;
-            constexpr int dtj = (j >> 1) % kDt, cj = (j >> 1) / kDt;
-            constexpr int offj = cj * 16 * kRowBytes + ((j & 1) ? 0 : kTileBytes);
-            ring[i % kRing] = tr_pair2<offj>(ha[dtj], hb[dtj]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        });
+            dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], vreg[dc], dp[h], 0, 0, 0);
+        } else {
+          if constexpr (dc == 0)
+            s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], kreg[dc], floatx16_t{}, 0, 0, 0);
+          else
+            s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], kreg[dc], s[h], 0, 0, 0);
+        }
+        if constexpr (i + kRing < kSteps) ring[i % kRing] = load(i + kRing);
+        if constexpr (hv >= 0)
+          static_for<kPer>([&](auto E) { valu(HV, std::integral_constant<int, i * kPer + decltype(E)::value>{}); });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    // dV += P^T dO and dK += dS^T Q of half h.  B operands by transpose reads
+    // of rows 16 c + 8 (e/4) + 4 hi + e%4 of the half (the k order of P); the
+    // reads run kRing MFMAs ahead; the VALU of half hv (if hv >= 0) spread
+    // over the steps
+    auto dvdk = [&](auto H, auto HV) __attribute__((always_inline)) {
+      constexpr int h = decltype(H)::value, hv = decltype(HV)::value;
+      const int hoff = boff + h * 32 * kRowBytes;  // row 0 of this half in the Q tile
+      uint32_t ha[kDt], hb[kDt];
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) {
+        ha[dt] = ta[dt] + hoff;
+        hb[dt] = tb[dt] + hoff;
       }
-    }
+      constexpr int kRing = 4;
+      constexpr int kSteps = kDt * 2 * 2;  // step i: dO (even) or Q (odd); (dt, c) = i / 2
+      constexpr int kPer = 16 / kSteps;
+      bf16x8_t ring[kRing];
+      static_for<kRing>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int dt = (i >> 1) % kDt, c = (i >> 1) / kDt;
+        constexpr int off = c * 16 * kRowBytes + ((i & 1) ? 0 : kTileBytes);
+        ring[i] = tr_pair2<off>(ha[dt], hb[dt]);
+      });
+      static_for<kSteps>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int dt = (i >> 1) % kDt, c = (i >> 1) / kDt;
+        lgkm_wait<2 * (kSteps - 1 - i < kRing - 1 ? kSteps - 1 - i : kRing - 1)>(ring[i % kRing]);
+        if constexpr (i & 1)
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsb[h][c], ring[i % kRing], dk[dt], 0, 0, 0);
+        else
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[h][c], ring[i % kRing], dv[dt], 0, 0, 0);
+        if constexpr (i + kRing < kSteps) {
+          constexpr int j = i + kRing;
+          constexpr int dtj = (j >> 1) % kDt, cj = (j >> 1) / kDt;
+          constexpr int offj = cj * 16 * kRowBytes + ((j & 1) ? 0 : kTileBytes);
+          ring[i % kRing] = tr_pair2<offj>(ha[dtj], hb[dtj]);
+        }
+        if constexpr (hv >= 0)
+          static_for<kPer>([&](auto E) { valu(HV, std::integral_constant<int, i * kPer + decltype(E)::value>{}); });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using CN = std::integral_constant<int, -1>;
+    sdp(C0{}, CN{});
+    load_ld(0);
+    sdp(C1{}, C0{});
+    load_ld(1);
+    dvdk(C0{}, C1{});
+    dvdk(C1{}, CN{});
   };
   for (int it = 0; it < n_iter; ++it) step(it, it & 1);
 
