@@ -58,9 +58,21 @@ struct EntParams {
   float scale, alpha;
 };
 
+// The weights' exponent e = 1/(alpha-1): alpha = 2 (sparsemax) gives e = 1
+// and alpha = 1.5 gives e = 2, where u^e and the power sums of the solver
+// need no transcendental; every other alpha goes through exp2/log2.
+enum { kPowGeneral = 0, kPowLinear = 1, kPowSquare = 2 };
+
 // u^e for u > 0 (0 otherwise)
+template <int PK>
 __device__ __forceinline__ float powpos(float u, float e) {
-  return u > 0.f ? __builtin_amdgcn_exp2f(e * __builtin_amdgcn_logf(u)) : 0.f;
+  if (!(u > 0.f)) return 0.f;
+  if constexpr (PK == kPowLinear)
+    return u;
+  else if constexpr (PK == kPowSquare)
+    return u * u;
+  else
+    return __builtin_amdgcn_exp2f(e * __builtin_amdgcn_logf(u));
 }
 
 template <int kLoads>
@@ -73,7 +85,7 @@ __device__ __forceinline__ void issue_rows(char *l, const uint16_t *g, const int
   }
 }
 
-template <int D>
+template <int D, int PK>
 __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   using L = Lds<D>;
   constexpr int kNW = 4;
@@ -161,14 +173,24 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   // 4 hi + i%4 for this lane's row; keys past kv_end, after the row (causal)
   // or rows past the end get -inf
   auto scores = [&](const char *sK, int kv0, floatx16_t (&s)[kKt]) {
+    {
+      // operand reads run kRing MFMAs ahead; consecutive MFMAs alternate
+      // between the kKt accumulators (step i: kt = i % kKt, dc = i / kKt)
+      constexpr int kRing = 4;
+      constexpr int kSteps = kKt * kDc;
+      auto load = [&](int i) {
+        return *reinterpret_cast<const bf16x8_t *>(sK + kaddr[i / kKt] + (i % kKt) * 32 * kRowBytes);
+      };
+      bf16x8_t ring[kRing];
 #pragma unroll
-    for (int kt = 0; kt < kKt; ++kt) {
+      for (int i = 0; i < kRing; ++i) ring[i] = load(i);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
-#pragma unroll
-      for (int dc = 0; dc < kDc; ++dc) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(sK + kaddr[dc] + kt * 32 * kRowBytes);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], s[kt], 0, 0, 0);
+      for (int i = 0; i < kSteps; ++i) {
+        const int kt = i % kKt, dc = i / kKt;
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], dc == 0 ? floatx16_t{} : s[kt],
+                                                        0, 0, 0);
+        if (i + kRing < kSteps) ring[i % kRing] = load(i + kRing);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
@@ -234,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
     const float mid = 0.5f * (lo + hi_t);
     float sum = 0.f;
 #pragma unroll
-    for (int bb = 0; bb < kBins; ++bb) sum += cnt[bb] * powpos(a1 * (base + bb * (W / kBins)) - mid, e);
+    for (int bb = 0; bb < kBins; ++bb) sum += cnt[bb] * powpos<PK>(a1 * (base + bb * (W / kBins)) - mid, e);
     if (sum >= 1.f)
       lo = mid;
     else
@@ -274,15 +296,27 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
           const float u = a1 * s[kt][i] - t;
           tmax = fmaxf(tmax, s[kt][i]);
           if (u > 0.f) {
-            const float pu = powpos(u, e);
-            s0 += pu;
-            if (p.alpha <= 2.f) {
-              const float r1 = pu / u;
-              s1 += r1;
-              if (p.alpha <= 1.5f) s2 += r1 / u;
+            // s0 = sum u^e, s1 = sum u^(e-1), s2 = sum u^(e-2) (the last two
+            // only where the step uses them)
+            if constexpr (PK == kPowSquare) {
+              s0 += u * u;
+              s1 += u;
+              s2 += 1.f;
+            } else if constexpr (PK == kPowLinear) {
+              s0 += u;
+              s1 += 1.f;
+            } else {
+              const float pu = powpos<PK>(u, e);
+              s0 += pu;
+              if (p.alpha <= 2.f) {
+                const float ru = __builtin_amdgcn_rcpf(u);
+                const float r1 = pu * ru;
+                s1 += r1;
+                if (p.alpha <= 1.5f) s2 += r1 * ru;
+              }
             }
           }
-          if (p.alpha > 2.f && first) shi += powpos(a1 * s[kt][i] - bhi, e);  // g at the upper end
+          if (p.alpha > 2.f && first) shi += powpos<PK>(a1 * s[kt][i] - bhi, e);  // g at the upper end
         }
       // mark the 128-key block if some live row's scores clear t_mask
       const bool any = __builtin_amdgcn_ballot_w64(live && a1 * tmax > t_mask) != 0;
@@ -372,21 +406,36 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
     for (int kt = 0; kt < kKt; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = powpos(a1 * s[kt][i] - t, e);
+        const float pv = powpos<PK>(a1 * s[kt][i] - t, e);
         l += pv;
         pb[kt][i >> 3][i & 7] = (__bf16)pv;
       }
+    {
+      // O^T += V^T P^T: V^T operands by transpose reads kRing MFMAs ahead,
+      // consecutive MFMAs alternating between the kDt accumulators (step i:
+      // dt = i % kDt, (kt, c) = i / kDt)
+      uint32_t vb[kDt];
 #pragma unroll
-    for (int kt = 0; kt < kKt; ++kt)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int dt = 0; dt < kDt; ++dt) {
-          const uint32_t addr = vlds[dt] + boff + kTileBytes + (kt * 32 + c * 16) * kRowBytes;
-          bf16x8_t a = tr_pair<0, 8 * kRowBytes>(addr);
-          lgkm_wait<0>(a);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][c], oacc[dt], 0, 0, 0);
-        }
+      for (int dt = 0; dt < kDt; ++dt) vb[dt] = vlds[dt] + boff + kTileBytes;
+      constexpr int kRing = 4;
+      constexpr int kSteps = kDt * kKt * 2;
+      bf16x8_t ring[kRing];
+      static_for<kRing>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        ring[i] = tr_pair<tr_off<L, kDt>(i), 8 * kRowBytes>(vb[i % kDt]);
+      });
+      static_for<kSteps>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int dt = i % kDt, kc = i / kDt;
+        // LDS reads complete in order: step i's are done once at most the
+        // reads issued after them are outstanding
+        lgkm_wait<2 * (kSteps - 1 - i < kRing - 1 ? kSteps - 1 - i : kRing - 1)>(ring[i % kRing]);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], pb[kc >> 1][kc & 1], oacc[dt], 0, 0, 0);
+        if constexpr (i + kRing < kSteps)
+          ring[i % kRing] = tr_pair<tr_off<L, kDt>(i + kRing), 8 * kRowBytes>(vb[(i + kRing) % kDt]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   const float l_tot = half_sum(l);
@@ -469,8 +518,17 @@ extern "C" int attn_entmax_fwd(const attn_tensor_t *q, const attn_tensor_t *k,
   p.alpha = alpha;
   const int64_t grid = (int64_t)p.n_tiles * p.batch * p.hq;
   void *args[] = {&p};
-  const void *fn = q->head_dim == 64 ? reinterpret_cast<const void *>(&attn_entmax_kernel<64>)
-                                     : reinterpret_cast<const void *>(&attn_entmax_kernel<128>);
+  // integer exponents (alpha = 2: e = 1; alpha = 1.5: e = 2) take the
+  // instantiation without transcendentals
+  const int pk = alpha == 2.f ? kPowLinear : (alpha == 1.5f ? kPowSquare : kPowGeneral);
+  const void *fns[2][3] = {
+      {reinterpret_cast<const void *>(&attn_entmax_kernel<64, kPowGeneral>),
+       reinterpret_cast<const void *>(&attn_entmax_kernel<64, kPowLinear>),
+       reinterpret_cast<const void *>(&attn_entmax_kernel<64, kPowSquare>)},
+      {reinterpret_cast<const void *>(&attn_entmax_kernel<128, kPowGeneral>),
+       reinterpret_cast<const void *>(&attn_entmax_kernel<128, kPowLinear>),
+       reinterpret_cast<const void *>(&attn_entmax_kernel<128, kPowSquare>)}};
+  const void *fn = fns[q->head_dim == 64 ? 0 : 1][pk];
   const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
