@@ -153,6 +153,23 @@ __device__ __forceinline__ void issue_rows(char *dst, const uint16_t *t0, const 
   }
 }
 
+// The 32 Q rows of one wave (from row `row0`, rows from `len` on re-reading
+// row len - 1) into LDS at `dst` in the K tiles' swizzled layout, with
+// whole-row 16 B loads.
+template <int kRowBytes, int kChunks, int kRowsPerWin>
+__device__ __forceinline__ void stage_q_rows(char *dst, const uint16_t *qg, int64_t q_ss, int row0, int len,
+                                             int lane) {
+  constexpr int kQLoads = 32 * kRowBytes / 1024;
+#pragma unroll
+  for (int n = 0; n < kQLoads; ++n) {
+    const int slot = n * 64 + lane;
+    const int r = slot / kChunks, pc = slot % kChunks;
+    const int64_t row = row0 + r < len ? row0 + r : len - 1;
+    const int swz = (r / kRowsPerWin) % kChunks;  // the K tiles' chunk swizzle
+    __builtin_amdgcn_global_load_lds(qg + row * q_ss + (pc ^ swz) * 8, (lds_void_t *)(dst + n * 1024), 16, 0, 0);
+  }
+}
+
 // One KV tile (K then V) into one LDS buffer.
 template <class C>
 __device__ __forceinline__ void issue_tile(char *kb, char *vb, const uint16_t *kt0,
@@ -332,12 +349,22 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
                     vg + (int64_t)kv_cur * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_cur);
   }
 
-  // ---- Q rows of this wave straight into registers (MFMA B operand: lane
-  // l32 holds head-dim values 16*dc + 8*hi .. +7 of its row); rows past the
-  // end of the sequence read as zero.  Loaded after the first K/V tile is
-  // issued, so that the two latencies overlap.
+  // ---- Q rows of this wave, the MFMA B operand (lane l32 holds head-dim
+  // values 16*dc + 8*hi .. +7 of its row), loaded after the first K/V tile is
+  // issued, so that the two latencies overlap.  The plain kernels load them
+  // straight into registers (rows past the end of the sequence read as
+  // zero).  The pipelined kernel stages them in this wave's part of the O
+  // staging area (free until the epilogue) with whole-row 16 B loads in the
+  // K tiles' swizzled layout and reads them into registers after the first
+  // barrier: loads in the operand layout touch 32 rows at 32 B each and
+  // queue at the texture unit for ~4x as many cache lines.  Rows past the
+  // end re-read the last row (finite; never stored).
   bf16x8_t qreg[kDc];
-  {
+  char *const q_stage = smem + 2 * kBufBytes + wave * 32 * L::kRowBytes;
+  if constexpr (kPipe) {
+    static_assert(kOwnStage, "Q is staged in the O staging area");
+    stage_q_rows<L::kRowBytes, L::kChunks, L::kRowsPerWin>(q_stage, qg, p.q_ss, q0 + wave * 32, len, lane);
+  } else {
     const int r = q0 + wave * 32 + l32;
 #pragma unroll
     for (int dc = 0; dc < kDc; ++dc) {
@@ -495,9 +522,14 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         __builtin_amdgcn_sched_barrier(0);
       });
     };
-    // iteration 0: scores of tile 0
+    // iteration 0: scores of tile 0 (first Q into registers: this wave's
+    // own staging loads have landed)
     sync();
     issue(0);
+#pragma unroll
+    for (int dc = 0; dc < kDc; ++dc)
+      qreg[dc] = *reinterpret_cast<const bf16x8_t *>(q_stage + kaddr[dc]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     phase(BufTag<0>{}, BufTag<0>{}, std::integral_constant<int, kOnlyS>{});
     if (!lagged) softmax(s, 0, pb);
     // iterations 1 .. n_own - 1, two per trip so that the buffers of each
