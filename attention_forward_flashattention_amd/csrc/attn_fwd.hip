@@ -160,6 +160,9 @@ template <int kRowBytes, int kChunks, int kRowsPerWin>
 __device__ __forceinline__ void stage_q_rows(char *dst, const uint16_t *qg, int64_t q_ss, int row0, int len,
                                              int lane) {
   constexpr int kQLoads = 32 * kRowBytes / 1024;
+  // (the empty asm keeps the compiler from sharing these lane offsets with the
+  // epilogue's similar ones, which would keep them live through the main loop)
+  asm volatile("" : "+v"(lane));
 #pragma unroll
   for (int n = 0; n < kQLoads; ++n) {
     const int slot = n * 64 + lane;
@@ -588,32 +591,33 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       kv_cur = kv_nxt;
       if (kv0 < 0) return false;
       if (CAUSAL && kv0 > wq_last) return false;  // whole tile above this wave's rows
-      const char *sK = smem + kBuf * kBufBytes;
 
       // ---- S^T = K Q^T : kKt tiles of 32 keys x 32 query rows
       floatx16_t s[kKt];
       {
-        // LDS operand reads run kRing MFMAs ahead of their use, and consecutive
-        // MFMAs alternate between the kKt independent accumulators, so neither
-        // the LDS latency nor the MFMA dependency latency is exposed
+        // LDS operand reads run kRing MFMAs ahead of their use, each waited for
+        // exactly (reads complete in order), and consecutive MFMAs alternate
+        // between the kKt independent accumulators, so neither the LDS
+        // latency nor the MFMA dependency latency is exposed
         constexpr int kRing = 4;
         constexpr int kSteps = kKt * kDc;  // step i: kt = i % kKt, dc = i / kKt
-        auto load = [&](int i) {
-          return *reinterpret_cast<const bf16x8_t *>(sK + kaddr[i / kKt] + (i % kKt) * 32 * L::kRowBytes);
+        auto load = [&](auto T) __attribute__((always_inline)) -> bf16x8_t {
+          constexpr int t = decltype(T)::value;
+          return ld_b128<kBuf * kBufBytes + (t % kKt) * 32 * L::kRowBytes>(klds[t / kKt]);
         };
         bf16x8_t ring[kRing];
-#pragma unroll
-        for (int i = 0; i < kRing; ++i) ring[i] = load(i);
-#pragma unroll
-        for (int i = 0; i < kSteps; ++i) {
-          const int kt = i % kKt, dc = i / kKt;
-          if (dc == 0)
+        static_for<kRing>([&](auto T) { ring[decltype(T)::value] = load(T); });
+        static_for<kSteps>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          constexpr int kt = i % kKt, dc = i / kKt;
+          lgkm_wait<(kSteps - 1 - i < kRing - 1 ? kSteps - 1 - i : kRing - 1)>(ring[i % kRing]);
+          if constexpr (dc == 0)
             s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], floatx16_t{}, 0, 0, 0);
           else
             s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], s[kt], 0, 0, 0);
-          if (i + kRing < kSteps) ring[i % kRing] = load(i + kRing);
+          if constexpr (i + kRing < kSteps) ring[i % kRing] = load(std::integral_constant<int, i + kRing>{});
           __builtin_amdgcn_sched_barrier(0);
-        }
+        });
       }
 
       bf16x8_t pb[kKt][2];
