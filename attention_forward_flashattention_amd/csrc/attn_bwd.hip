@@ -296,13 +296,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   // per-lane LDS offsets: row-wise reads of K and V (row l32, chunk 2 dc + hi)
   // and the two transpose reads of K^T (rows 4 hi + j16/4 and 8 more, the
   // 4 columns at 32 dt + 16 (l32/16) + 4 (j16%4))
-  int kaddr[kDc], vaddr[kDc];
+  uint32_t kaddr[kDc], vaddr[kDc];
   uint32_t ta[kDt], tb[kDt];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char_t *)smem;
 #pragma unroll
   for (int dc = 0; dc < kDc; ++dc) {
-    kaddr[dc] = LK::at(l32, 2 * dc + hi);
-    vaddr[dc] = LV::kq(l32, 2 * dc + hi);
+    kaddr[dc] = smem_lds + LK::at(l32, 2 * dc + hi);
+    vaddr[dc] = smem_lds + kTileBytes + LV::kq(l32, 2 * dc + hi);
     asm volatile("" : "+v"(kaddr[dc]));
     asm volatile("" : "+v"(vaddr[dc]));
   }
@@ -328,27 +328,49 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
     kv_cur = kv_nxt;
     if (kv0 < 0) return;
     if (CAUSAL && kv0 > wq_last) return;
-    const char *sK = smem + kBuf * kBufBytes;
-    const char *sV = sK + kTileBytes;
-
     const bool need_mask = (kv0 + kBN > len) || (CAUSAL && kv0 + kBN - 1 > q0 + wave * 32);
+    // key kv0 + 32 kt + hi*4 + o (o a compile-time offset) is masked when o > lim - 32 kt
+    const int lim = (CAUSAL ? min(qrow, len - 1) : len - 1) - kv0 - hi * 4;
     // one 32-key half of the tile at a time (bounds the live registers)
     static_for<kKt>([&](auto KT) {
       constexpr int kt = decltype(KT)::value;
       if (CAUSAL && kv0 + kt * 32 > wq_last) return;  // this half lies above every row
       // ---- S^T = K Q^T and dP^T = V dO^T (32 keys x 32 query rows)
+      // (operand reads four MFMAs ahead, each waited for exactly: LDS reads
+      // complete in order; step i: S (even i, a K row) or dP (odd i, a V
+      // row) of head-dim chunk i / 2)
       floatx16_t s, dp;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] = 0.f;
-        dp[i] = 0.f;
-      }
-#pragma unroll
-      for (int dc = 0; dc < kDc; ++dc) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(sK + kaddr[dc] + kt * 32 * kRowBytes);
-        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(sV + vaddr[dc] + kt * 32 * kRowBytes);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[dc], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, greg[dc], dp, 0, 0, 0);
+      {
+        constexpr int kRing = 4;
+        constexpr int kSteps = 2 * kDc;
+        constexpr int kOff = kBuf * kBufBytes + kt * 32 * kRowBytes;
+        auto load = [&](auto T) __attribute__((always_inline)) -> bf16x8_t {
+          constexpr int t = decltype(T)::value;
+          if constexpr (t & 1)
+            return ld_b128<kOff>(vaddr[t >> 1]);
+          else
+            return ld_b128<kOff>(kaddr[t >> 1]);
+        };
+        bf16x8_t ring[kRing];
+        static_for<kRing>([&](auto T) { ring[decltype(T)::value] = load(T); });
+        static_for<kSteps>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          constexpr int dc = i >> 1;
+          lgkm_wait<(kSteps - 1 - i < kRing - 1 ? kSteps - 1 - i : kRing - 1)>(ring[i % kRing]);
+          if constexpr (i & 1) {
+            if constexpr (dc == 0)
+              dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], greg[dc], floatx16_t{}, 0, 0, 0);
+            else
+              dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], greg[dc], dp, 0, 0, 0);
+          } else {
+            if constexpr (dc == 0)
+              s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], floatx16_t{}, 0, 0, 0);
+            else
+              s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], s, 0, 0, 0);
+          }
+          if constexpr (i + kRing < kSteps) ring[i % kRing] = load(std::integral_constant<int, i + kRing>{});
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
       // ---- P^T = 2^(c s - lse2) with the causal diagonal and sequence tail
       // masked, dS^T = P^T (dP^T - D), rounded to bf16 in the B operand
@@ -358,21 +380,29 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -lse2));
-        if (need_mask) {
-          const int key = kv0 + kt * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-          if (key >= len || (CAUSAL && key > qrow)) pv = 0.f;
-        }
+        if (need_mask && kt * 32 + (i >> 2) * 8 + (i & 3) > lim) pv = 0.f;
         dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - drow));
       }
-      // ---- dQ^T += K^T dS^T
-      static_for<kDt * 2>([&](auto I) {
-        constexpr int i = decltype(I)::value;
-        constexpr int dt = i % kDt, c = i / kDt;
-        constexpr int off = kBuf * kBufBytes + (32 * kt + 16 * c) * kRowBytes;
-        bf16x8_t a = tr_pair2<off>(ta[dt], tb[dt]);
-        lgkm_wait<0>(a);
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[c], acc[dt], 0, 0, 0);
-      });
+      // ---- dQ^T += K^T dS^T (K^T by transpose reads four MFMAs ahead,
+      // waited for exactly; consecutive MFMAs on different accumulators)
+      {
+        constexpr int kRing = 4;
+        constexpr int kSteps = kDt * 2;  // step i: dt = i % kDt, c = i / kDt
+        auto load = [&](auto T) __attribute__((always_inline)) -> bf16x8_t {
+          constexpr int t = decltype(T)::value;
+          return tr_pair2<kBuf * kBufBytes + (32 * kt + 16 * (t / kDt)) * kRowBytes>(ta[t % kDt], tb[t % kDt]);
+        };
+        bf16x8_t ring[kRing];
+        static_for<kRing>([&](auto T) { ring[decltype(T)::value] = load(T); });
+        static_for<kSteps>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          constexpr int dt = i % kDt, c = i / kDt;
+          lgkm_wait<2 * (kSteps - 1 - i < kRing - 1 ? kSteps - 1 - i : kRing - 1)>(ring[i % kRing]);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], dsb[c], acc[dt], 0, 0, 0);
+          if constexpr (i + kRing < kSteps) ring[i % kRing] = load(std::integral_constant<int, i + kRing>{});
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
     });
   };
   for (int it = 0; it < n_iter; it += 2) {
