@@ -616,12 +616,12 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
   // per-lane LDS offsets: row-wise reads of Q and dO (row l32, chunk
   // 2 dc + hi) and transpose reads (rows 4 hi + j16/4 and 8 more, the 4
   // columns at 32 dt + 16 (l32/16) + 4 (j16%4))
-  int raddr[kDc];
+  uint32_t raddr[kDc];
   uint32_t ta[kDt], tb[kDt];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char_t *)smem;
 #pragma unroll
   for (int dc = 0; dc < kDc; ++dc) {
-    raddr[dc] = L::at(l32, 2 * dc + hi);
+    raddr[dc] = smem_lds + L::at(l32, 2 * dc + hi);
     asm volatile("" : "+v"(raddr[dc]));
   }
 #pragma unroll
@@ -666,39 +666,51 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     };
+    // Register i of half h holds query row qh0 + 4 hi + r, r = 8 (i/4) + i%4
+    // (a compile-time offset): the row is visible to this lane's key when
+    // r >= key - (qh0 + 4 hi) (causal) and r < len - (qh0 + 4 hi)
+    int rlo[2], rhi[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r0 = q0 + 32 * h + 4 * hi;
+      rlo[h] = key - r0;
+      rhi[h] = len - r0;
+    }
     // VALU of element i (of 16) of half h: P = 2^(c s - lse2), dS = P (dP - D);
     // rows past the end and keys after their query (causal) get P = 0
     auto valu = [&](auto H, auto I) __attribute__((always_inline)) {
       constexpr int h = decltype(H)::value, i = decltype(I)::value;
-      constexpr int g4 = i / 4, e = i % 4;
+      constexpr int g4 = i / 4, e = i % 4, r = 8 * g4 + e;
       const float lv = e == 0 ? l4[g4].x : e == 1 ? l4[g4].y : e == 2 ? l4[g4].z : l4[g4].w;
       const float dv4 = e == 0 ? d4[g4].x : e == 1 ? d4[g4].y : e == 2 ? d4[g4].z : d4[g4].w;
       const int qh0 = q0 + 32 * h;
       const bool need_mask = (qh0 + 32 > len) || (CAUSAL && qh0 < kw0 + 31);
       float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][i], p.c, -lv));
-      const int qr = qh0 + 8 * g4 + 4 * hi + e;
-      if (need_mask && (qr >= len || (CAUSAL && key > qr))) pv = 0.f;
+      if (need_mask && (r >= rhi[h] || (CAUSAL && r < rlo[h]))) pv = 0.f;
       pb[h][i >> 3][i & 7] = (__bf16)pv;
       dsb[h][i >> 3][i & 7] = (__bf16)(pv * (dp[h][i] - dv4));
     };
+    // this tile's buffer: row-wise read addresses of Q (dO kTileBytes on)
+    uint32_t rb[kDc];
+#pragma unroll
+    for (int dc = 0; dc < kDc; ++dc) rb[dc] = raddr[dc] + boff;
     // S = Q K^T and dP = dO V^T of half h (32 query rows x 32 keys; lane =
-    // key), operand reads kRing MFMAs ahead, S and dP alternating; the VALU
-    // of half hv (if hv >= 0) spread over the steps
+    // key), operand reads kRing MFMAs ahead with exact waits, S and dP
+    // alternating; the VALU of half hv (if hv >= 0) spread over the steps
     auto sdp = [&](auto H, auto HV) __attribute__((always_inline)) {
       constexpr int h = decltype(H)::value, hv = decltype(HV)::value;
-      const char *sQ = smem + boff + h * 32 * kRowBytes;
       constexpr int kRing = 4;
       constexpr int kSteps = 2 * kDc;  // step i: dc = i / 2, Q (even) or dO (odd)
       constexpr int kPer = 16 / kSteps;  // VALU elements per step
-      auto load = [&](int i) {
-        return *reinterpret_cast<const bf16x8_t *>(sQ + raddr[i >> 1] + (i & 1) * kTileBytes);
-      };
       bf16x8_t ring[kRing];
-#pragma unroll
-      for (int i = 0; i < kRing; ++i) ring[i] = load(i);
+      static_for<kRing>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        ring[i] = ld_b128<h * 32 * kRowBytes + (i & 1) * kTileBytes>(rb[i >> 1]);
+      });
       static_for<kSteps>([&](auto I) {
         constexpr int i = decltype(I)::value;
         constexpr int dc = i >> 1;
+        lgkm_wait<(kSteps - 1 - i < kRing - 1 ? kSteps - 1 - i : kRing - 1)>(ring[i % kRing]);
         if constexpr (i & 1) {
           if constexpr (dc == 0)
             dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], vreg[dc], floatx16_t{}, 0, 0, 0);
@@ -710,7 +722,10 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
           else
             s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], kreg[dc], s[h], 0, 0, 0);
         }
-        if constexpr (i + kRing < kSteps) ring[i % kRing] = load(i + kRing);
+        if constexpr (i + kRing < kSteps) {
+          constexpr int j = i + kRing;
+          ring[i % kRing] = ld_b128<h * 32 * kRowBytes + (j & 1) * kTileBytes>(rb[j >> 1]);
+        }
         if constexpr (hv >= 0)
           static_for<kPer>([&](auto E) { valu(HV, std::integral_constant<int, i * kPer + decltype(E)::value>{}); });
         __builtin_amdgcn_sched_barrier(0);
