@@ -376,12 +376,24 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
       // masked, dS^T = P^T (dP^T - D), rounded to bf16 in the B operand
       // layout (MFMA k index e of step c = key 32 kt + 16 c + 8 (e/4) +
       // 4 hi + e%4)
+      // (two copies behind a uniform branch: left to itself the compiler
+      // evaluates the mask on every tile and selects)
       bf16x8_t dsb[2];
+      auto ds_tile = [&](auto M) __attribute__((always_inline)) {
+        constexpr bool kMask = decltype(M)::value;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -lse2));
-        if (need_mask && kt * 32 + (i >> 2) * 8 + (i & 3) > lim) pv = 0.f;
-        dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - drow));
+        for (int i = 0; i < 16; ++i) {
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c, -lse2));
+          if (kMask && kt * 32 + (i >> 2) * 8 + (i & 3) > lim) pv = 0.f;
+          dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - drow));
+        }
+      };
+      if (need_mask) {
+        asm volatile("; masked tile");
+        ds_tile(std::true_type{});
+      } else {
+        asm volatile("; unmasked tile");
+        ds_tile(std::false_type{});
       }
       // ---- dQ^T += K^T dS^T (K^T by transpose reads four MFMAs ahead,
       // waited for exactly; consecutive MFMAs on different accumulators)
@@ -677,18 +689,32 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
       rhi[h] = len - r0;
     }
     // VALU of element i (of 16) of half h: P = 2^(c s - lse2), dS = P (dP - D);
-    // rows past the end and keys after their query (causal) get P = 0
-    auto valu = [&](auto H, auto I) __attribute__((always_inline)) {
+    // with kMask, rows past the end and keys after their query (causal) get
+    // P = 0
+    auto valu_m = [&](auto H, auto I, auto M) __attribute__((always_inline)) {
       constexpr int h = decltype(H)::value, i = decltype(I)::value;
+      constexpr bool kMask = decltype(M)::value;
       constexpr int g4 = i / 4, e = i % 4, r = 8 * g4 + e;
       const float lv = e == 0 ? l4[g4].x : e == 1 ? l4[g4].y : e == 2 ? l4[g4].z : l4[g4].w;
       const float dv4 = e == 0 ? d4[g4].x : e == 1 ? d4[g4].y : e == 2 ? d4[g4].z : d4[g4].w;
-      const int qh0 = q0 + 32 * h;
-      const bool need_mask = (qh0 + 32 > len) || (CAUSAL && qh0 < kw0 + 31);
       float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][i], p.c, -lv));
-      if (need_mask && (r >= rhi[h] || (CAUSAL && r < rlo[h]))) pv = 0.f;
+      if (kMask && (r >= rhi[h] || (CAUSAL && r < rlo[h]))) pv = 0.f;
       pb[h][i >> 3][i & 7] = (__bf16)pv;
       dsb[h][i >> 3][i & 7] = (__bf16)(pv * (dp[h][i] - dv4));
+    };
+    // the unmasked form, spread over the MFMA steps of the other half
+    auto valu = [&](auto H, auto I) __attribute__((always_inline)) { valu_m(H, I, std::false_type{}); };
+    // a half whose rows reach past the end, or (causal) precede some of this
+    // wave's keys, is formed again with the mask once its unmasked VALU is
+    // done (a uniform branch, taken on the diagonal and the tail only; left
+    // to itself the compiler would evaluate the mask on every half)
+    auto fixup = [&](auto H) __attribute__((always_inline)) {
+      constexpr int h = decltype(H)::value;
+      const int qh0 = q0 + 32 * h;
+      if ((qh0 + 32 > len) || (CAUSAL && qh0 < kw0 + 31)) {
+        asm volatile("; masked half");
+        static_for<16>([&](auto I) { valu_m(H, I, std::true_type{}); });
+      }
     };
     // this tile's buffer: row-wise read addresses of Q (dO kTileBytes on)
     uint32_t rb[kDc];
@@ -779,8 +805,10 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
     sdp(C0{}, CN{});
     load_ld(0);
     sdp(C1{}, C0{});
+    fixup(C0{});
     load_ld(1);
     dvdk(C0{}, C1{});
+    fixup(C1{});
     dvdk(C1{}, CN{});
   };
   for (int it = 0; it < n_iter; ++it) step(it, it & 1);
