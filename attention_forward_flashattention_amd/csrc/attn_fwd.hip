@@ -341,8 +341,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   const int wq_last = q0 + wave * 32 + 31;
 
   // Dense problems with two waves per SIMD from one workgroup run the
-  // software-pipelined loop below; the other kernels the plain one.
-  constexpr bool kPipe = MODE == kDense && C::NW >= 8;
+  // software-pipelined loop below, and so does head_dim 256 (one wave per
+  // SIMD, in its solo form); the other kernels the plain one.
+  constexpr bool kSolo = MODE == kDense && C::NW == 4 && D == 256;
+  constexpr bool kPipe = (MODE == kDense && C::NW >= 8) || kSolo;
   int kv_cur = n_iter > 0 ? kv_start(0) : -1;
   if (kv_cur >= 0 && loader) {
     if constexpr (kPipe)
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   // running max).  Then the max is raised to the tile's, O and l are
   // rescaled and P is computed again.
   bool first = true;  // no tile processed yet by this wave
-  auto softmax = [&](floatx16_t (&s)[kKt], const int kv0, bf16x8_t (&pb)[kKt][2]) __attribute__((always_inline)) {
+  auto mask_tile = [&](floatx16_t (&s)[kKt], const int kv0) __attribute__((always_inline)) {
     const bool need_mask = (kv0 + kBN > len) || (CAUSAL && kv0 + kBN - 1 > q0 + wave * 32);
     if (need_mask) {
       // key kv0 + hi*4 + o (o a compile-time offset) is masked when o > lim
@@ -418,13 +420,11 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         for (int i = 0; i < 16; ++i)
           if (kt * 32 + (i >> 2) * 8 + (i & 3) > lim) s[kt][i] = -INFINITY;
     }
-    float rs = 0.f;
-    bool slow = first;
-    if (!first) {
-      rs = exp_tile(s, p.c, m_run == -INFINITY ? 0.f : m_run, pb);
-      slow = __builtin_amdgcn_ballot_w64(rs > kFastSum) != 0;
-    }
-    first = false;
+  };
+  // the rest of the online softmax once P has been formed against the
+  // running max (row sums rs), or not at all on the wave's first tile
+  // (slow): the max raise, O rescale and P again when needed
+  auto softmax_slow = [&](floatx16_t (&s)[kKt], bf16x8_t (&pb)[kKt][2], float rs, bool slow) __attribute__((always_inline)) {
     if (slow) {
       float mx = -INFINITY;
 #pragma unroll
@@ -446,6 +446,17 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     }
     l_run += rs;
     if (OSK) d_run += rs;
+  };
+  auto softmax = [&](floatx16_t (&s)[kKt], const int kv0, bf16x8_t (&pb)[kKt][2]) __attribute__((always_inline)) {
+    mask_tile(s, kv0);
+    float rs = 0.f;
+    bool slow = first;
+    if (!first) {
+      rs = exp_tile(s, p.c, m_run == -INFINITY ? 0.f : m_run, pb);
+      slow = __builtin_amdgcn_ballot_w64(rs > kFastSum) != 0;
+    }
+    first = false;
+    softmax_slow(s, pb, rs, slow);
   };
 
   int n_done = n_iter;  // tiles walked (ordered skipping may stop early)
@@ -534,6 +545,74 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       qreg[dc] = *reinterpret_cast<const bf16x8_t *>(q_stage + kaddr[dc]);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     phase(BufTag<0>{}, BufTag<0>{}, std::integral_constant<int, kOnlyS>{});
+    if constexpr (kSolo) {
+      // ---- one wave per SIMD: no other wave fills the matrix core while
+      // this one runs its softmax, so the softmax is spread over its own
+      // MFMAs.  Iteration j forms S(j), then runs O^T += V(j-1)^T P(j-1)^T
+      // with the fast-path exp2 of S(j) (against the running max) issued one
+      // element per MFMA, then finishes the softmax of S(j) (the rare max
+      // raise and O rescale come after the PV MFMAs that precede them).
+      // P(j) goes to P buffer j % 2.
+      static_assert(kKt == 1 && kDt == 8, "one 32-key score tile; one exp2 per PV MFMA");
+      bf16x8_t pp[2][kKt][2];
+      softmax(s, 0, pp[0]);
+      auto pv_exp = [&](auto vb_tag, auto ps_tag, auto pd_tag) __attribute__((always_inline)) -> float {
+        constexpr int kVb = decltype(vb_tag)::value;  // V buffer of the PV tile
+        constexpr int kPs = decltype(ps_tag)::value;  // its P buffer
+        constexpr int kPd = decltype(pd_tag)::value;  // P buffer of S (-1: no exp2)
+        constexpr int kN = kDt * kKt * 2;
+        constexpr int kRing = 4;
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float rs = 0.f;
+        auto load = [&](auto T) __attribute__((always_inline)) -> bf16x8_t {
+          constexpr int t = decltype(T)::value;
+          return tr_pair<kVb * kBufBytes + kTileBytes + tr_off<L, kDt>(t), 8 * L::kRowBytes>(vlds[t % kDt]);
+        };
+        bf16x8_t ring[kRing];
+        static_for<kRing>([&](auto T) { ring[decltype(T)::value] = load(T); });
+        static_for<kN>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          constexpr int dt = i % kDt, kc = i / kDt;
+          lgkm_wait<2 * (kN - 1 - i < kRing - 1 ? kN - 1 - i : kRing - 1)>(ring[i % kRing]);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], pp[kPs][kc >> 1][kc & 1], oacc[dt], 0, 0, 0);
+          if constexpr (i + kRing < kN) ring[i % kRing] = load(std::integral_constant<int, i + kRing>{});
+          if constexpr (kPd >= 0) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][i], p.c, -m_use));
+            rs += pv;
+            pp[kPd][0][i >> 3][i & 7] = (__bf16)pv;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        return rs;
+      };
+      int j = 1;
+      auto body_solo = [&](auto kb_tag) __attribute__((always_inline)) {
+        constexpr int kKb = decltype(kb_tag)::value;  // = j % 2
+        sync();
+        issue(j);
+        phase(kb_tag, BufTag<1 - kKb>{}, std::integral_constant<int, kOnlyS>{});
+        mask_tile(s, j * kBN);
+        const float rs = pv_exp(BufTag<1 - kKb>{}, BufTag<1 - kKb>{}, BufTag<kKb>{});
+        softmax_slow(s, pp[kKb], rs, __builtin_amdgcn_ballot_w64(rs > kFastSum) != 0);
+        ++j;
+      };
+      while (j + 1 < n_own) {
+        body_solo(BufTag<1>{});
+        body_solo(BufTag<0>{});
+      }
+      if (j < n_own) body_solo(BufTag<1>{});
+      // iteration n_own: PV of the wave's last tile
+      sync();
+      issue(n_own);
+      if ((n_own - 1) & 1)
+        pv_exp(BufTag<1>{}, BufTag<1>{}, BufTag<-1>{});
+      else
+        pv_exp(BufTag<0>{}, BufTag<0>{}, BufTag<-1>{});
+      for (int jj = n_own + 1; jj <= n_iter; ++jj) {
+        sync();
+        issue(jj);
+      }
+    } else {
     if (!lagged) softmax(s, 0, pb);
     // iterations 1 .. n_own - 1, two per trip so that the buffers of each
     // are compile-time constants
@@ -564,6 +643,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     for (int jj = n_own + 1; jj <= n_iter; ++jj) {
       sync();
       issue(jj);
+    }
     }
   } else {
     // Returns true (ordered skipping only) when the walk stops before tile `it`.
