@@ -193,9 +193,12 @@ def test_empty_allowed_set():
     P.compare(o, l, o_ref, l_ref, "empty")
 
 
-def test_large_scores_shifted_keys():
-    """Keys shifted by a large constant (scores of several hundred) stay finite and exact."""
-    w = W.make_dense("sh", 20, 1, 512, 2, 1, 128, True)
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_large_scores_shifted_keys(d):
+    """Keys shifted by a large constant (scores of several hundred) stay finite and exact
+    (each head_dim runs its own loop form)."""
+    note(f"shifted keys d={d}")
+    w = W.make_dense("sh", 20, 1, 512, 2, 1, d, True)
     kf = W.bf16_bits_to_f32(w.k) + np.float32(24.0)
     w.k = W.f32_to_bf16_bits(kf)
     stats = P.check_workload(w)
@@ -293,11 +296,14 @@ def test_block_mask_workload_sampled():
     note(f"  {stats}")
 
 
-def test_late_large_score_raises_running_max():
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_late_large_score_raises_running_max(d):
     """A key late in the sequence scores far above every earlier key (P would be
-    ~2^50 against the running max): the kernel must raise the max and rescale O
-    and l mid-row.  Q is positive so that key 700 wins in every row that sees it."""
-    w = W.make_dense("late", 22, 1, 1024, 4, 2, 128, True)
+    2^22 or more against the running max): the kernel must raise the max and
+    rescale O and l mid-row, in each head_dim's loop form.  Q is positive so
+    that key 700 wins in every row that sees it."""
+    note(f"late large score d={d}")
+    w = W.make_dense("late", 22, 1, 1024, 4, 2, d, True)
     qf = np.abs(W.bf16_bits_to_f32(w.q))
     w.q = W.f32_to_bf16_bits(qf)
     kf = W.bf16_bits_to_f32(w.k)
