@@ -665,18 +665,32 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
     //   dV, dK of half 0 + VALU of half 1 | dV, dK of half 1.
     floatx16_t s[2], dp[2];
     bf16x8_t pb[2][2], dsb[2][2];
-    float4 l4[4], d4[4];
+    typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+    f32x4_t l4[2][4], d4[2][4];
     // lse2 and D of this lane's 16 rows of half h (register i: row 8 (i/4) +
-    // 4 hi + i%4), waited for at once (the phases' own LDS reads are counted
-    // by explicit waits)
-    auto load_ld = [&](const int h) __attribute__((always_inline)) {
-      const float *sL = reinterpret_cast<const float *>(smem + boff + 2 * kTileBytes) + 32 * h;
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        l4[g4] = *reinterpret_cast<const float4 *>(sL + 8 * g4 + 4 * hi);
-        d4[g4] = *reinterpret_cast<const float4 *>(sL + kBQ + 8 * g4 + 4 * hi);
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // 4 hi + i%4), by inline-assembly reads like the operand rings (a plain
+    // load would make the compiler wait for every LDS read in flight at the
+    // first use).  Read early (head_dim 128), they need no wait of their own:
+    // the half's VALU uses S of that half, whose last MFMA follows the
+    // lgkmcnt(0) that ends its phase, which comes after these reads (LDS
+    // reads complete in order).  Read late (head_dim 64), ld_wait ties them
+    // to a wait of their own.
+    const uint32_t ld_base = smem_lds + boff + 2 * kTileBytes + 16 * hi;
+    auto load_ld = [&](auto H) __attribute__((always_inline)) {
+      constexpr int h = decltype(H)::value;
+      static_for<4>([&](auto G) {
+        constexpr int g4 = decltype(G)::value;
+        l4[h][g4] = __builtin_bit_cast(f32x4_t, ld_b128<(32 * h + 8 * g4) * 4>(ld_base));
+        d4[h][g4] = __builtin_bit_cast(f32x4_t, ld_b128<(kBQ + 32 * h + 8 * g4) * 4>(ld_base));
+      });
+    };
+    auto ld_wait = [&](auto H) __attribute__((always_inline)) {
+      constexpr int h = decltype(H)::value;
+      f32x4_t(&lh)[4] = l4[h];
+      f32x4_t(&dh)[4] = d4[h];
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(lh[0]), "+v"(lh[1]), "+v"(lh[2]), "+v"(lh[3]), "+v"(dh[0]), "+v"(dh[1]), "+v"(dh[2]),
+                     "+v"(dh[3]));
     };
     // Register i of half h holds query row qh0 + 4 hi + r, r = 8 (i/4) + i%4
     // (a compile-time offset): the row is visible to this lane's key when
@@ -688,32 +702,36 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
       rlo[h] = key - r0;
       rhi[h] = len - r0;
     }
-    // VALU of element i (of 16) of half h: P = 2^(c s - lse2), dS = P (dP - D);
-    // with kMask, rows past the end and keys after their query (causal) get
-    // P = 0
-    auto valu_m = [&](auto H, auto I, auto M) __attribute__((always_inline)) {
+    // VALU of element i (of 16) of half h: P = 2^(c s - lse2), dS = P (dP - D),
+    // spread over the MFMA steps of the other half; no mask here
+    auto valu = [&](auto H, auto I) __attribute__((always_inline)) {
       constexpr int h = decltype(H)::value, i = decltype(I)::value;
-      constexpr bool kMask = decltype(M)::value;
-      constexpr int g4 = i / 4, e = i % 4, r = 8 * g4 + e;
-      const float lv = e == 0 ? l4[g4].x : e == 1 ? l4[g4].y : e == 2 ? l4[g4].z : l4[g4].w;
-      const float dv4 = e == 0 ? d4[g4].x : e == 1 ? d4[g4].y : e == 2 ? d4[g4].z : d4[g4].w;
-      float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][i], p.c, -lv));
-      if (kMask && (r >= rhi[h] || (CAUSAL && r < rlo[h]))) pv = 0.f;
+      constexpr int g4 = i / 4, e = i % 4;
+      const float lv = l4[h][g4][e];
+      const float dv4 = d4[h][g4][e];
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][i], p.c, -lv));
       pb[h][i >> 3][i & 7] = (__bf16)pv;
       dsb[h][i >> 3][i & 7] = (__bf16)(pv * (dp[h][i] - dv4));
     };
-    // the unmasked form, spread over the MFMA steps of the other half
-    auto valu = [&](auto H, auto I) __attribute__((always_inline)) { valu_m(H, I, std::false_type{}); };
-    // a half whose rows reach past the end, or (causal) precede some of this
-    // wave's keys, is formed again with the mask once its unmasked VALU is
-    // done (a uniform branch, taken on the diagonal and the tail only; left
-    // to itself the compiler would evaluate the mask on every half)
+    // A half whose rows reach past the end, or (causal) precede some of this
+    // wave's keys, then has P and dS zeroed where the row is past the end or
+    // before the lane's key (a uniform branch, taken on the diagonal and the
+    // tail only; evaluating the mask inside the spread VALU would cost two
+    // compares and a select per element on every half).  Patching, rather
+    // than forming the half again, keeps the spread VALU's results live on
+    // both paths, so the compiler cannot sink them below the branch.
     auto fixup = [&](auto H) __attribute__((always_inline)) {
       constexpr int h = decltype(H)::value;
       const int qh0 = q0 + 32 * h;
       if ((qh0 + 32 > len) || (CAUSAL && qh0 < kw0 + 31)) {
         asm volatile("; masked half");
-        static_for<16>([&](auto I) { valu_m(H, I, std::true_type{}); });
+        static_for<16>([&](auto I) {
+          constexpr int i = decltype(I)::value, r = 8 * (i / 4) + i % 4;
+          if (r >= rhi[h] || (CAUSAL && r < rlo[h])) {
+            pb[h][i >> 3][i & 7] = (__bf16)0.f;
+            dsb[h][i >> 3][i & 7] = (__bf16)0.f;
+          }
+        });
       }
     };
     // this tile's buffer: row-wise read addresses of Q (dO kTileBytes on)
@@ -802,11 +820,23 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
     using CN = std::integral_constant<int, -1>;
+    // (at head_dim 128 the wave has registers to spare for both halves'
+    // values at once; at 64 they are read just before their half's VALU)
+    constexpr bool kEarly = D == 128;
+    if constexpr (kEarly) load_ld(C0{});
     sdp(C0{}, CN{});
-    load_ld(0);
+    if constexpr (kEarly) {
+      load_ld(C1{});
+    } else {
+      load_ld(C0{});
+      ld_wait(C0{});
+    }
     sdp(C1{}, C0{});
     fixup(C0{});
-    load_ld(1);
+    if constexpr (!kEarly) {
+      load_ld(C1{});
+      ld_wait(C1{});
+    }
     dvdk(C0{}, C1{});
     fixup(C1{});
     dvdk(C1{}, CN{});
