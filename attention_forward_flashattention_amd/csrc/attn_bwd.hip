@@ -141,6 +141,13 @@ __device__ __forceinline__ void issue_pair_full(char *la, char *lb, const uint16
   }
 }
 
+// Load n of a whole tile's rows (as issue_pair_full does for every n), for
+// callers that spread the loads over other work.
+template <int kN>
+__device__ __forceinline__ void issue_one(char *l, const uint16_t *g, const int64_t *off) {
+  __builtin_amdgcn_global_load_lds(g + off[kN], (lds_void_t *)(l + kN * 1024), 16, 0, 0);
+}
+
 // One dword per lane from global to 64 consecutive LDS dwords.
 __device__ __forceinline__ void issue_dwords(char *l, const float *src) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t *)l, 4, 0, 0);
@@ -576,12 +583,16 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
     qoff[n] = (int64_t)r * p.q_ss + (pc ^ L::f(r)) * 8;
     goff[n] = (int64_t)r * p.g_ss + (pc ^ L::f(r)) * 8;
   }
-  auto issue = [&](int buf, int q0, int head) {
+  // Loads of the query tile at q0 of `head` into buffer buf: Q and dO rows
+  // (unless `rows_deferred`: a whole tile whose rows the caller issues
+  // itself, one load at a time) and the lse2 / D values.
+  auto issue = [&](int buf, int q0, int head, bool rows_deferred = false) {
     char *bq = smem + buf * kBufBytes;
     const uint16_t *qt = qbase + (int64_t)head * p.q_sh + (int64_t)q0 * p.q_ss;
     const uint16_t *gt = gbase + (int64_t)head * p.g_sh + (int64_t)q0 * p.g_ss;
     const int rows_left = len - q0;
-    if (rows_left >= kBQ)
+    if (rows_deferred) {
+    } else if (rows_left >= kBQ)
       issue_pair_full<kLoads>(bq + slot_byte0, bq + kTileBytes + slot_byte0, qt, gt, qoff, goff);
     else
       issue_pair<kLoads>(bq + slot_byte0, bq + kTileBytes + slot_byte0, qt, gt, qoff, goff, lrow,
@@ -651,10 +662,18 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     int q_nxt = 0, head_nxt = 0;
+    // a whole next tile has its Q / dO row loads spread over the first
+    // half's S / dP MFMAs (their issue would otherwise hold up the matrix
+    // core after the barrier); a partial one is issued here
+    bool spread = false;
     if (it + 1 < n_iter) {
       q_nxt = q_start(it + 1, head_nxt);
-      issue(1 - buf, q_nxt, head_nxt);
+      spread = len - q_nxt >= kBQ;
+      issue(1 - buf, q_nxt, head_nxt, spread);
     }
+    const uint16_t *const qt_n = qbase + (int64_t)head_nxt * p.q_sh + (int64_t)q_nxt * p.q_ss;
+    const uint16_t *const gt_n = gbase + (int64_t)head_nxt * p.g_sh + (int64_t)q_nxt * p.g_ss;
+    char *const bq_n = smem + (1 - buf) * kBufBytes + slot_byte0;
     const int q0 = q_cur;
     q_cur = q_nxt;
     const int boff = buf * kBufBytes;
@@ -746,6 +765,7 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
       constexpr int kRing = 4;
       constexpr int kSteps = 2 * kDc;  // step i: dc = i / 2, Q (even) or dO (odd)
       constexpr int kPer = 16 / kSteps;  // VALU elements per step
+      static_assert(2 * kLoads <= kSteps, "the next tile's row loads fit in the first half's steps");
       bf16x8_t ring[kRing];
       static_for<kRing>([&](auto I) {
         constexpr int i = decltype(I)::value;
@@ -769,6 +789,16 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
         if constexpr (i + kRing < kSteps) {
           constexpr int j = i + kRing;
           ring[i % kRing] = ld_b128<h * 32 * kRowBytes + (j & 1) * kTileBytes>(rb[j >> 1]);
+        }
+        if constexpr (h == 0 && i < 2 * kLoads) {
+          // load i / 2 of the next tile's Q (even i) or dO (odd i) rows
+          constexpr int n = i >> 1;
+          if (spread) {
+            if constexpr (i & 1)
+              issue_one<n>(bq_n + kTileBytes, gt_n, goff);
+            else
+              issue_one<n>(bq_n, qt_n, qoff);
+          }
         }
         if constexpr (hv >= 0)
           static_for<kPer>([&](auto E) { valu(HV, std::integral_constant<int, i * kPer + decltype(E)::value>{}); });
