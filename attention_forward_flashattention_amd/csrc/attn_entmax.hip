@@ -165,33 +165,47 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
     if (live) x = ld_global16(qg + (int64_t)qrow * p.q_ss + dc * 16 + hi * 8);
     qreg[dc] = __builtin_bit_cast(bf16x8_t, x);
   }
-  int kaddr[kDc];
+  // absolute LDS addresses of this lane's K operand reads in buffer 0 (the
+  // empty asm keeps each in one register)
+  uint32_t kabs[kDc];
 #pragma unroll
-  for (int dc = 0; dc < kDc; ++dc) kaddr[dc] = L::kq(l32, dc * 2 + hi);
+  for (int dc = 0; dc < kDc; ++dc) {
+    kabs[dc] = (uint32_t)(uintptr_t)(lds_char_t *)smem + (uint32_t)L::kq(l32, dc * 2 + hi);
+    asm volatile("" : "+v"(kabs[dc]));
+  }
 
   // S^T of one K tile: s[kt][i] is the score of key kv0 + 32 kt + 8 (i/4) +
   // 4 hi + i%4 for this lane's row; keys past kv_end, after the row (causal)
   // or rows past the end get -inf
-  auto scores = [&](const char *sK, int kv0, floatx16_t (&s)[kKt]) {
+  auto scores = [&](const int buf_off, int kv0, floatx16_t (&s)[kKt]) {
     {
-      // operand reads run kRing MFMAs ahead; consecutive MFMAs alternate
-      // between the kKt accumulators (step i: kt = i % kKt, dc = i / kKt)
+      // operand reads (K tile at byte buf_off of the LDS) run kRing MFMAs
+      // ahead, each waited for exactly (inline-assembly reads: LDS reads
+      // complete in order; the compiler would wait for each group of kRing
+      // at once); consecutive MFMAs alternate between the kKt accumulators
+      // (step i: kt = i % kKt, dc = i / kKt)
       constexpr int kRing = 4;
       constexpr int kSteps = kKt * kDc;
-      auto load = [&](int i) {
-        return *reinterpret_cast<const bf16x8_t *>(sK + kaddr[i / kKt] + (i % kKt) * 32 * kRowBytes);
+      uint32_t ka[kDc];
+#pragma unroll
+      for (int dc = 0; dc < kDc; ++dc) ka[dc] = kabs[dc] + (uint32_t)buf_off;
+      auto load = [&](auto T) __attribute__((always_inline)) -> bf16x8_t {
+        constexpr int t = decltype(T)::value;
+        return ld_b128<(t % kKt) * 32 * kRowBytes>(ka[t / kKt]);
       };
       bf16x8_t ring[kRing];
-#pragma unroll
-      for (int i = 0; i < kRing; ++i) ring[i] = load(i);
-#pragma unroll
-      for (int i = 0; i < kSteps; ++i) {
-        const int kt = i % kKt, dc = i / kKt;
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], dc == 0 ? floatx16_t{} : s[kt],
-                                                        0, 0, 0);
-        if (i + kRing < kSteps) ring[i % kRing] = load(i + kRing);
+      static_for<kRing>([&](auto T) { ring[decltype(T)::value] = load(T); });
+      static_for<kSteps>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        constexpr int kt = i % kKt, dc = i / kKt;
+        lgkm_wait<(kSteps - 1 - i < kRing - 1 ? kSteps - 1 - i : kRing - 1)>(ring[i % kRing]);
+        if constexpr (dc == 0)
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], floatx16_t{}, 0, 0, 0);
+        else
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], qreg[dc], s[kt], 0, 0, 0);
+        if constexpr (i + kRing < kSteps) ring[i % kRing] = load(std::integral_constant<int, i + kRing>{});
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     }
 #pragma unroll
     for (int kt = 0; kt < kKt; ++kt)
@@ -210,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
       __syncthreads();
       if (it + 1 < n_kv) issue((it + 1) & 1, (it + 1) * kBN, false);
       floatx16_t s[kKt];
-      scores(smem + (it & 1) * kBufBytes, it * kBN, s);
+      scores((it & 1) * kBufBytes, it * kBN, s);
       f(it * kBN, s);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -400,7 +414,7 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
     kv_cur = kv_nxt;
     const int boff = (it & 1) * kBufBytes;
     floatx16_t s[kKt];
-    scores(smem + boff, kv0, s);
+    scores(boff, kv0, s);
     bf16x8_t pb[kKt][2];
 #pragma unroll
     for (int kt = 0; kt < kKt; ++kt)
