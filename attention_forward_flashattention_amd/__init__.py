@@ -12,6 +12,8 @@ import math
 import os
 from typing import Optional, Tuple
 
+from . import build as _build
+
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libattn_fwd.so")
 
@@ -96,8 +98,21 @@ def load_library(path: str = LIB_PATH):
         lib.attn_status_str.argtypes = [ctypes.c_int]
         lib.attn_version.restype = ctypes.c_int
         lib.attn_version.argtypes = []
+        lib.attn_source_sha.restype = ctypes.c_char_p
+        lib.attn_source_sha.argtypes = []
+        built = lib.attn_source_sha().decode()
+        if path == LIB_PATH and os.path.isdir(_build.CSRC):
+            tree = _build.source_sha()
+            if built != tree:
+                raise RuntimeError(f"{path} was built from other sources (library {built}, sources here {tree}): "
+                                   "rebuild it with `python -m attention_forward_flashattention_amd.build`")
         _lib = lib
     return _lib
+
+
+def source_sha() -> str:
+    """sha256[:16] of the sources the loaded library was built from (``attn_source_sha``)."""
+    return load_library().attn_source_sha().decode()
 
 
 def status_str(status: int) -> str:
@@ -124,6 +139,80 @@ def _stream_handle(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+# ---------------------------------------------------------------------------
+# Shape checks.  The C layer sees only the descriptors built here (sizes taken
+# from q), so every tensor the kernels index is checked against the shape
+# derived from q, k and cu_seqlens before any descriptor is built: an
+# undersized buffer would otherwise be read or written out of bounds.
+# ---------------------------------------------------------------------------
+def _shape(t):
+    return tuple(int(x) for x in t.shape)
+
+
+def _need_shape(name: str, t, shape) -> None:
+    if _shape(t) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {_shape(t)}")
+
+
+def _need(name: str, t, dtype, device: bool = True, contiguous: bool = False) -> None:
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _problem(q, k, v, cu_seqlens, max_seqlen):
+    """(packed, batch, seqlen, hq, hkv, d) from q, k, v and cu_seqlens; checks that
+    k and v match q in every size but heads, and each other exactly."""
+    packed = cu_seqlens is not None
+    if packed:
+        if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+            raise ValueError("packed q, k, v must be [T, H, D]")
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be a 1-d tensor [batch + 1]")
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with cu_seqlens")
+        batch, seqlen = int(cu_seqlens.numel()) - 1, int(max_seqlen)
+    else:
+        if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+            raise ValueError("q, k, v must be [B, S, H, D]")
+        batch, seqlen = int(q.shape[0]), int(q.shape[1])
+    hq, d = int(q.shape[-2]), int(q.shape[-1])
+    hkv = int(k.shape[-2])
+    _need_shape("k", k, _shape(q)[:-2] + (hkv, d))
+    _need_shape("v", v, _shape(k))
+    return packed, batch, seqlen, hq, hkv, d
+
+
+def _lse_shape(packed, batch, seqlen, hq, q):
+    return (hq, int(q.shape[0])) if packed else (batch, hq, seqlen)
+
+
+def _check_block_mask(mask, batch: int, hkv: int, seqlen: int) -> None:
+    """A bit-packed block mask [B|1, Hkv|1, n_qblk, words] covering ceil(S/128) query
+    blocks of ceil(S/128) KV blocks each."""
+    if mask.dim() != 4:
+        raise ValueError("block_mask must be 4-d [B|1, Hkv|1, n_qblk, words]")
+    n_qblk = (seqlen + 127) // 128
+    b0, h0, rows, words = _shape(mask)
+    if b0 not in (1, batch):
+        raise ValueError(f"block_mask dim 0 must be 1 or the batch size {batch}, got {b0}")
+    if h0 not in (1, hkv):
+        raise ValueError(f"block_mask dim 1 must be 1 or the KV head count {hkv}, got {h0}")
+    if rows < n_qblk or words < max(1, (n_qblk + 31) // 32):
+        raise ValueError(f"block_mask must hold at least {n_qblk} rows of {max(1, (n_qblk + 31) // 32)} "
+                         f"words, got {rows} x {words}")
+
+
+def _check_block_list(block_list, seqlen: int) -> None:
+    row_ptr, col_idx = block_list
+    n_qblk = (seqlen + 127) // 128
+    if row_ptr.dim() != 1 or int(row_ptr.numel()) != n_qblk + 1 or col_idx.dim() != 1:
+        raise ValueError(f"block list row_ptr must be 1-d [{n_qblk + 1}] and col_idx 1-d")
+
+
 def block_mask_descriptor(mask) -> AttnBlockMask:
     """C descriptor of a bit-packed block mask tensor.
 
@@ -142,6 +231,17 @@ def block_mask_descriptor(mask) -> AttnBlockMask:
     return AttnBlockMask(mask.data_ptr(), 128, 128, int(mask.shape[2]), int(mask.shape[3]), ss, sh)
 
 
+def _list_descriptor(block_list) -> AttnBlockList:
+    import torch
+
+    row_ptr, col_idx = block_list
+    for t in (row_ptr, col_idx):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("block list tensors must be contiguous int32 device tensors")
+    return AttnBlockList(row_ptr.data_ptr(), col_idx.data_ptr() if col_idx.numel() else row_ptr.data_ptr(),
+                         128, 128, int(row_ptr.numel()) - 1)
+
+
 def attn_fwd(q, k, v, cu_seqlens=None, causal: bool = False, scale: Optional[float] = None,
              block_list: Optional[Tuple] = None, out=None, lse=None, max_seqlen: Optional[int] = None,
              return_lse: bool = True, stream=None, block_mask=None):
@@ -152,8 +252,9 @@ def attn_fwd(q, k, v, cu_seqlens=None, causal: bool = False, scale: Optional[flo
     block_list: optional (row_ptr, col_idx) int32 device tensors, 128x128 blocks
     block_mask: optional bit-packed block mask (see ``block_mask_descriptor``);
         not together with ``block_list``
-    out: optional bf16 output like q;  lse: optional fp32 [B, Hq, S] (packed [Hq, T])
-    max_seqlen: packed form only, an upper bound on every sequence length
+    out: optional bf16 output shaped like q;  lse: optional fp32 [B, Hq, S] (packed [Hq, T])
+    max_seqlen: packed form only, an upper bound on every sequence length (the
+        kernel trusts it and the contents of cu_seqlens, which live on the device)
     Returns (out, lse) (lse None when ``return_lse`` is false and none is given).
     """
     import torch
@@ -161,48 +262,32 @@ def attn_fwd(q, k, v, cu_seqlens=None, causal: bool = False, scale: Optional[flo
     if block_list is not None and block_mask is not None:
         raise ValueError("give a block list or a block mask, not both")
     lib = load_library()
-    packed = cu_seqlens is not None
+    packed, batch, seqlen, hq, hkv, d = _problem(q, k, v, cu_seqlens, max_seqlen)
+    if out is not None:
+        _need_shape("out", out, _shape(q))
+        _need("out", out, torch.bfloat16)
+    if lse is not None:
+        _need_shape("lse", lse, _lse_shape(packed, batch, seqlen, hq, q))
+        _need("lse", lse, torch.float32, contiguous=True)
+    if block_mask is not None:
+        _check_block_mask(block_mask, batch, hkv, seqlen)
+    if block_list is not None:
+        _check_block_list(block_list, seqlen)
     if packed:
-        if q.dim() != 3:
-            raise ValueError("packed q must be [T, H, D]")
-        batch = int(cu_seqlens.numel()) - 1
-        if max_seqlen is None:
-            raise ValueError("max_seqlen is required with cu_seqlens")
-        seqlen = int(max_seqlen)
-        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
-            raise ValueError("cu_seqlens must be an int32 device tensor")
-    else:
-        if q.dim() != 4:
-            raise ValueError("q must be [B, S, H, D]")
-        batch, seqlen = int(q.shape[0]), int(q.shape[1])
+        _need("cu_seqlens", cu_seqlens, torch.int32, contiguous=True)
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda:
-            raise ValueError(f"{name} must be a bfloat16 device tensor")
-    d = int(q.shape[-1])
+        _need(name, t, torch.bfloat16)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    hq = int(q.shape[-2])
     if lse is None and return_lse:
-        if packed:
-            lse = torch.empty((hq, int(q.shape[0])), dtype=torch.float32, device=q.device)
-        else:
-            lse = torch.empty((batch, hq, seqlen), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 tensor")
+        lse = torch.empty(_lse_shape(packed, batch, seqlen, hq, q), dtype=torch.float32, device=q.device)
     dq = describe(q, batch, seqlen, packed)
     dk = describe(k, batch, seqlen, packed)
     dv = describe(v, batch, seqlen, packed)
     do = describe(out, batch, seqlen, packed)
-    bl = None
-    if block_list is not None:
-        row_ptr, col_idx = block_list
-        for t in (row_ptr, col_idx):
-            if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
-                raise ValueError("block list tensors must be contiguous int32 device tensors")
-        bl = AttnBlockList(row_ptr.data_ptr(), col_idx.data_ptr() if col_idx.numel() else row_ptr.data_ptr(),
-                           128, 128, int(row_ptr.numel()) - 1)
+    bl = _list_descriptor(block_list) if block_list is not None else None
     cu_p = ctypes.c_void_p(cu_seqlens.data_ptr()) if packed else None
     lse_p = ctypes.c_void_p(lse.data_ptr()) if lse is not None else None
     if block_mask is not None:
@@ -232,26 +317,28 @@ def attn_fwd_osk(q, k, v, block_list: Tuple, tau: float, min_visit: int = 2, cau
     import torch
 
     lib = load_library()
-    if q.dim() != 4:
-        raise ValueError("q must be [1, S, H, D]")
+    _, batch, seqlen, hq, _, d = _problem(q, k, v, None, None)
+    _check_block_list(block_list, seqlen)
+    n_qblk = (seqlen + 127) // 128
+    if out is not None:
+        _need_shape("out", out, _shape(q))
+        _need("out", out, torch.bfloat16)
+    if lse is not None:
+        _need_shape("lse", lse, (batch, hq, seqlen))
+        _need("lse", lse, torch.float32, contiguous=True)
+    if visited is not None:
+        _need_shape("visited", visited, (hq, n_qblk))
+        _need("visited", visited, torch.int32, contiguous=True)
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda:
-            raise ValueError(f"{name} must be a bfloat16 device tensor")
-    batch, seqlen, hq, d = (int(x) for x in q.shape)
+        _need(name, t, torch.bfloat16)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out = torch.empty_like(q) if out is None else out
     if lse is None:
         lse = torch.empty((batch, hq, seqlen), dtype=torch.float32, device=q.device)
-    row_ptr, col_idx = block_list
-    for t in (row_ptr, col_idx):
-        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("block list tensors must be contiguous int32 device tensors")
-    n_qblk = int(row_ptr.numel()) - 1
     if visited is None:
         visited = torch.empty((hq, n_qblk), dtype=torch.int32, device=q.device)
-    bl = AttnBlockList(row_ptr.data_ptr(), col_idx.data_ptr() if col_idx.numel() else row_ptr.data_ptr(),
-                       128, 128, n_qblk)
+    bl = _list_descriptor(block_list)
     dq, dk, dv, do = (describe(t, batch, seqlen, False) for t in (q, k, v, out))
     st = lib.attn_fwd_osk(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(bool(causal)), float(scale),
                           ctypes.byref(bl), float(tau), int(min_visit), ctypes.byref(do),
@@ -274,12 +361,12 @@ def attn_entmax_fwd(q, k, v, alpha: float, causal: bool = False, scale: Optional
     import torch
 
     lib = load_library()
-    if q.dim() != 4:
-        raise ValueError("q must be [B, S, H, D]")
+    _, batch, seqlen, hq, _, d = _problem(q, k, v, None, None)
+    if out is not None:
+        _need_shape("out", out, _shape(q))
+        _need("out", out, torch.bfloat16)
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda:
-            raise ValueError(f"{name} must be a bfloat16 device tensor")
-    batch, seqlen, hq, d = (int(x) for x in q.shape)
+        _need(name, t, torch.bfloat16)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out = torch.empty_like(q) if out is None else out
@@ -305,6 +392,38 @@ def attn_entmax_fwd(q, k, v, alpha: float, causal: bool = False, scale: Optional
     return res
 
 
+def _bwd_prepare(q, k, v, out, dout, lse, cu_seqlens, max_seqlen, block_mask, dq, dk, dv, scale):
+    """Shape and dtype checks of the backward's tensors; returns the descriptors, the
+    problem sizes and the (possibly allocated) gradient tensors."""
+    import torch
+
+    packed, batch, seqlen, hq, hkv, d = _problem(q, k, v, cu_seqlens, max_seqlen)
+    _need_shape("out", out, _shape(q))
+    _need_shape("dout", dout, _shape(q))
+    _need_shape("lse", lse, _lse_shape(packed, batch, seqlen, hq, q))
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is not None:
+            _need_shape(name, t, _shape(like))
+    if block_mask is not None:
+        _check_block_mask(block_mask, batch, hkv, seqlen)
+    if packed:
+        _need("cu_seqlens", cu_seqlens, torch.int32, contiguous=True)
+    _need("lse", lse, torch.float32, contiguous=True)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        if t is not None:
+            _need(name, t, torch.bfloat16)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    descs = [describe(t, batch, seqlen, packed) for t in (q, k, v, out, dout, dq, dk, dv)]
+    bm = block_mask_descriptor(block_mask) if block_mask is not None else None
+    cu_p = ctypes.c_void_p(cu_seqlens.data_ptr()) if packed else None
+    return descs, bm, cu_p, float(scale), (dq, dk, dv)
+
+
 def attn_bwd(q, k, v, out, dout, lse, cu_seqlens=None, causal: bool = False,
              scale: Optional[float] = None, max_seqlen: Optional[int] = None, block_mask=None,
              dq=None, dk=None, dv=None, workspace=None, stream=None):
@@ -319,40 +438,19 @@ def attn_bwd(q, k, v, out, dout, lse, cu_seqlens=None, causal: bool = False,
     import torch
 
     lib = load_library()
-    packed = cu_seqlens is not None
-    if packed:
-        if q.dim() != 3:
-            raise ValueError("packed q must be [T, H, D]")
-        if max_seqlen is None:
-            raise ValueError("max_seqlen is required with cu_seqlens")
-        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
-            raise ValueError("cu_seqlens must be an int32 device tensor")
-        batch, seqlen = int(cu_seqlens.numel()) - 1, int(max_seqlen)
-    else:
-        if q.dim() != 4:
-            raise ValueError("q must be [B, S, H, D]")
-        batch, seqlen = int(q.shape[0]), int(q.shape[1])
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda:
-            raise ValueError(f"{name} must be a bfloat16 device tensor")
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous float32 device tensor")
-    if scale is None:
-        scale = 1.0 / math.sqrt(int(q.shape[-1]))
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    descs = [describe(t, batch, seqlen, packed) for t in (q, k, v, out, dout, dq, dk, dv)]
+    descs, bm, cu_p, scale, grads = _bwd_prepare(q, k, v, out, dout, lse, cu_seqlens, max_seqlen, block_mask,
+                                                 dq, dk, dv, scale)
     need = int(lib.attn_bwd_workspace_size(ctypes.byref(descs[0])))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
-    bm = block_mask_descriptor(block_mask) if block_mask is not None else None
-    st = lib.attn_bwd(*(ctypes.byref(d) for d in descs[:5]), ctypes.c_void_p(lse.data_ptr()),
-                      ctypes.c_void_p(cu_seqlens.data_ptr()) if packed else None,
-                      int(bool(causal)), float(scale), ctypes.byref(bm) if bm is not None else None,
+    st = lib.attn_bwd(*(ctypes.byref(d) for d in descs[:5]), ctypes.c_void_p(lse.data_ptr()), cu_p,
+                      int(bool(causal)), scale, ctypes.byref(bm) if bm is not None else None,
                       *(ctypes.byref(d) for d in descs[5:]), ctypes.c_void_p(workspace.data_ptr()),
                       ws_bytes, ctypes.c_void_p(_stream_handle(stream)))
     if st != ATTN_OK:
         raise AttnError(st, status_str(st), "attn_bwd")
-    return dq, dk, dv
+    return grads
+

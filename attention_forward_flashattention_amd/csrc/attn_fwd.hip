@@ -58,7 +58,7 @@ struct Params {
   int batch, seqlen, hq, group;
   int n_tiles;   // query tiles per (sequence, head) = ceil(seqlen / BM)
   int n_units;   // batch * hq
-  int xcd_remap; // 1 when n_units % 8 == 0
+  int xcd_remap; // 1 when n_units % (8 * group) == 0 (whole GQA groups dealt over the 8 XCDs)
   float c;       // scale * log2(e)
 };
 
@@ -1037,4 +1037,9 @@ extern "C" const char *attn_status_str(int status) {
   }
 }
 
-extern "C" int attn_version(void) { return 300; }
+extern "C" int attn_version(void) { return 301; }
+
+#ifndef ATTN_SOURCE_SHA
+#define ATTN_SOURCE_SHA "unknown"
+#endif
+extern "C" const char *attn_source_sha(void) { return ATTN_SOURCE_SHA; }

@@ -261,6 +261,11 @@ const char *attn_status_str(int status);
 /* Library ABI version: major*10000 + minor*100 + patch. */
 int attn_version(void);
 
+/* sha256[:16] (hex) of the compile flags and sources the library was built
+ * from, fixed at build time; lets a caller detect a library built from other
+ * sources than the headers and kernels beside it. */
+const char *attn_source_sha(void);
+
 #ifdef __cplusplus
 }
 #endif

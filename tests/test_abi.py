@@ -26,11 +26,11 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_validate", "attn_bwd_workspace_size",
-                                    "attn_entmax_fwd", "attn_entmax_fwd_validate", "attn_fwd",
-                                    "attn_fwd_mask", "attn_fwd_mask_validate", "attn_fwd_osk",
-                                    "attn_fwd_osk_validate", "attn_fwd_validate", "attn_status_str",
-                                    "attn_version"]
+    assert declared_functions() == ["attn_bwd", "attn_bwd_validate",
+                                    "attn_bwd_workspace_size", "attn_entmax_fwd", "attn_entmax_fwd_validate",
+                                    "attn_fwd", "attn_fwd_mask", "attn_fwd_mask_validate", "attn_fwd_osk",
+                                    "attn_fwd_osk_validate", "attn_fwd_validate", "attn_source_sha",
+                                    "attn_status_str", "attn_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -41,8 +41,17 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.attn_version() == 300
+    assert lib.attn_version() == 301
     assert attn.status_str(0) == "ok" and attn.status_str(-3) == "kernel launch failed"
+
+
+def test_library_was_built_from_these_sources():
+    """The library carries the hash of the sources it was compiled from; it must be
+    the hash of the sources in this tree (load_library refuses a stale library)."""
+    from attention_forward_flashattention_amd import build
+
+    assert attn.source_sha() == build.source_sha()
+    assert len(attn.source_sha()) == 16 and attn.source_sha() != "unknown"
 
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation only reads the descriptors
@@ -264,3 +273,70 @@ def test_entmax_argument_checks():
     s = 128 * 33                                        # 33 blocks need 2 mask words
     assert val(words=1, qd=desc(b=1, s=s, h=4), kd=desc(b=1, s=s, h=2)) == -1
     assert val(words=2, qd=desc(b=1, s=s, h=4), kd=desc(b=1, s=s, h=2)) == 0
+
+
+# ---------------------------------------------------------------------------
+# Binding shape checks: every tensor the kernels index is checked against the
+# shape derived from q, k and cu_seqlens before any descriptor reaches the C
+# layer (host tensors suffice: the shape checks come before the device checks).
+# ---------------------------------------------------------------------------
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_rejects_mismatched_kv():
+    q = _t(2, 64, 4, 64)
+    with pytest.raises(ValueError, match="k must have shape"):
+        attn.attn_fwd(q, _t(2, 32, 2, 64), _t(2, 32, 2, 64))          # k shorter than q
+    with pytest.raises(ValueError, match="v must have shape"):
+        attn.attn_fwd(q, _t(2, 64, 2, 64), _t(2, 64, 1, 64))          # v heads differ from k
+    with pytest.raises(ValueError, match="k must have shape"):
+        attn.attn_fwd(_t(100, 4, 64), _t(90, 2, 64), _t(90, 2, 64), cu_seqlens=_t(3, dtype=None), max_seqlen=64)
+
+
+def test_binding_rejects_undersized_outputs():
+    import torch
+    q, k = _t(2, 64, 4, 64), _t(2, 64, 2, 64)
+    with pytest.raises(ValueError, match="out must have shape"):
+        attn.attn_fwd(q, k, k, out=_t(2, 64, 2, 64))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        attn.attn_fwd(q, k, k, lse=torch.zeros((2, 4, 63)))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        attn.attn_fwd(_t(100, 4, 64), _t(100, 2, 64), _t(100, 2, 64), cu_seqlens=torch.zeros(3, dtype=torch.int32),
+                      max_seqlen=64, lse=torch.zeros((4, 99)))
+    with pytest.raises(ValueError, match="visited must have shape"):
+        attn.attn_fwd_osk(_t(1, 256, 4, 64), _t(1, 256, 2, 64), _t(1, 256, 2, 64),
+                          (torch.zeros(3, dtype=torch.int32), torch.zeros(4, dtype=torch.int32)), 0.1,
+                          visited=torch.zeros((4, 1), dtype=torch.int32))
+    with pytest.raises(ValueError, match="row_ptr"):
+        attn.attn_fwd(_t(1, 256, 4, 64), _t(1, 256, 2, 64), _t(1, 256, 2, 64),
+                      block_list=(torch.zeros(2, dtype=torch.int32), torch.zeros(4, dtype=torch.int32)))
+
+
+def test_binding_rejects_bad_block_masks():
+    import torch
+    q, k = _t(2, 300, 4, 64), _t(2, 300, 2, 64)
+    ok = torch.zeros((1, 2, 3, 1), dtype=torch.int32)
+    for bad, what in ((torch.zeros((3, 1, 3, 1), dtype=torch.int32), "dim 0"),
+                      (torch.zeros((1, 4, 3, 1), dtype=torch.int32), "dim 1"),
+                      (torch.zeros((1, 1, 2, 1), dtype=torch.int32), "rows"),
+                      (torch.zeros((2, 2, 3), dtype=torch.int32), "4-d")):
+        with pytest.raises(ValueError, match=what):
+            attn.attn_fwd(q, k, k, causal=True, block_mask=bad)
+    with pytest.raises(ValueError, match="device"):      # a valid shape reaches the device check
+        attn.attn_fwd(q, k, k, causal=True, block_mask=ok)
+
+
+def test_binding_rejects_bad_backward_tensors():
+    import torch
+    q, k = _t(2, 64, 4, 64), _t(2, 64, 2, 64)
+    lse = torch.zeros((2, 4, 64))
+    with pytest.raises(ValueError, match="dout must have shape"):
+        attn.attn_bwd(q, k, k, q, _t(2, 64, 4, 32), lse)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        attn.attn_bwd(q, k, k, q, q, torch.zeros((2, 4, 32)))
+    with pytest.raises(ValueError, match="dk must have shape"):
+        attn.attn_bwd(q, k, k, q, q, lse, dk=_t(2, 64, 4, 64))
+    with pytest.raises(ValueError, match="dq must have shape"):
+        attn.attn_bwd(q, k, k, q, q, lse, dq=_t(2, 32, 4, 64))
