@@ -16,9 +16,21 @@ LSE_MAX_ABS = 1e-3
 O_REL_RMS = 1e-2   # ||O - O_ref||_2 / ||O_ref||_2, catches errors the loose max-abs bound can hide
 
 
+def check_inputs(w: W.Workload) -> None:
+    """Refuse a workload whose Q, K or V holds a non-finite value: every parity bound
+    assumes finite inputs (an infinite score would make both sides' NaN agree or not
+    by accident)."""
+    for name, a in (("q", w.q), ("k", w.k), ("v", w.v)):
+        x = W.bf16_bits_to_f32(a)
+        if not np.all(np.isfinite(x)):
+            raise ValueError(f"{w.name}: non-finite values in {name} ({int(np.sum(~np.isfinite(x)))} elements)")
+
+
 def to_device(w: W.Workload, layout: str = "bshd"):
     """Device tensors for a workload: q, k, v (bf16), cu_seqlens, and the keyword
-    arguments that carry its block sparsity ({} dense, block_list or block_mask)."""
+    arguments that carry its block sparsity ({} dense, block_list or block_mask).
+    Non-finite inputs are refused (``check_inputs``)."""
+    check_inputs(w)
     import torch
 
     dev = torch.device("cuda:0")
@@ -78,7 +90,9 @@ def sample_tokens(w: W.Workload, per_seq: int = 48, seed: int = 0) -> np.ndarray
 
 def compare(o_gpu, l_gpu, o_ref, l_ref, label=""):
     """Check the tolerances; returns a dict of error statistics."""
+    assert o_gpu.shape == o_ref.shape and l_gpu.shape == l_ref.shape, (label, o_gpu.shape, o_ref.shape)
     assert np.all(np.isfinite(o_gpu)), f"{label}: non-finite O"
+    assert not np.any(np.isnan(l_gpu)) and not np.any(l_gpu == np.inf), f"{label}: NaN or +inf in LSE"
     fin = np.isfinite(l_ref)
     assert np.array_equal(np.isfinite(l_gpu), fin), f"{label}: LSE finiteness differs"
     assert np.all(l_gpu[~fin] == l_ref[~fin]), f"{label}: empty rows must give -inf"
@@ -96,15 +110,44 @@ def compare(o_gpu, l_gpu, o_ref, l_ref, label=""):
     return stats
 
 
+def oracle_threads() -> int:
+    """Threads for the oracle in tests (the oracle's own default: the CPUs this process
+    may run on, at most 16)."""
+    import oracle
+    return oracle.default_threads()
+
+
 def check_workload(w: W.Workload, rows=None, layout: str = "bshd", nthreads: int = 0):
     """GPU vs oracle on all rows (rows=None) or on the given packed token ids."""
     import oracle
 
     o, l = run_gpu(w, layout)
-    o_ref, l_ref = oracle.run_workload(w, rows=rows, nthreads=nthreads)
+    o_ref, l_ref = oracle.run_workload(w, rows=rows, nthreads=nthreads or oracle_threads())
     if rows is not None:
         o, l = o[rows], l[rows]
     return compare(o, l, o_ref, l_ref, w.name)
+
+
+def one_head_per_kv_head(w: W.Workload):
+    """Query heads c*g + (c mod g) for each KV head c: one head of every GQA group,
+    each at a different position within its group."""
+    g = w.hq // w.hkv
+    return [c * g + (c % g) for c in range(w.hkv)]
+
+
+def oracle_heads(w: W.Workload, heads, nthreads: int = 0):
+    """The oracle on every row of the given query heads (at most one per KV head):
+    O [T, len(heads), D], LSE [T, len(heads)]."""
+    import oracle
+
+    g = w.hq // w.hkv
+    kvh = [h // g for h in heads]
+    assert len(set(kvh)) == len(kvh), "one query head per KV head"
+    q, k, v = w.packed_views()
+    f = lambda a: W.bf16_bits_to_f32(a).astype(np.float64)
+    return oracle.attn_fwd(f(q[:, heads]), f(k[:, kvh]), f(v[:, kvh]), w.cu_seqlens_or_fixed(), w.causal,
+                           w.scale, w.row_ptr, w.col_idx, 128, None, nthreads or oracle_threads(),
+                           block_mask=None if w.block_mask is None else w.block_mask[:, kvh])
 
 
 # ---------------------------------------------------------------------------
@@ -166,6 +209,7 @@ def compare_grads(got, ref, label=""):
     """Check the gradient tolerances on (dq, dk, dv); returns the error statistics."""
     stats = {}
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        assert g.shape == r.shape, (label, name, g.shape, r.shape)
         assert np.all(np.isfinite(g)), f"{label}: non-finite {name}"
         nrm = np.linalg.norm(r)
         err = np.abs(g - r)
