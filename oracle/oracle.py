@@ -78,8 +78,21 @@ def _load():
     return _lib
 
 
+MAX_THREADS = 16   # a GPU machine grants one GPU's jobs a share of 16 host CPUs, whatever it reports online
+
+
 def default_threads() -> int:
-    return int(_load().oracle_default_threads())
+    """Threads the oracle uses when asked for 0: the CPUs this process may run on
+    (its affinity mask), at most MAX_THREADS."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = int(_load().oracle_default_threads())
+    return max(1, min(MAX_THREADS, n))
+
+
+def _threads(n: int) -> int:
+    return int(n) if n and n > 0 else default_threads()
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -129,13 +142,13 @@ def attn_fwd(q, k, v, cu_seqlens, causal: bool, scale: float, row_ptr=None, col_
         rc = _load().oracle_attn_fwd_mask(
             _ptr(q), _ptr(k), _ptr(v), _ptr(cu), n_seqs, hq, hkv, d, int(bool(causal)),
             float(scale), _ptr(m), ss, sh, words, n_qblk, int(block), _ptr(rows_a),
-            0 if rows_a is None else len(rows_a), _ptr(out), _ptr(lse), _ptr(psum), int(nthreads))
+            0 if rows_a is None else len(rows_a), _ptr(out), _ptr(lse), _ptr(psum), _threads(nthreads))
     else:
         rc = _load().oracle_attn_fwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(cu), n_seqs, hq, hkv, d, int(bool(causal)),
             float(scale), _ptr(rp), _ptr(ci), 0 if rp is None else len(rp) - 1, int(block),
             _ptr(rows_a), 0 if rows_a is None else len(rows_a), _ptr(out), _ptr(lse), _ptr(psum),
-            int(nthreads))
+            _threads(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_attn_fwd failed with code {rc}")
     if with_psum:
@@ -180,7 +193,7 @@ def attn_bwd(q, k, v, dout, cu_seqlens, causal: bool, scale: float, block_mask=N
     dv = np.zeros_like(v)
     rc = _load().oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(cu), n_seqs, hq, hkv, d,
                                  int(bool(causal)), float(scale), _ptr(m), ss, sh, words, int(block),
-                                 _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads))
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _threads(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_attn_bwd failed with code {rc}")
     return dq, dk, dv
@@ -217,7 +230,7 @@ def attn_fwd_osk(q, k, v, causal: bool, scale: float, row_ptr, col_idx, tau: flo
     rc = _load().oracle_attn_fwd_osk(_ptr(q), _ptr(k), _ptr(v), t, hq, hkv, d, int(bool(causal)), float(scale),
                                      _ptr(rp), _ptr(ci), n_qblk, int(block), float(tau), int(min_visit),
                                      _ptr(sel), len(sel), _ptr(out), _ptr(lse), _ptr(visited), _ptr(ratio),
-                                     int(nthreads))
+                                     _threads(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_attn_fwd_osk failed with code {rc}")
     return out, lse, visited, ratio
@@ -251,7 +264,7 @@ def entmax_fwd(q, k, v, cu_seqlens, causal: bool, scale: float, alpha: float, bi
         mask = np.zeros((n_seqs, hq, n_qblk, words), dtype=np.uint32)
     rc = _load().oracle_entmax_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), n_seqs, hq, hkv, d, int(bool(causal)),
                                    float(scale), float(alpha), int(bins), _ptr(out), _ptr(tau), _ptr(tau_h),
-                                   _ptr(mask), int(block), n_qblk, words, int(nthreads))
+                                   _ptr(mask), int(block), n_qblk, words, _threads(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_entmax_fwd failed with code {rc}")
     if with_mask:

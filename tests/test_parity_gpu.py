@@ -2,8 +2,10 @@
 
 Tolerances (bf16 I/O, fp32 accumulation): O max abs <= 2e-2, O mean abs
 <= 2e-3, LSE max abs <= 1e-3, plus a relative RMS bound on O of 1e-2.
-Small problems are compared on every output; the full-size workloads on
-sampled rows (every head of each sampled row) that the oracle computes one by
+Small problems and the dense causal MHA and GQA workloads are compared on
+every output; the packed variable-length workloads on every row of one query
+head per KV head plus every head of sampled rows; the 128K block-sparse
+workload on its 256 sampled rows (all heads), which the oracle computes one by
 one.  Structural properties (GQA = repeated MHA, packed = per-sequence, list
 = dense, run-to-run determinism) are checked bitwise where the kernel's
 arithmetic is the same.
@@ -74,13 +76,34 @@ def test_bhsd_layout_matches():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-# ---------------------------------------------------------------- full-size workloads, sampled rows
-@pytest.mark.parametrize("name", ["mha", "gqa", "varlen_d64", "varlen_d128", "varlen_d256"])
-def test_workload_sampled(name):
+# ---------------------------------------------------------------- full-size workloads, every output
+@pytest.mark.parametrize("name", ["mha", "gqa"])
+def test_workload_full(name):
+    """Every row of every head of the dense causal workloads against the oracle."""
     w = workload(name)
+    note(f"workload {name}: all {w.tokens} rows x {w.hq} heads")
+    stats = P.check_workload(w)
+    note(f"  {stats}")
+
+
+@pytest.mark.parametrize("name", ["varlen_d64", "varlen_d128", "varlen_d256"])
+def test_varlen_workload(name):
+    """Packed variable-length workloads: every row of one query head per KV head
+    (c*g + c mod g: every tile, wave and XCD slot of the schedule, and every head
+    position within a GQA group), plus every head of sampled rows (tile edges and
+    sequence ends of every sequence and random rows)."""
+    w = workload(name)
+    o, l = P.run_gpu(w)
+    heads = P.one_head_per_kv_head(w)
+    note(f"workload {name}: all {w.tokens} rows of heads {heads}")
+    o_ref, l_ref = P.oracle_heads(w, heads)
+    stats = P.compare(o[:, heads], l[:, heads], o_ref, l_ref, f"{name} heads {heads}")
+    note(f"  {stats}")
+    import oracle
     rows = P.sample_tokens(w, per_seq=48, seed=1)
     note(f"workload {name}: {len(rows)} sampled rows x {w.hq} heads")
-    stats = P.check_workload(w, rows=rows)
+    o_ref, l_ref = oracle.run_workload(w, rows=rows, nthreads=P.oracle_threads())
+    stats = P.compare(o[rows], l[rows], o_ref, l_ref, f"{name} sampled rows")
     note(f"  {stats}")
 
 
