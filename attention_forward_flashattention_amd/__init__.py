@@ -21,6 +21,8 @@ ATTN_OK = 0
 ATTN_ERR_INVALID_ARG = -1
 ATTN_ERR_UNSUPPORTED = -2
 ATTN_ERR_LAUNCH = -3
+ATTN_ERR_TOO_LARGE = -4
+ATTN_BWD_SCRATCH_BYTES = 32 << 20   # the static scratch of attn_bwd_noalloc (include/attn_bwd.h)
 
 
 class AttnTensor(ctypes.Structure):
@@ -92,6 +94,8 @@ def load_library(path: str = LIB_PATH):
         lib.attn_bwd_validate.restype = ctypes.c_int
         lib.attn_bwd_validate.argtypes = [T, T, T, T, T, P, P, ctypes.c_int, ctypes.c_float, BM, T, T,
                                           T, P, ctypes.c_size_t]
+        lib.attn_bwd_noalloc.restype = ctypes.c_int
+        lib.attn_bwd_noalloc.argtypes = [T, T, T, T, T, P, P, ctypes.c_int, ctypes.c_float, BM, T, T, T, P]
         lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
         lib.attn_bwd_workspace_size.argtypes = [T]
         lib.attn_status_str.restype = ctypes.c_char_p
@@ -454,3 +458,23 @@ def attn_bwd(q, k, v, out, dout, lse, cu_seqlens=None, causal: bool = False,
         raise AttnError(st, status_str(st), "attn_bwd")
     return grads
 
+
+def attn_bwd_noalloc(q, k, v, out, dout, lse, dq, dk, dv, cu_seqlens=None, causal: bool = False,
+                     scale: Optional[float] = None, max_seqlen: Optional[int] = None, block_mask=None,
+                     stream=None):
+    """``attn_bwd`` without a workspace: the library's static per-device scratch holds
+    the per-row values instead, so neither this call nor the library allocates (the
+    caller passes dq, dk, dv).  Problems needing more than ``ATTN_BWD_SCRATCH_BYTES`` of
+    workspace raise ``AttnError`` with status ``ATTN_ERR_TOO_LARGE``; calls that overlap
+    on one GPU race on the shared scratch."""
+    lib = load_library()
+    if dq is None or dk is None or dv is None:
+        raise ValueError("attn_bwd_noalloc writes into caller-provided dq, dk, dv")
+    descs, bm, cu_p, scale, grads = _bwd_prepare(q, k, v, out, dout, lse, cu_seqlens, max_seqlen, block_mask,
+                                                 dq, dk, dv, scale)
+    st = lib.attn_bwd_noalloc(*(ctypes.byref(d) for d in descs[:5]), ctypes.c_void_p(lse.data_ptr()), cu_p,
+                              int(bool(causal)), scale, ctypes.byref(bm) if bm is not None else None,
+                              *(ctypes.byref(d) for d in descs[5:]), ctypes.c_void_p(_stream_handle(stream)))
+    if st != ATTN_OK:
+        raise AttnError(st, status_str(st), "attn_bwd_noalloc")
+    return grads

@@ -31,6 +31,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "attn_bwd.h"
 #include "attn_common.h"
 
@@ -899,11 +901,11 @@ size_t ws_entries(const attn_tensor_t *q) {
   return (size_t)q->heads * (size_t)q->batch * (size_t)q->seqlen;
 }
 
-int validate_bwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
-                 const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,
-                 const int32_t *cu, int causal, float scale, const attn_block_mask_t *mask,
-                 const attn_tensor_t *dq, const attn_tensor_t *dk, const attn_tensor_t *dv,
-                 const void *ws, size_t ws_bytes) {
+// Argument checks of attn_bwd other than the workspace.
+int validate_bwd_args(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                      const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,
+                      const int32_t *cu, int causal, float scale, const attn_block_mask_t *mask,
+                      const attn_tensor_t *dq, const attn_tensor_t *dk, const attn_tensor_t *dv) {
   if (!dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
   // q, k, v, out; then dout and dq like out, dk and dv like k and v
   int st = mask ? attn_fwd_mask_validate(q, k, v, cu, causal, scale, mask, out)
@@ -917,10 +919,22 @@ int validate_bwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tens
   if (q->head_dim == 256) return ATTN_ERR_UNSUPPORTED;
   const bool empty = q->batch == 0 || q->seqlen == 0;
   if (empty) return ATTN_OK;
-  if (!lse || !ws) return ATTN_ERR_INVALID_ARG;
+  if (!lse) return ATTN_ERR_INVALID_ARG;
+  if (mask && (q->seqlen + kListBlock - 1) / kListBlock > kMaxQBlocks) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+int validate_bwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                 const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,
+                 const int32_t *cu, int causal, float scale, const attn_block_mask_t *mask,
+                 const attn_tensor_t *dq, const attn_tensor_t *dk, const attn_tensor_t *dv,
+                 const void *ws, size_t ws_bytes) {
+  const int st = validate_bwd_args(q, k, v, out, dout, lse, cu, causal, scale, mask, dq, dk, dv);
+  if (st != ATTN_OK) return st;
+  if (q->batch == 0 || q->seqlen == 0) return ATTN_OK;
+  if (!ws) return ATTN_ERR_INVALID_ARG;
   if (ws_bytes < 2 * sizeof(float) * ws_entries(q)) return ATTN_ERR_INVALID_ARG;
   if (((uintptr_t)ws & 15u) != 0) return ATTN_ERR_UNSUPPORTED;
-  if (mask && (q->seqlen + kListBlock - 1) / kListBlock > kMaxQBlocks) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -977,16 +991,15 @@ extern "C" int attn_bwd_validate(const attn_tensor_t *q, const attn_tensor_t *k,
                       workspace, workspace_bytes);
 }
 
-extern "C" int attn_bwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
-                        const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,
-                        const int32_t *cu_seqlens, int causal, float scale,
-                        const attn_block_mask_t *mask, attn_tensor_t *dq, attn_tensor_t *dk,
-                        attn_tensor_t *dv, void *workspace, size_t workspace_bytes,
-                        void *stream) {
-  const int st = validate_bwd(q, k, v, out, dout, lse, cu_seqlens, causal, scale, mask, dq, dk,
-                              dv, workspace, workspace_bytes);
-  if (st != ATTN_OK) return st;
-  if (q->batch == 0 || q->seqlen == 0) return ATTN_OK;
+namespace {
+
+// Both kernels of the backward, with the per-row workspace at `workspace`
+// (already validated).
+int run_bwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+            const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,
+            const int32_t *cu_seqlens, int causal, float scale, const attn_block_mask_t *mask,
+            attn_tensor_t *dq, attn_tensor_t *dk, attn_tensor_t *dv, void *workspace,
+            void *stream) {
   BwdParams p;
   p.q = static_cast<const uint16_t *>(q->data);
   p.k = static_cast<const uint16_t *>(k->data);
@@ -1023,4 +1036,67 @@ extern "C" int attn_bwd(const attn_tensor_t *q, const attn_tensor_t *k, const at
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (q->head_dim == 64) return launch_d<64>(p, causal != 0, mask != nullptr, s);
   return launch_d<128>(p, causal != 0, mask != nullptr, s);
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of attn_bwd_noalloc: the per-row workspace of the backward
+// in a fixed device array, for callers that cannot allocate.  In host code
+// `scratch` names a host-side stand-in, not device memory, so its device
+// address is taken once per device with hipGetSymbolAddress (each device
+// holds its own copy) and only that address is handed to the kernels.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[ATTN_BWD_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of the current device's scratch (taken on the first call on
+// that device), or null if it cannot be obtained.
+void *scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int attn_bwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                        const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,
+                        const int32_t *cu_seqlens, int causal, float scale,
+                        const attn_block_mask_t *mask, attn_tensor_t *dq, attn_tensor_t *dk,
+                        attn_tensor_t *dv, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  const int st = validate_bwd(q, k, v, out, dout, lse, cu_seqlens, causal, scale, mask, dq, dk,
+                              dv, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  if (q->batch == 0 || q->seqlen == 0) return ATTN_OK;
+  return run_bwd(q, k, v, out, dout, lse, cu_seqlens, causal, scale, mask, dq, dk, dv, workspace,
+                 stream);
+}
+
+extern "C" int attn_bwd_noalloc(const attn_tensor_t *q, const attn_tensor_t *k,
+                                const attn_tensor_t *v, const attn_tensor_t *out,
+                                const attn_tensor_t *dout, const float *lse,
+                                const int32_t *cu_seqlens, int causal, float scale,
+                                const attn_block_mask_t *mask, attn_tensor_t *dq,
+                                attn_tensor_t *dk, attn_tensor_t *dv, void *stream) {
+  const int st = validate_bwd_args(q, k, v, out, dout, lse, cu_seqlens, causal, scale, mask, dq,
+                                   dk, dv);
+  if (st != ATTN_OK) return st;
+  if (q->batch == 0 || q->seqlen == 0) return ATTN_OK;
+  if (2 * sizeof(float) * ws_entries(q) > (size_t)ATTN_BWD_SCRATCH_BYTES) return ATTN_ERR_TOO_LARGE;
+  void *ws = scratch_address();
+  if (!ws) return ATTN_ERR_LAUNCH;
+  return run_bwd(q, k, v, out, dout, lse, cu_seqlens, causal, scale, mask, dq, dk, dv, ws, stream);
 }

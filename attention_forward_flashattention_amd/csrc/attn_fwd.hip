@@ -1033,6 +1033,7 @@ extern "C" const char *attn_status_str(int status) {
     case ATTN_ERR_INVALID_ARG: return "invalid argument";
     case ATTN_ERR_UNSUPPORTED: return "unsupported argument combination";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_TOO_LARGE: return "problem exceeds the library's static scratch buffer";
     default: return "unknown status";
   }
 }

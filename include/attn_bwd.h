@@ -82,6 +82,31 @@ int attn_bwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t
              attn_tensor_t *dq, attn_tensor_t *dk, attn_tensor_t *dv, void *workspace,
              size_t workspace_bytes, void *stream);
 
+/*
+ * attn_bwd_noalloc — attn_bwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation and arguments without the
+ * workspace, which lives instead in a static device array of
+ * ATTN_BWD_SCRATCH_BYTES inside the library (one per GPU, held until the
+ * process ends).  The call allocates nothing.  The problem must fit it:
+ * attn_bwd_workspace_size(q) <= ATTN_BWD_SCRATCH_BYTES (8 bytes per query
+ * row and head: e.g. 32 heads x 131072 rows), else ATTN_ERR_TOO_LARGE.  The
+ * scratch of the current device (hipGetDevice) is used, so `stream` must
+ * belong to that device.  Every call on one GPU shares its scratch and each
+ * call overwrites what it needs before reading it, so nothing carries over
+ * between calls; calls that overlap on one GPU (other streams, other host
+ * threads) race on it and must be serialised by the caller.
+ * Returns what attn_bwd returns (the workspace checks aside), or
+ * ATTN_ERR_TOO_LARGE, or ATTN_ERR_LAUNCH if the scratch's device address
+ * cannot be obtained.
+ */
+#define ATTN_BWD_SCRATCH_BYTES (32u << 20)
+int attn_bwd_noalloc(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
+                     const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,
+                     const int32_t *cu_seqlens, int causal, float scale,
+                     const attn_block_mask_t *mask, attn_tensor_t *dq, attn_tensor_t *dk,
+                     attn_tensor_t *dv, void *stream);
+
 /* The argument checks of attn_bwd alone: host code only, no HIP call. */
 int attn_bwd_validate(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
                       const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,

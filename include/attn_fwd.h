@@ -100,7 +100,8 @@ enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = -1, /* arguments contradict each other or are null */
   ATTN_ERR_UNSUPPORTED = -2, /* valid, but not implemented by this library   */
-  ATTN_ERR_LAUNCH = -3       /* the HIP kernel launch itself failed          */
+  ATTN_ERR_LAUNCH = -3,      /* the HIP kernel launch itself failed          */
+  ATTN_ERR_TOO_LARGE = -4    /* the problem exceeds a fixed-size static buffer */
 };
 
 /*

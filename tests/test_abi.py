@@ -26,7 +26,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_validate",
+    assert declared_functions() == ["attn_bwd", "attn_bwd_noalloc", "attn_bwd_validate",
                                     "attn_bwd_workspace_size", "attn_entmax_fwd", "attn_entmax_fwd_validate",
                                     "attn_fwd", "attn_fwd_mask", "attn_fwd_mask_validate", "attn_fwd_osk",
                                     "attn_fwd_osk_validate", "attn_fwd_validate", "attn_source_sha",
