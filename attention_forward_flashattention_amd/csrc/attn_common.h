@@ -151,6 +151,13 @@ __device__ __forceinline__ void lgkm_wait(bf16x8_t &x) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "i"(N));
 }
 
+// Sum of x over the 64 lanes of a wave (every lane gets the sum).
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
 __device__ __forceinline__ uint4_t ld_global16(const uint16_t *p) {
   return *reinterpret_cast<const uint4_t *>(p);
 }

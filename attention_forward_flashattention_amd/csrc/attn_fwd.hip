@@ -57,8 +57,9 @@ struct Params {
   int32_t *visited;        // ordered skipping: entries visited per (query head, query block), or null
   int batch, seqlen, hq, group;
   int n_tiles;   // query tiles per (sequence, head) = ceil(seqlen / BM)
-  int n_units;   // batch * hq
-  int xcd_remap; // 1 when n_units % (8 * group) == 0 (whole GQA groups dealt over the 8 XCDs)
+  int n_units;   // batch * (hq / query heads per workgroup)
+  int unit_group;  // units per KV head (group / query heads per workgroup)
+  int xcd_remap; // 1 when n_units % (8 * unit_group) == 0 (whole GQA groups dealt over the 8 XCDs)
   float c;       // scale * log2(e)
 };
 
@@ -104,10 +105,11 @@ __device__ __forceinline__ float exp_tile(const floatx16_t (&s)[kKt], float c, f
   return rs;
 }
 
-// Decode the workgroup id into (query tile, sequence, head).  Workgroups are
-// dealt round-robin over the 8 XCDs (each with its own L2).  When the
-// (sequence, head) units split evenly, the `group` query heads that share one
-// KV head stay together and those groups are dealt round-robin over the XCDs,
+// Decode the workgroup id into (query tile, unit); a unit is one sequence and
+// one (or, for the paired block-sparse kernels, two) query heads.  Workgroups
+// are dealt round-robin over the 8 XCDs (each with its own L2).  When the
+// units split evenly, the `unit_group` units that share one KV head stay
+// together and those groups are dealt round-robin over the XCDs,
 // so every XCD gets the same mix of sequences (packed batches stay balanced)
 // and the heads that read the same K/V share one L2.  Within an XCD, causal
 // and block-list tiles are issued heaviest first.
@@ -121,7 +123,7 @@ __device__ __forceinline__ void decode_tile(const Params &p, bool heavy_first, i
     const int local = w >> 3;
     rank = local / upx;
     const int lu = local % upx;      // unit slot within this XCD
-    unit = ((lu / p.group) * 8 + xcd) * p.group + lu % p.group;
+    unit = ((lu / p.unit_group) * 8 + xcd) * p.unit_group + lu % p.unit_group;
   } else {
     rank = w / p.n_units;
     unit = w % p.n_units;
@@ -220,25 +222,14 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes + (kOwnStage ? kStageBytes : 0) + kFlagBytes];
   uint32_t *osk_flag = reinterpret_cast<uint32_t *>(smem + 2 * kBufBytes + (kOwnStage ? kStageBytes : 0));
 
-  int tile, unit;
-  decode_tile(p, CAUSAL || LIST, tile, unit);
-  const int b = unit / p.hq;
-  const int h = unit % p.hq;
-  const int kvh = h / p.group;
-
-  int64_t tok0 = 0;
-  int len = p.seqlen;
-  if (p.cu) {
-    tok0 = p.cu[b];
-    len = p.cu[b + 1] - p.cu[b];
-  }
-  const int q0 = tile * kBM;
-  if (q0 >= len) return;
-
-  const uint16_t *qg = p.q + (p.cu ? tok0 * p.q_ss : (int64_t)b * p.q_sb) + (int64_t)h * p.q_sh;
-  const uint16_t *kg = p.k + (p.cu ? tok0 * p.k_ss : (int64_t)b * p.k_sb) + (int64_t)kvh * p.k_sh;
-  const uint16_t *vg = p.v + (p.cu ? tok0 * p.v_ss : (int64_t)b * p.v_sb) + (int64_t)kvh * p.v_sh;
-  uint16_t *og = p.o + (p.cu ? tok0 * p.o_ss : (int64_t)b * p.o_sb) + (int64_t)h * p.o_sh;
+  // Query heads per workgroup: the pipelined block-list and block-mask kernels
+  // take two query heads of one GQA group, 128 rows (one query block) each;
+  // the two share the KV head and the block set, so every K/V tile staged in
+  // LDS serves both, as a 256-row dense tile does.
+  constexpr int kHpw = (LIST && !OSK && C::NW == 8) ? 2 : 1;
+  constexpr int kWph = C::NW / kHpw;  // waves per query head
+  constexpr int kRows = kBM / kHpw;   // query rows per workgroup and head
+  static_assert(!LIST || kRows == kListBlock, "one query block per workgroup and head");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -247,6 +238,28 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   const int hi = lane >> 5;  // lane half
   const int j16 = lane & 15;
 
+  int tile, unit;
+  decode_tile(p, CAUSAL || LIST, tile, unit);
+  const int n_hu = p.hq / kHpw;                       // units per sequence
+  const int b = unit / n_hu;
+  const int h = (unit % n_hu) * kHpw + wave / kWph;   // this wave's query head
+  const int kvh = ((unit % n_hu) * kHpw) / p.group;   // the workgroup's KV head
+
+  int64_t tok0 = 0;
+  int len = p.seqlen;
+  if (p.cu) {
+    tok0 = p.cu[b];
+    len = p.cu[b + 1] - p.cu[b];
+  }
+  const int q0 = tile * kRows;
+  if (q0 >= len) return;
+  const int w_row0 = q0 + (wave % kWph) * 32;  // this wave's first query row
+
+  const uint16_t *qg = p.q + (p.cu ? tok0 * p.q_ss : (int64_t)b * p.q_sb) + (int64_t)h * p.q_sh;
+  const uint16_t *kg = p.k + (p.cu ? tok0 * p.k_ss : (int64_t)b * p.k_sb) + (int64_t)kvh * p.k_sh;
+  const uint16_t *vg = p.v + (p.cu ? tok0 * p.v_ss : (int64_t)b * p.v_sb) + (int64_t)kvh * p.v_sh;
+  uint16_t *og = p.o + (p.cu ? tok0 * p.o_ss : (int64_t)b * p.o_sb) + (int64_t)h * p.o_sh;
+
   // ---- KV iteration space
   constexpr int kSub = kListBlock / kBN;  // KV tiles per 128-key block
   // (the stop flags of an entry are written after its last tile and read after
@@ -254,7 +267,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   // from racing a read of the previous flags)
   static_assert(!OSK || kSub >= 2, "ordered skipping needs two or more tiles per list entry");
   int n_iter;
-  int e0 = 0;
+  int e0 = 0, n_ent = 0;
   const int n_kvblk = (len + kListBlock - 1) / kListBlock;
   // block mask: this query block's row of the (sequence, kv head) mask; under
   // causal masking only blocks up to the query block count
@@ -267,14 +280,19 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   };
   if (MODE == kList || MODE == kOsk) {
     e0 = p.row_ptr[tile];
-    n_iter = (p.row_ptr[tile + 1] - e0) * kSub;
+    n_ent = p.row_ptr[tile + 1] - e0;
+    n_iter = n_ent * kSub;
   } else if (MODE == kMask) {
     mrow = p.mask + b * p.mask_ss + kvh * p.mask_sh + (int64_t)tile * p.mask_words;
+    // set bits below m_lim, one word per lane, summed over the wave
     int n_blk = 0;
-    for (int w = 0; w < m_words; ++w) n_blk += __builtin_popcount(mrow[w] & m_valid(w));
-    n_iter = n_blk * kSub;
+    for (int w0 = 0; w0 < m_words; w0 += 64) {
+      const int w = w0 + lane;
+      n_blk += wave_sum(w < m_words ? __builtin_popcount(mrow[w] & m_valid(w)) : 0);
+    }
+    n_iter = __builtin_amdgcn_readfirstlane(n_blk) * kSub;
   } else {
-    const int kv_end = CAUSAL ? min(len, q0 + kBM) : len;
+    const int kv_end = CAUSAL ? min(len, q0 + kRows) : len;
     n_iter = (kv_end + kBN - 1) / kBN;
   }
   // kv start of iteration `it` (called for it = 0, 1, 2, ... in order), or -1
@@ -299,7 +317,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     }
     const int cb = p.col_idx[e0 + it / kSub];
     if (cb < 0 || cb >= n_kvblk) return -1;
-    if (CAUSAL && cb * kListBlock > q0 + kBM - 1) return -1;
+    if (CAUSAL && cb * kListBlock > q0 + kRows - 1) return -1;
     return cb * kListBlock + (it % kSub) * kBN;
   };
 
@@ -337,19 +355,74 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   float l_run = 0.f;  // running sum over this lane's half of the keys
   float d_run = 0.f;  // ordered skipping: the current list entry's part of l_run
 
-  const int qrow = q0 + wave * 32 + l32;  // this lane's query row (sequence position)
-  const int wq_last = q0 + wave * 32 + 31;
+  const int qrow = w_row0 + l32;  // this lane's query row (sequence position)
+  const int wq_last = w_row0 + 31;
 
-  // Dense problems with two waves per SIMD from one workgroup run the
-  // software-pipelined loop below, and so does head_dim 256 (one wave per
-  // SIMD, in its solo form); the other kernels the plain one.
-  constexpr bool kSolo = MODE == kDense && C::NW == 4 && D == 256;
-  constexpr bool kPipe = (MODE == kDense && C::NW >= 8) || kSolo;
-  int kv_cur = n_iter > 0 ? kv_start(0) : -1;
-  if (kv_cur >= 0 && loader) {
-    if constexpr (kPipe)
-      issue_rows<C>(smem + slot_byte0, kg + (int64_t)kv_cur * p.k_ss, koff, lrow, p.k_ss, len - kv_cur);
-    else
+  // Problems with two waves per SIMD from one workgroup (dense, or the
+  // paired block-list and block-mask kernels) run the software-pipelined loop
+  // below, and so does head_dim 256 (one wave per SIMD, in its solo form); the
+  // other kernels (ordered skipping, and block lists of unpaired heads) the
+  // plain one.
+  constexpr bool kSolo = !OSK && C::NW == 4 && D == 256;
+  constexpr bool kPipe = (!OSK && C::NW >= 8) || kSolo;
+  int kv_cur = -1;  // plain loop: first key of the tile in flight
+
+  // ---- tile walk of the pipelined loop.  Each tile has a load position (its
+  // first key) and a mask position: the same, or far past every key (the
+  // whole tile masked) for a list entry that names no block of the sequence,
+  // which is loaded from block 0.  Dense: tile t starts at key t*kBN.  Block
+  // list and mask: tile t is sub-tile t % kSub of the (t / kSub)-th visited
+  // block, visited in list order (mask: set bits, lowest first).  The next
+  // list entry (mask word) is read one entry ahead, so its scalar load has a
+  // whole entry's tiles to land before it is needed.
+  constexpr int kFarKey = 1 << 30;
+  int w_t = 0;          // dense: next tile
+  int w_sub = kSub;     // sub-tile of the current entry (kSub: go to the next entry)
+  int w_ent = -1;       // list: current entry
+  int w_blk = 0;        // current block
+  bool w_ok = true;     // it lies in the sequence
+  int w_raw = (kPipe && MODE == kList && n_ent > 0) ? p.col_idx[e0] : 0;  // id of entry w_ent + 1
+  int mw_w = -1;        // mask: word being walked
+  uint32_t mw_bits = 0u;  // its set bits not yet visited
+  uint32_t mw_pf = (kPipe && MODE == kMask && m_words > 0) ? (mrow[0] & m_valid(0)) : 0u;  // word mw_w + 1
+  auto walk = [&](int &lpos, int &mpos) __attribute__((always_inline)) {
+    if constexpr (MODE == kDense) {
+      lpos = mpos = w_t * kBN;
+      ++w_t;
+    } else {
+      if (w_sub == kSub) {
+        w_sub = 0;
+        if constexpr (MODE == kList) {
+          ++w_ent;
+          w_ok = w_raw >= 0 && w_raw < n_kvblk;
+          w_blk = w_ok ? w_raw : 0;
+          if (w_ent + 1 < n_ent) w_raw = p.col_idx[e0 + w_ent + 1];
+        } else {
+          while (mw_bits == 0u && mw_w + 1 < m_words) {
+            ++mw_w;
+            mw_bits = mw_pf;
+            mw_pf = mw_w + 1 < m_words ? (mrow[mw_w + 1] & m_valid(mw_w + 1)) : 0u;
+          }
+          w_ok = mw_bits != 0u;  // (always, for the counted tiles)
+          w_blk = w_ok ? 32 * mw_w + __builtin_ctz(mw_bits) : 0;
+          mw_bits &= mw_bits - 1u;
+        }
+      }
+      lpos = w_blk * kListBlock + w_sub * kBN;
+      mpos = w_ok ? lpos : kFarKey;
+      ++w_sub;
+    }
+  };
+  int lp_cur = 0, lp_nxt = 0;              // pipelined loop: load positions of tiles j, j + 1
+  int mp_prv = 0, mp_cur = 0, mp_nxt = 0;  // ... and mask positions of tiles j - 1, j, j + 1
+  if constexpr (kPipe) {
+    if (n_iter > 0) {
+      walk(lp_cur, mp_cur);
+      if (loader) issue_rows<C>(smem + slot_byte0, kg + (int64_t)lp_cur * p.k_ss, koff, lrow, p.k_ss, len - lp_cur);
+    }
+  } else {
+    kv_cur = n_iter > 0 ? kv_start(0) : -1;
+    if (kv_cur >= 0 && loader)
       issue_tile<C>(smem + slot_byte0, smem + kTileBytes + slot_byte0, kg + (int64_t)kv_cur * p.k_ss,
                     vg + (int64_t)kv_cur * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_cur);
   }
@@ -368,9 +441,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   char *const q_stage = smem + 2 * kBufBytes + wave * 32 * L::kRowBytes;
   if constexpr (kPipe) {
     static_assert(kOwnStage, "Q is staged in the O staging area");
-    stage_q_rows<L::kRowBytes, L::kChunks, L::kRowsPerWin>(q_stage, qg, p.q_ss, q0 + wave * 32, len, lane);
+    // (an empty block set writes O = 0 through the same area at once: no loads then)
+    if (n_iter > 0) stage_q_rows<L::kRowBytes, L::kChunks, L::kRowsPerWin>(q_stage, qg, p.q_ss, w_row0, len, lane);
   } else {
-    const int r = q0 + wave * 32 + l32;
+    const int r = w_row0 + l32;
 #pragma unroll
     for (int dc = 0; dc < kDc; ++dc) {
       uint4_t x = {0u, 0u, 0u, 0u};
@@ -404,13 +478,14 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   // scale folded into c): masks the causal diagonal and the sequence tail
   // where the tile needs it, forms P in bf16 in the MFMA operand layout and
   // adds the tile's row sums to l_run.  P is first computed against the
-  // running max as it stands; the tile's own max is taken only on the wave's
-  // first tile or when some row sum exceeds kFastSum (a score well above the
-  // running max).  Then the max is raised to the tile's, O and l are
-  // rescaled and P is computed again.
-  bool first = true;  // no tile processed yet by this wave
+  // running max as it stands; the tile's own max is taken only while some
+  // row of the wave has no running max yet (no visible key so far: the
+  // wave's first tiles) or when some row sum exceeds kFastSum (a score well
+  // above the running max).  Then the max is raised to the tile's, O and l
+  // are rescaled and P is computed again.
+  bool first = true;  // some row of this wave has seen no visible key yet
   auto mask_tile = [&](floatx16_t (&s)[kKt], const int kv0) __attribute__((always_inline)) {
-    const bool need_mask = (kv0 + kBN > len) || (CAUSAL && kv0 + kBN - 1 > q0 + wave * 32);
+    const bool need_mask = (kv0 + kBN > len) || (CAUSAL && kv0 + kBN - 1 > w_row0);
     if (need_mask) {
       // key kv0 + hi*4 + o (o a compile-time offset) is masked when o > lim
       const int lim = (CAUSAL ? min(qrow, len - 1) : len - 1) - kv0 - hi * 4;
@@ -443,6 +518,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         for (int dt = 0; dt < kDt; ++dt) oacc[dt] = oacc[dt] * alpha;
       }
       rs = exp_tile(s, p.c, m_run == -INFINITY ? 0.f : m_run, pb);
+      // (a row whose keys were all masked so far keeps m = -inf, and the
+      // next tiles must take their max again)
+      first = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
     }
     l_run += rs;
     if (OSK) d_run += rs;
@@ -455,44 +533,51 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       rs = exp_tile(s, p.c, m_run == -INFINITY ? 0.f : m_run, pb);
       slow = __builtin_amdgcn_ballot_w64(rs > kFastSum) != 0;
     }
-    first = false;
     softmax_slow(s, pb, rs, slow);
   };
 
   int n_done = n_iter;  // tiles walked (ordered skipping may stop early)
   if constexpr (kPipe) {
-    // ---- software-pipelined dense loop.  Iteration j (one barrier each,
+   if (n_iter > 0) {
+    // ---- software-pipelined loop.  Iteration j (one barrier each,
     // j = 0 .. n_iter) issues the loads of K(j+1) and V(j), and each wave
     // runs one MFMA phase with the scores S(j) = K(j) Q^T interleaved with
     // the PV product of the tile before, O^T += V(j-1)^T P(j-1)^T, and the
     // online softmax of one tile.  K buffer j % 2 holds K(j), V buffer j % 2
     // holds V(j); a buffer is rewritten one barrier after its last read.
-    // Waves w, w + 4 (and w + 8) share a SIMD; waves 4-7 run the iteration
+    // Tile positions come from the walk (called once per tile, in order, by
+    // every wave).  Waves w, w + 4 (and w + 8) share a SIMD (in the paired
+    // block-sparse kernels: the same rows of the two heads); waves 4-7 run the iteration
     // rotated against the others: waves 0-3 (and 8-11) do [MFMA phase]
     // [softmax of S(j)], waves 4-7 [softmax of S(j-1)][MFMA phase], so that
     // while one wave works through the exp2 and VALU work of the softmax
     // another keeps the matrix core busy.
     const bool lagged = ((wave >> 2) & 1) != 0;
-    // tiles this wave needs (under causal masking, those not wholly above its rows)
-    const int n_own = CAUSAL ? min(n_iter, wq_last / kBN + 1) : n_iter;
+    // tiles this wave needs (dense causal: those not wholly above its rows)
+    const int n_own = (CAUSAL && MODE == kDense) ? min(n_iter, wq_last / kBN + 1) : n_iter;
     floatx16_t s[kKt];
     bf16x8_t pb[kKt][2];
     auto sync = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
     };
+    // step j's loads: K(j + 1) (walking on to tile j + 1) and V(j)
     auto issue = [&](const int j) __attribute__((always_inline)) {
-      if (!loader) return;
       if (j + 1 < n_iter) {
-        const int kv = (j + 1) * kBN;
-        issue_rows<C>(smem + ((j + 1) & 1) * kBufBytes + slot_byte0, kg + (int64_t)kv * p.k_ss, koff,
-                      lrow, p.k_ss, len - kv);
+        walk(lp_nxt, mp_nxt);
+        if (loader)
+          issue_rows<C>(smem + ((j + 1) & 1) * kBufBytes + slot_byte0, kg + (int64_t)lp_nxt * p.k_ss, koff,
+                        lrow, p.k_ss, len - lp_nxt);
       }
-      if (j < n_iter) {
-        const int kv = j * kBN;
-        issue_rows<C>(smem + (j & 1) * kBufBytes + kTileBytes + slot_byte0, vg + (int64_t)kv * p.v_ss,
-                      voff, lrow, p.v_ss, len - kv);
-      }
+      if (j < n_iter && loader)
+        issue_rows<C>(smem + (j & 1) * kBufBytes + kTileBytes + slot_byte0, vg + (int64_t)lp_cur * p.v_ss,
+                      voff, lrow, p.v_ss, len - lp_cur);
+    };
+    // end of step j: tile j + 1 becomes the current one
+    auto shift = [&]() __attribute__((always_inline)) {
+      mp_prv = mp_cur;
+      mp_cur = mp_nxt;
+      lp_cur = lp_nxt;
     };
     // One MFMA phase: K from buffer kKb, V from buffer kVb.  Operand reads run
     // kRing steps ahead of their MFMA; consecutive MFMAs alternate between
@@ -555,7 +640,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       // P(j) goes to P buffer j % 2.
       static_assert(kKt == 1 && kDt == 8, "one 32-key score tile; one exp2 per PV MFMA");
       bf16x8_t pp[2][kKt][2];
-      softmax(s, 0, pp[0]);
+      softmax(s, mp_cur, pp[0]);
+      shift();
       auto pv_exp = [&](auto vb_tag, auto ps_tag, auto pd_tag) __attribute__((always_inline)) -> float {
         constexpr int kVb = decltype(vb_tag)::value;  // V buffer of the PV tile
         constexpr int kPs = decltype(ps_tag)::value;  // its P buffer
@@ -591,9 +677,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         sync();
         issue(j);
         phase(kb_tag, BufTag<1 - kKb>{}, std::integral_constant<int, kOnlyS>{});
-        mask_tile(s, j * kBN);
+        mask_tile(s, mp_cur);
         const float rs = pv_exp(BufTag<1 - kKb>{}, BufTag<1 - kKb>{}, BufTag<kKb>{});
-        softmax_slow(s, pp[kKb], rs, __builtin_amdgcn_ballot_w64(rs > kFastSum) != 0);
+        softmax_slow(s, pp[kKb], rs, first || __builtin_amdgcn_ballot_w64(rs > kFastSum) != 0);
+        shift();
         ++j;
       };
       while (j + 1 < n_own) {
@@ -608,12 +695,15 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         pv_exp(BufTag<1>{}, BufTag<1>{}, BufTag<-1>{});
       else
         pv_exp(BufTag<0>{}, BufTag<0>{}, BufTag<-1>{});
+      shift();
       for (int jj = n_own + 1; jj <= n_iter; ++jj) {
         sync();
         issue(jj);
+        shift();
       }
     } else {
-    if (!lagged) softmax(s, 0, pb);
+    if (!lagged) softmax(s, mp_cur, pb);
+    shift();
     // iterations 1 .. n_own - 1, two per trip so that the buffers of each
     // are compile-time constants
     int j = 1;
@@ -621,9 +711,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       constexpr int kKb = decltype(kb_tag)::value;  // = j % 2
       sync();
       issue(j);
-      if (lagged) softmax(s, (j - 1) * kBN, pb);
+      if (lagged) softmax(s, mp_prv, pb);
       phase(kb_tag, BufTag<1 - kKb>{}, std::integral_constant<int, kBoth>{});
-      if (!lagged) softmax(s, j * kBN, pb);
+      if (!lagged) softmax(s, mp_cur, pb);
+      shift();
       ++j;
     };
     while (j + 1 < n_own) {
@@ -634,17 +725,20 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     // iteration n_own: PV of the wave's last tile
     sync();
     issue(n_own);
-    if (lagged) softmax(s, (n_own - 1) * kBN, pb);
+    if (lagged) softmax(s, mp_prv, pb);
     if ((n_own - 1) & 1)
       phase(BufTag<0>{}, BufTag<1>{}, std::integral_constant<int, kOnlyPV>{});
     else
       phase(BufTag<0>{}, BufTag<0>{}, std::integral_constant<int, kOnlyPV>{});
+    shift();
     // the other waves' remaining iterations: barriers and loads only
     for (int jj = n_own + 1; jj <= n_iter; ++jj) {
       sync();
       issue(jj);
+      shift();
     }
     }
+   }
   } else {
     // Returns true (ordered skipping only) when the walk stops before tile `it`.
     auto step = [&](const int it, auto buf_tag) -> bool {
@@ -798,15 +892,15 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       const int r = k * kRowsPerStore + r0;
       x[k] = *reinterpret_cast<const uint4_t *>(so + r * kRowB + ((ch ^ (r % kCh)) * 16));
     }
-    uint16_t *orow = og + (int64_t)(q0 + wave * 32 + r0) * p.o_ss + ch * 8;
+    uint16_t *orow = og + (int64_t)(w_row0 + r0) * p.o_ss + ch * 8;
     const int64_t step_rows = (int64_t)kRowsPerStore * p.o_ss;
-    if (q0 + wave * 32 + 32 <= len) {
+    if (w_row0 + 32 <= len) {
 #pragma unroll
       for (int k = 0; k < kStores; ++k) *reinterpret_cast<uint4_t *>(orow + k * step_rows) = x[k];
     } else {
 #pragma unroll
       for (int k = 0; k < kStores; ++k)
-        if (q0 + wave * 32 + k * kRowsPerStore + r0 < len)
+        if (w_row0 + k * kRowsPerStore + r0 < len)
           *reinterpret_cast<uint4_t *>(orow + k * step_rows) = x[k];
     }
   }
@@ -878,7 +972,13 @@ int validate(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t
 
 template <class C, bool CAUSAL, int MODE>
 int launch(Params p, hipStream_t stream) {
-  p.n_tiles = (p.seqlen + C::kBM - 1) / C::kBM;
+  // query heads per workgroup: two for the paired block-list / block-mask kernels
+  const int hpw = (MODE == kList || MODE == kMask) && C::NW == 8 ? 2 : 1;
+  const int rows = C::kBM / hpw;
+  p.n_tiles = (p.seqlen + rows - 1) / rows;
+  p.n_units = p.batch * (p.hq / hpw);
+  p.unit_group = p.group / hpw;
+  p.xcd_remap = (p.n_units % (8 * p.unit_group)) == 0 ? 1 : 0;
   const int64_t n_blocks = (int64_t)p.n_tiles * p.n_units;
   void *args[] = {&p};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<C, CAUSAL, MODE>),
@@ -890,10 +990,19 @@ template <int D>
 int launch_d(const Params &p, bool causal, int mode, hipStream_t s) {
   using Dense = Config<D, D == 64 ? 12 : (D == 128 ? 8 : 4)>;
   using Listed = Config<D, 4>;
-  if (mode == kList)
+  // Block list and block mask: two query heads of one GQA group per workgroup
+  // when the group splits in pairs (head_dim 256: one head, four waves, in the
+  // solo form of the pipelined loop); else the plain four-wave kernel.
+  using Paired = Config<D, D == 256 ? 4 : 8>;
+  const bool paired = D == 256 || p.group % 2 == 0;
+  if (mode == kList) {
+    if (paired) return causal ? launch<Paired, true, kList>(p, s) : launch<Paired, false, kList>(p, s);
     return causal ? launch<Listed, true, kList>(p, s) : launch<Listed, false, kList>(p, s);
-  if (mode == kMask)
+  }
+  if (mode == kMask) {
+    if (paired) return causal ? launch<Paired, true, kMask>(p, s) : launch<Paired, false, kMask>(p, s);
     return causal ? launch<Listed, true, kMask>(p, s) : launch<Listed, false, kMask>(p, s);
+  }
   if (mode == kOsk)
     return causal ? launch<Listed, true, kOsk>(p, s) : launch<Listed, false, kOsk>(p, s);
   return causal ? launch<Dense, true, kDense>(p, s) : launch<Dense, false, kDense>(p, s);
@@ -936,9 +1045,7 @@ Params make_params(const attn_tensor_t *q, const attn_tensor_t *k, const attn_te
   p.seqlen = q->seqlen;
   p.hq = q->heads;
   p.group = q->heads / k->heads;
-  p.n_tiles = 0;  // set per configuration at launch
-  p.n_units = q->batch * q->heads;
-  p.xcd_remap = (p.n_units % (8 * p.group)) == 0 ? 1 : 0;
+  p.n_tiles = p.n_units = p.unit_group = p.xcd_remap = 0;  // set per configuration at launch
   p.c = scale * 1.44269504088896340736f;
   return p;
 }

@@ -204,6 +204,52 @@ def test_full_list_equals_dense():
     P.compare(os_, ls, od, ld, "shuffled list")
 
 
+def random_list(seed, n_qblk, n_kblk, p=0.4, bad_ids=True, empty_row=None):
+    """A block list in random order per query block: the diagonal and a random share of
+    the others (some above the diagonal), plus ids outside the sequence that must be
+    skipped; one row may be left empty."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for qb in range(n_qblk):
+        ids = [b for b in range(n_kblk) if b == qb or rng.random() < p]
+        if bad_ids and qb % 3 == 1:
+            ids += [-1, n_kblk + 2]
+        rng.shuffle(ids)
+        rows.append([] if qb == empty_row else ids)
+    row_ptr = np.zeros(n_qblk + 1, np.int32)
+    row_ptr[1:] = np.cumsum([len(r) for r in rows])
+    return row_ptr, np.array([c for r in rows for c in r] or [0], np.int32)[:row_ptr[-1]]
+
+
+LIST_CASES = [
+    # name, S, hq, hkv, d, causal (paired kernels for even groups; g = 1 and 3 use the 4-wave kernel)
+    ("list_d64_causal", 700, 4, 2, 64, True),
+    ("list_d64_noncausal", 700, 4, 2, 64, False),
+    ("list_d128_causal", 900, 8, 2, 128, True),
+    ("list_d128_noncausal_g1", 500, 3, 3, 128, False),
+    ("list_d128_causal_g3", 600, 6, 2, 128, True),
+    ("list_d256_causal", 650, 4, 2, 256, True),
+    ("list_d256_noncausal", 400, 2, 1, 256, False),
+]
+
+
+@pytest.mark.parametrize("case", LIST_CASES, ids=[c[0] for c in LIST_CASES])
+def test_block_list_small_full(case):
+    """Random block lists (any order, ids above the diagonal, ids outside the sequence,
+    an empty row, a ragged last block) against the oracle on every output."""
+    name, s, hq, hkv, d, causal = case
+    note(f"block list case {name}")
+    w = W.make_dense(name, 25, 1, s, hq, hkv, d, causal)
+    n = (s + 127) // 128
+    w.row_ptr, w.col_idx = random_list(26, n, n, empty_row=2)
+    o, l = P.run_gpu(w)
+    assert np.all(o[256:384] == 0) and np.all(l[256:384] == -np.inf)
+    import oracle
+    o_ref, l_ref = oracle.run_workload(w, nthreads=P.oracle_threads())
+    stats = P.compare(o, l, o_ref, l_ref, name)
+    note(f"  {stats}")
+
+
 def test_empty_allowed_set():
     """A query block that lists only a future block: O = 0 and LSE = -inf."""
     w = W.make_dense("e", 19, 1, 384, 2, 1, 64, True)
@@ -244,6 +290,8 @@ MASK_CASES = [
     ("per_seq_noncausal_d64", None, 3, 300, 4, 4, 64, False, (3, 1)),
     ("per_seq_head_varlen_d128", [300, 1, 700, 129], 0, 0, 8, 2, 128, True, (4, 2)),
     ("per_head_causal_d256", None, 1, 520, 4, 2, 256, True, (1, 2)),
+    ("per_head_causal_d64_paired", None, 2, 700, 4, 2, 64, True, (1, 2)),
+    ("per_seq_head_varlen_d64", [640, 3, 200], 0, 0, 8, 2, 64, True, (3, 2)),
     ("two_words_causal_d64", None, 1, 40 * 128 + 17, 2, 2, 64, True, (1, 2)),
     ("shared_noncausal_d128", None, 2, 400, 2, 1, 128, False, (1, 1)),
 ]
