@@ -26,6 +26,8 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // s_waitcnt immediate that waits for vmcnt == 0 and leaves the other counters
 // free (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14])
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
+// ... and the immediate that waits for vmcnt <= n (n < 64)
+constexpr int wait_vmcnt(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
 
 
 // ---------------------------------------------------------------------------

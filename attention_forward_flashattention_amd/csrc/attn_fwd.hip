@@ -219,8 +219,28 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   constexpr bool kOwnStage = C::kMinBlocks == 1;
   constexpr int kStageBytes = C::NW * 32 * D * 2;
   constexpr int kFlagBytes = OSK ? 16 : 0;  // one stop flag per wave
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes + (kOwnStage ? kStageBytes : 0) + kFlagBytes];
-  uint32_t *osk_flag = reinterpret_cast<uint32_t *>(smem + 2 * kBufBytes + (kOwnStage ? kStageBytes : 0));
+  // Problems with two waves per SIMD from one workgroup (dense, or the
+  // paired block-list and block-mask kernels) run the software-pipelined loop
+  // below, and so does head_dim 256 (one wave per SIMD, in its solo form); the
+  // other kernels (ordered skipping, and block lists of unpaired heads) the
+  // plain one.
+  constexpr bool kSolo = !OSK && C::NW == 4 && D == 256;
+  constexpr bool kPipe = (!OSK && C::NW >= 8) || kSolo;
+  // K/V tiles in LDS.  Pipelined loop: a ring of kStages slots, all K tiles
+  // first (slot b at b * kTileBytes), then all V tiles (slot b at
+  // kStages * kTileBytes + b * kTileBytes), so that every operand read's
+  // immediate offset stays below 64 KiB.  Three slots (loads issued two
+  // tiles ahead) at head_dim 256, whose 32-key tiles leave one iteration too
+  // little time for a load to land (+7% there); two elsewhere (a third slot
+  // gained nothing at 64 and 128, and 64-key tiles of block-sparse lists
+  // lose to random addresses no matter how early they are issued).  Plain
+  // loop: two buffers of [K tile, V tile].
+  constexpr int kStages = (kPipe && D == 256) ? 3 : 2;
+  constexpr int kKVBytes = kStages * kBufBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[kKVBytes + (kOwnStage ? kStageBytes : 0) + kFlagBytes];
+  uint32_t *osk_flag = reinterpret_cast<uint32_t *>(smem + kKVBytes + (kOwnStage ? kStageBytes : 0));
+  auto kslot = [](int b) { return b * kTileBytes; };
+  auto vslot = [](int b) { return kStages * kTileBytes + b * kTileBytes; };
 
   // Query heads per workgroup: the pipelined block-list and block-mask kernels
   // take two query heads of one GQA group, 128 rows (one query block) each;
@@ -358,13 +378,6 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   const int qrow = w_row0 + l32;  // this lane's query row (sequence position)
   const int wq_last = w_row0 + 31;
 
-  // Problems with two waves per SIMD from one workgroup (dense, or the
-  // paired block-list and block-mask kernels) run the software-pipelined loop
-  // below, and so does head_dim 256 (one wave per SIMD, in its solo form); the
-  // other kernels (ordered skipping, and block lists of unpaired heads) the
-  // plain one.
-  constexpr bool kSolo = !OSK && C::NW == 4 && D == 256;
-  constexpr bool kPipe = (!OSK && C::NW >= 8) || kSolo;
   int kv_cur = -1;  // plain loop: first key of the tile in flight
 
   // ---- tile walk of the pipelined loop.  Each tile has a load position (its
@@ -413,12 +426,14 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       ++w_sub;
     }
   };
-  int lp_cur = 0, lp_nxt = 0;              // pipelined loop: load positions of tiles j, j + 1
-  int mp_prv = 0, mp_cur = 0, mp_nxt = 0;  // ... and mask positions of tiles j - 1, j, j + 1
+  // pipelined loop, before iteration j: lp[i] is the load position of tile
+  // j + i (i < kStages), mp[i] the mask position of tile j - 1 + i (i <= kStages)
+  int lp[kStages] = {};
+  int mp[kStages + 1] = {};
   if constexpr (kPipe) {
     if (n_iter > 0) {
-      walk(lp_cur, mp_cur);
-      if (loader) issue_rows<C>(smem + slot_byte0, kg + (int64_t)lp_cur * p.k_ss, koff, lrow, p.k_ss, len - lp_cur);
+      walk(lp[0], mp[1]);
+      if (loader) issue_rows<C>(smem + kslot(0) + slot_byte0, kg + (int64_t)lp[0] * p.k_ss, koff, lrow, p.k_ss, len - lp[0]);
     }
   } else {
     kv_cur = n_iter > 0 ? kv_start(0) : -1;
@@ -438,11 +453,23 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   // queue at the texture unit for ~4x as many cache lines.  Rows past the
   // end re-read the last row (finite; never stored).
   bf16x8_t qreg[kDc];
-  char *const q_stage = smem + 2 * kBufBytes + wave * 32 * L::kRowBytes;
+  char *const q_stage = smem + kKVBytes + wave * 32 * L::kRowBytes;
   if constexpr (kPipe) {
     static_assert(kOwnStage, "Q is staged in the O staging area");
     // (an empty block set writes O = 0 through the same area at once: no loads then)
-    if (n_iter > 0) stage_q_rows<L::kRowBytes, L::kChunks, L::kRowsPerWin>(q_stage, qg, p.q_ss, w_row0, len, lane);
+    if (n_iter > 0) {
+      stage_q_rows<L::kRowBytes, L::kChunks, L::kRowsPerWin>(q_stage, qg, p.q_ss, w_row0, len, lane);
+      // with three slots, K(1) and V(0) behind them (the ring runs two tiles ahead)
+      if constexpr (kStages == 3) {
+        if (n_iter > 1) {
+          walk(lp[1], mp[2]);
+          if (loader)
+            issue_rows<C>(smem + kslot(1) + slot_byte0, kg + (int64_t)lp[1] * p.k_ss, koff, lrow, p.k_ss, len - lp[1]);
+        }
+        if (loader)
+          issue_rows<C>(smem + vslot(0) + slot_byte0, vg + (int64_t)lp[0] * p.v_ss, voff, lrow, p.v_ss, len - lp[0]);
+      }
+    }
   } else {
     const int r = w_row0 + l32;
 #pragma unroll
@@ -471,7 +498,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   for (int dt = 0; dt < kDt; ++dt) {
     vaddr[dt] = L::vv(4 * hi + (j16 >> 2), 2 * dt + (l32 >> 4), (j16 & 3) * 8);
     asm volatile("" : "+v"(vaddr[dt]));
-    vlds[dt] = smem_lds + (uint32_t)vaddr[dt];
+    vlds[dt] = smem_lds + (kPipe ? (uint32_t)vslot(0) : 0u) + (uint32_t)vaddr[dt];
   }
 
   // ---- online softmax of one score tile whose first key is kv0 (base 2,
@@ -539,47 +566,59 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   int n_done = n_iter;  // tiles walked (ordered skipping may stop early)
   if constexpr (kPipe) {
    if (n_iter > 0) {
-    // ---- software-pipelined loop.  Iteration j (one barrier each,
-    // j = 0 .. n_iter) issues the loads of K(j+1) and V(j), and each wave
-    // runs one MFMA phase with the scores S(j) = K(j) Q^T interleaved with
-    // the PV product of the tile before, O^T += V(j-1)^T P(j-1)^T, and the
-    // online softmax of one tile.  K buffer j % 2 holds K(j), V buffer j % 2
-    // holds V(j); a buffer is rewritten one barrier after its last read.
-    // Tile positions come from the walk (called once per tile, in order, by
-    // every wave).  Waves w, w + 4 (and w + 8) share a SIMD (in the paired
-    // block-sparse kernels: the same rows of the two heads); waves 4-7 run the iteration
-    // rotated against the others: waves 0-3 (and 8-11) do [MFMA phase]
-    // [softmax of S(j)], waves 4-7 [softmax of S(j-1)][MFMA phase], so that
-    // while one wave works through the exp2 and VALU work of the softmax
-    // another keeps the matrix core busy.
+    // ---- software-pipelined loop over a ring of kStages K and V slots.
+    // Iteration j (one barrier each, j = 0 .. n_iter) issues the loads of
+    // K(j + kStages - 1) and V(j + kStages - 2), and each wave runs one MFMA
+    // phase with the scores S(j) = K(j) Q^T interleaved with the PV product
+    // of the tile before, O^T += V(j-1)^T P(j-1)^T, and the online softmax of
+    // one tile.  K slot t % kStages holds K(t), V slot t % kStages holds
+    // V(t); a slot is rewritten one barrier after its last read, and a load
+    // has kStages - 1 iterations to land.  Tile positions come from the walk
+    // (called once per tile, in order, by every wave).  Waves w, w + 4 (and w + 8)
+    // share a SIMD (in the paired block-sparse kernels: the same rows of the
+    // two heads); waves 4-7 run the iteration rotated against the others:
+    // waves 0-3 (and 8-11) do [MFMA phase][softmax of S(j)], waves 4-7
+    // [softmax of S(j-1)][MFMA phase], so that while one wave works through
+    // the exp2 and VALU work of the softmax another keeps the matrix core
+    // busy.
     const bool lagged = ((wave >> 2) & 1) != 0;
     // tiles this wave needs (dense causal: those not wholly above its rows)
     const int n_own = (CAUSAL && MODE == kDense) ? min(n_iter, wq_last / kBN + 1) : n_iter;
     floatx16_t s[kKt];
     bf16x8_t pb[kKt][2];
-    auto sync = [&]() __attribute__((always_inline)) {
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // Before iteration j: K(j) and V(j-1) have landed.  With three slots they
+    // were issued one iteration before the loads of iteration j-1, which may
+    // stay in flight (2 kLoads per loading wave when that iteration issued
+    // both tiles); with two, they are the last loads issued.
+    auto sync = [&](const int j) __attribute__((always_inline)) {
+      if (kStages == 3 && loader && j + 1 < n_iter)
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * C::kLoads));
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
     };
-    // step j's loads: K(j + 1) (walking on to tile j + 1) and V(j)
+    // iteration j's loads: K(j + kStages - 1) (walking on to that tile) and
+    // V(j + kStages - 2)
+    constexpr int kAhead = kStages - 1;
     auto issue = [&](const int j) __attribute__((always_inline)) {
-      if (j + 1 < n_iter) {
-        walk(lp_nxt, mp_nxt);
+      if (j + kAhead < n_iter) {
+        walk(lp[kAhead], mp[kAhead + 1]);
         if (loader)
-          issue_rows<C>(smem + ((j + 1) & 1) * kBufBytes + slot_byte0, kg + (int64_t)lp_nxt * p.k_ss, koff,
-                        lrow, p.k_ss, len - lp_nxt);
+          issue_rows<C>(smem + kslot((j + kAhead) % kStages) + slot_byte0, kg + (int64_t)lp[kAhead] * p.k_ss,
+                        koff, lrow, p.k_ss, len - lp[kAhead]);
       }
-      if (j < n_iter && loader)
-        issue_rows<C>(smem + (j & 1) * kBufBytes + kTileBytes + slot_byte0, vg + (int64_t)lp_cur * p.v_ss,
-                      voff, lrow, p.v_ss, len - lp_cur);
+      if (j + kAhead - 1 < n_iter && loader)
+        issue_rows<C>(smem + vslot((j + kAhead - 1) % kStages) + slot_byte0, vg + (int64_t)lp[kAhead - 1] * p.v_ss,
+                      voff, lrow, p.v_ss, len - lp[kAhead - 1]);
     };
-    // end of step j: tile j + 1 becomes the current one
+    // end of iteration j: tile j + 1 becomes the current one
     auto shift = [&]() __attribute__((always_inline)) {
-      mp_prv = mp_cur;
-      mp_cur = mp_nxt;
-      lp_cur = lp_nxt;
+      static_for<kStages>([&](auto I) { mp[decltype(I)::value] = mp[decltype(I)::value + 1]; });
+      static_for<kStages - 1>([&](auto I) { lp[decltype(I)::value] = lp[decltype(I)::value + 1]; });
     };
-    // One MFMA phase: K from buffer kKb, V from buffer kVb.  Operand reads run
+    int &mp_prv = mp[0];  // mask positions of tiles j - 1 and j
+    int &mp_cur = mp[1];
+    // One MFMA phase: K from slot kKb, V from slot kVb.  Operand reads run
     // kRing steps ahead of their MFMA; consecutive MFMAs alternate between
     // independent accumulators.
     auto phase = [&](auto kb_tag, auto vb_tag, auto what_tag) __attribute__((always_inline)) {
@@ -594,9 +633,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         constexpr int t = decltype(T)::value;
         constexpr int x = step_idx(kW, t);
         if constexpr (step_kind(kW, t) == 0)
-          return ld_b128<kKb * kBufBytes + (x % kKt) * 32 * L::kRowBytes>(klds[x / kKt]);
+          return ld_b128<kKb * kTileBytes + (x % kKt) * 32 * L::kRowBytes>(klds[x / kKt]);
         else
-          return tr_pair<kVb * kBufBytes + kTileBytes + tr_off<L, kDt>(x), 8 * L::kRowBytes>(vlds[x % kDt]);
+          return tr_pair<kVb * kTileBytes + tr_off<L, kDt>(x), 8 * L::kRowBytes>(vlds[x % kDt]);
       };
       bf16x8_t ring[kRing];
       static_for<kRing>([&](auto T) {
@@ -623,36 +662,47 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     };
     // iteration 0: scores of tile 0 (first Q into registers: this wave's
     // own staging loads have landed)
-    sync();
+    sync(0);
     issue(0);
 #pragma unroll
     for (int dc = 0; dc < kDc; ++dc)
       qreg[dc] = *reinterpret_cast<const bf16x8_t *>(q_stage + kaddr[dc]);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     phase(BufTag<0>{}, BufTag<0>{}, std::integral_constant<int, kOnlyS>{});
+    // Calls body(BufTag<j % kStages>) (the slots of an iteration are
+    // compile-time constants, so every LDS operand address is a
+    // loop-invariant lane offset plus an immediate).
+    auto dispatch = [&](const int j, auto &&body) __attribute__((always_inline)) {
+      const int b = j % kStages;
+      if (b == 0) body(BufTag<0>{});
+      else if (kStages == 2 || b == 1) body(BufTag<1>{});
+      else body(BufTag<kStages - 1>{});
+    };
     if constexpr (kSolo) {
       // ---- one wave per SIMD: no other wave fills the matrix core while
       // this one runs its softmax, so the softmax is spread over its own
       // MFMAs.  Iteration j forms S(j), then runs O^T += V(j-1)^T P(j-1)^T
-      // with the fast-path exp2 of S(j) (against the running max) issued one
-      // element per MFMA, then finishes the softmax of S(j) (the rare max
+      // with the fast-path exp2 of S(j) (against the running max) issued
+      // along the PV MFMAs, then finishes the softmax of S(j) (the rare max
       // raise and O rescale come after the PV MFMAs that precede them).
-      // P(j) goes to P buffer j % 2.
-      static_assert(kKt == 1 && kDt == 8, "one 32-key score tile; one exp2 per PV MFMA");
-      bf16x8_t pp[2][kKt][2];
+      // P(j) goes to P buffer j % 3 (the slot index of its tile).
+      constexpr int kNpv = kDt * kKt * 2;          // PV MFMAs per tile
+      constexpr int kE = kKt * 16 / kNpv;          // exp2 issued per PV MFMA
+      static_assert(kE * kNpv == kKt * 16, "the scores of a tile spread evenly over its PV MFMAs");
+      bf16x8_t pp[kStages][kKt][2];
       softmax(s, mp_cur, pp[0]);
       shift();
       auto pv_exp = [&](auto vb_tag, auto ps_tag, auto pd_tag) __attribute__((always_inline)) -> float {
-        constexpr int kVb = decltype(vb_tag)::value;  // V buffer of the PV tile
+        constexpr int kVb = decltype(vb_tag)::value;  // V slot of the PV tile
         constexpr int kPs = decltype(ps_tag)::value;  // its P buffer
         constexpr int kPd = decltype(pd_tag)::value;  // P buffer of S (-1: no exp2)
-        constexpr int kN = kDt * kKt * 2;
+        constexpr int kN = kNpv;
         constexpr int kRing = 4;
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float rs = 0.f;
         auto load = [&](auto T) __attribute__((always_inline)) -> bf16x8_t {
           constexpr int t = decltype(T)::value;
-          return tr_pair<kVb * kBufBytes + kTileBytes + tr_off<L, kDt>(t), 8 * L::kRowBytes>(vlds[t % kDt]);
+          return tr_pair<kVb * kTileBytes + tr_off<L, kDt>(t), 8 * L::kRowBytes>(vlds[t % kDt]);
         };
         bf16x8_t ring[kRing];
         static_for<kRing>([&](auto T) { ring[decltype(T)::value] = load(T); });
@@ -663,9 +713,12 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], pp[kPs][kc >> 1][kc & 1], oacc[dt], 0, 0, 0);
           if constexpr (i + kRing < kN) ring[i % kRing] = load(std::integral_constant<int, i + kRing>{});
           if constexpr (kPd >= 0) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][i], p.c, -m_use));
-            rs += pv;
-            pp[kPd][0][i >> 3][i & 7] = (__bf16)pv;
+            static_for<kE>([&](auto E) {
+              constexpr int e = i * kE + decltype(E)::value;  // score e % 16 of tile e / 16
+              const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e / 16][e % 16], p.c, -m_use));
+              rs += pv;
+              pp[kPd][e / 16][(e % 16) >> 3][e & 7] = (__bf16)pv;
+            });
           }
           __builtin_amdgcn_sched_barrier(0);
         });
@@ -673,70 +726,71 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       };
       int j = 1;
       auto body_solo = [&](auto kb_tag) __attribute__((always_inline)) {
-        constexpr int kKb = decltype(kb_tag)::value;  // = j % 2
-        sync();
+        constexpr int kKb = decltype(kb_tag)::value;  // = j % kStages: K slot and P buffer of tile j
+        constexpr int kVb = (kKb + kStages - 1) % kStages;
+        sync(j);
         issue(j);
-        phase(kb_tag, BufTag<1 - kKb>{}, std::integral_constant<int, kOnlyS>{});
+        phase(kb_tag, BufTag<kVb>{}, std::integral_constant<int, kOnlyS>{});
         mask_tile(s, mp_cur);
-        const float rs = pv_exp(BufTag<1 - kKb>{}, BufTag<1 - kKb>{}, BufTag<kKb>{});
+        const float rs = pv_exp(BufTag<kVb>{}, BufTag<kVb>{}, BufTag<kKb>{});
         softmax_slow(s, pp[kKb], rs, first || __builtin_amdgcn_ballot_w64(rs > kFastSum) != 0);
         shift();
         ++j;
       };
-      while (j + 1 < n_own) {
-        body_solo(BufTag<1>{});
-        body_solo(BufTag<0>{});
+      // iterations 1 .. n_own - 1, kStages per trip (j % kStages = 1, .., 0)
+      while (j + kStages - 1 < n_own) {
+        static_for<kStages>([&](auto I) { body_solo(BufTag<(decltype(I)::value + 1) % kStages>{}); });
       }
-      if (j < n_own) body_solo(BufTag<1>{});
+      static_for<kStages - 1>([&](auto I) {
+        if (j < n_own) body_solo(BufTag<decltype(I)::value + 1>{});
+      });
       // iteration n_own: PV of the wave's last tile
-      sync();
+      sync(n_own);
       issue(n_own);
-      if ((n_own - 1) & 1)
-        pv_exp(BufTag<1>{}, BufTag<1>{}, BufTag<-1>{});
-      else
-        pv_exp(BufTag<0>{}, BufTag<0>{}, BufTag<-1>{});
+      auto last_solo = [&](auto vb_tag) __attribute__((always_inline)) { pv_exp(vb_tag, vb_tag, BufTag<-1>{}); };
+      dispatch(n_own - 1, last_solo);
       shift();
       for (int jj = n_own + 1; jj <= n_iter; ++jj) {
-        sync();
+        sync(jj);
         issue(jj);
         shift();
       }
     } else {
-    if (!lagged) softmax(s, mp_cur, pb);
-    shift();
-    // iterations 1 .. n_own - 1, two per trip so that the buffers of each
-    // are compile-time constants
-    int j = 1;
-    auto body = [&](auto kb_tag) __attribute__((always_inline)) {
-      constexpr int kKb = decltype(kb_tag)::value;  // = j % 2
-      sync();
-      issue(j);
-      if (lagged) softmax(s, mp_prv, pb);
-      phase(kb_tag, BufTag<1 - kKb>{}, std::integral_constant<int, kBoth>{});
       if (!lagged) softmax(s, mp_cur, pb);
       shift();
-      ++j;
-    };
-    while (j + 1 < n_own) {
-      body(BufTag<1>{});
-      body(BufTag<0>{});
-    }
-    if (j < n_own) body(BufTag<1>{});
-    // iteration n_own: PV of the wave's last tile
-    sync();
-    issue(n_own);
-    if (lagged) softmax(s, mp_prv, pb);
-    if ((n_own - 1) & 1)
-      phase(BufTag<0>{}, BufTag<1>{}, std::integral_constant<int, kOnlyPV>{});
-    else
-      phase(BufTag<0>{}, BufTag<0>{}, std::integral_constant<int, kOnlyPV>{});
-    shift();
-    // the other waves' remaining iterations: barriers and loads only
-    for (int jj = n_own + 1; jj <= n_iter; ++jj) {
-      sync();
-      issue(jj);
+      int j = 1;
+      auto body = [&](auto kb_tag) __attribute__((always_inline)) {
+        constexpr int kKb = decltype(kb_tag)::value;  // = j % kStages
+        sync(j);
+        issue(j);
+        if (lagged) softmax(s, mp_prv, pb);
+        phase(kb_tag, BufTag<(kKb + kStages - 1) % kStages>{}, std::integral_constant<int, kBoth>{});
+        if (!lagged) softmax(s, mp_cur, pb);
+        shift();
+        ++j;
+      };
+      // iterations 1 .. n_own - 1, kStages per trip (j % kStages = 1, .., 0)
+      while (j + kStages - 1 < n_own) {
+        static_for<kStages>([&](auto I) { body(BufTag<(decltype(I)::value + 1) % kStages>{}); });
+      }
+      static_for<kStages - 1>([&](auto I) {
+        if (j < n_own) body(BufTag<decltype(I)::value + 1>{});
+      });
+      // iteration n_own: PV of the wave's last tile
+      sync(n_own);
+      issue(n_own);
+      if (lagged) softmax(s, mp_prv, pb);
+      auto last = [&](auto vb_tag) __attribute__((always_inline)) {
+        phase(BufTag<0>{}, vb_tag, std::integral_constant<int, kOnlyPV>{});
+      };
+      dispatch(n_own - 1, last);
       shift();
-    }
+      // the other waves' remaining iterations: barriers and loads only
+      for (int jj = n_own + 1; jj <= n_iter; ++jj) {
+        sync(jj);
+        issue(jj);
+        shift();
+      }
     }
    }
   } else {
@@ -870,7 +924,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     constexpr int kRowB = D * 2;           // bytes per O row
     constexpr int kCh = D / 8;             // 16 B chunks per row
     constexpr int kRowsPerStore = 1024 / kRowB;
-    char *so = smem + (kOwnStage ? 2 * kBufBytes : 0) + wave * 32 * kRowB;
+    char *so = smem + (kOwnStage ? kKVBytes : 0) + wave * 32 * kRowB;
 #pragma unroll
     for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
