@@ -158,13 +158,21 @@ __device__ __forceinline__ void issue_dwords(char *l, const float *src) {
 // ===========================================================================
 // dQ kernel
 // ===========================================================================
+// Workgroups per CU of the dQ kernel: two up to head_dim 128; at 256 the Q,
+// dO and dQ registers of a wave's 32 rows (~380) leave one wave per SIMD.
+template <int D>
+constexpr int dq_min_blocks() {
+  return D == 256 ? 1 : 2;
+}
+
 template <int D, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, dq_min_blocks<D>()) void attn_bwd_dq_kernel(BwdParams p) {
   using LK = Dual<D>;  // K tile: row-wise reads (S^T) and transpose reads (dQ^T)
   using LV = Lds<D>;   // V tile: row-wise reads only
   constexpr int kNW = 4;
   constexpr int kBM = 32 * kNW;
-  constexpr int kBN = 64;
+  // keys per KV tile (32 at head_dim 256: LDS operand offsets stay below 64 KiB)
+  constexpr int kBN = D == 256 ? 32 : 64;
   constexpr int kRowBytes = D * 2;
   constexpr int kChunks = D / 8;
   constexpr int kDc = D / 16;
@@ -473,6 +481,15 @@ template <int D>
 constexpr int dkdv_min_blocks() {
   return D == 64 ? 2 : 1;
 }
+// dK/dV columns per workgroup: all of them up to head_dim 128; at 256 the K
+// and V operands (the whole head dimension, for S and dP) and the
+// accumulators of all 256 columns would not fit one wave's registers, so each
+// workgroup takes one 128-column half of dK and dV (S and dP are formed once
+// per half).
+template <int D>
+constexpr int dkdv_cols() {
+  return D == 256 ? 128 : D;
+}
 
 template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kernel(BwdParams p) {
@@ -483,7 +500,8 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
   constexpr int kRowBytes = D * 2;
   constexpr int kChunks = D / 8;
   constexpr int kDc = D / 16;
-  constexpr int kDt = D / 32;
+  constexpr int kHalves = D / dkdv_cols<D>();  // column halves of dK / dV (one per workgroup)
+  constexpr int kDt = dkdv_cols<D>() / 32;     // 32-column output tiles of this workgroup
   constexpr int kTileBytes = kBQ * kRowBytes;
   constexpr int kVecBytes = kBQ * 4;
   constexpr int kBufBytes = 2 * kTileBytes + 2 * kVecBytes;  // Q, dO, lse2, D
@@ -495,8 +513,9 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
 
   int tile, unit;
   decode(p, false, tile, unit);  // causal: low key blocks (most query tiles) first
-  const int b = unit / p.hkv;
-  const int kvh = unit % p.hkv;
+  const int half = unit % kHalves;  // the dK / dV columns 32 kDt half .. of this workgroup
+  const int b = unit / kHalves / p.hkv;
+  const int kvh = unit / kHalves % p.hkv;
   int64_t tok0 = 0;
   int len = p.seqlen;
   if (p.cu) {
@@ -651,7 +670,7 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
   }
 #pragma unroll
   for (int dt = 0; dt < kDt; ++dt) {
-    const int ch = 4 * dt + 2 * (l32 >> 4) + ((j16 & 3) >> 1);
+    const int ch = 4 * (half * kDt + dt) + 2 * (l32 >> 4) + ((j16 & 3) >> 1);
     ta[dt] = smem_lds + L::at(4 * hi + (j16 >> 2), ch) + (j16 & 1) * 8;
     tb[dt] = smem_lds + L::at(8 + 4 * hi + (j16 >> 2), ch) + (j16 & 1) * 8;
     asm volatile("" : "+v"(ta[dt]));
@@ -766,7 +785,9 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
       constexpr int h = decltype(H)::value, hv = decltype(HV)::value;
       constexpr int kRing = 4;
       constexpr int kSteps = 2 * kDc;  // step i: dc = i / 2, Q (even) or dO (odd)
-      constexpr int kPer = 16 / kSteps;  // VALU elements per step
+      // VALU elements per step (kPer on every kStride-th step)
+      constexpr int kPer = kSteps >= 16 ? 1 : 16 / kSteps;
+      constexpr int kStride = kSteps >= 16 ? kSteps / 16 : 1;
       static_assert(2 * kLoads <= kSteps, "the next tile's row loads fit in the first half's steps");
       bf16x8_t ring[kRing];
       static_for<kRing>([&](auto I) {
@@ -802,8 +823,10 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
               issue_one<n>(bq_n, qt_n, qoff);
           }
         }
-        if constexpr (hv >= 0)
-          static_for<kPer>([&](auto E) { valu(HV, std::integral_constant<int, i * kPer + decltype(E)::value>{}); });
+        if constexpr (hv >= 0 && i % kStride == 0)
+          static_for<kPer>([&](auto E) {
+            valu(HV, std::integral_constant<int, (i / kStride) * kPer + decltype(E)::value>{});
+          });
         __builtin_amdgcn_sched_barrier(0);
       });
     };
@@ -887,8 +910,9 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
       for (int dt = 0; dt < kDt; ++dt) {
         const __bf16 xk = (__bf16)(dk[dt][i] * p.scale);
         const __bf16 xv = (__bf16)dv[dt][i];
-        dkg[(int64_t)kr * p.dk_ss + 32 * dt + l32] = __builtin_bit_cast(uint16_t, xk);
-        dvg[(int64_t)kr * p.dv_ss + 32 * dt + l32] = __builtin_bit_cast(uint16_t, xv);
+        const int col = 32 * (half * kDt + dt) + l32;
+        dkg[(int64_t)kr * p.dk_ss + col] = __builtin_bit_cast(uint16_t, xk);
+        dvg[(int64_t)kr * p.dv_ss + col] = __builtin_bit_cast(uint16_t, xv);
       }
     }
   }
@@ -916,7 +940,6 @@ int validate_bwd_args(const attn_tensor_t *q, const attn_tensor_t *k, const attn
   st = attn_fwd_validate(q, dk, dv, cu, causal, scale, nullptr, dq);
   if (st != ATTN_OK) return st;
   if (dk->heads != k->heads) return ATTN_ERR_INVALID_ARG;
-  if (q->head_dim == 256) return ATTN_ERR_UNSUPPORTED;
   const bool empty = q->batch == 0 || q->seqlen == 0;
   if (empty) return ATTN_OK;
   if (!lse) return ATTN_ERR_INVALID_ARG;
@@ -953,10 +976,12 @@ int launch_pair(BwdParams p, hipStream_t s) {
         dim3((unsigned)((int64_t)n_tiles * p.n_units)), dim3(256), args, 0, s);
     if (e != hipSuccess) return ATTN_ERR_LAUNCH;
   }
-  // dK/dV: one workgroup per 128-key block of each (sequence, KV head)
-  p.n_units = p.batch * p.hkv;
-  p.unit_group = 1;
-  p.xcd_remap = (p.n_units % 8) == 0 ? 1 : 0;
+  // dK/dV: one workgroup per 128-key block of each (sequence, KV head) and
+  // column half (head_dim 256), the halves of one KV head on one XCD
+  const int halves = D / dkdv_cols<D>();
+  p.n_units = p.batch * p.hkv * halves;
+  p.unit_group = halves;
+  p.xcd_remap = (p.n_units % (8 * halves)) == 0 ? 1 : 0;
   {
     void *args[] = {&p};
     const hipError_t e = hipLaunchKernel(
@@ -1035,6 +1060,7 @@ int run_bwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t 
   p.scale = scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (q->head_dim == 64) return launch_d<64>(p, causal != 0, mask != nullptr, s);
+  if (q->head_dim == 256) return launch_d<256>(p, causal != 0, mask != nullptr, s);
   return launch_d<128>(p, causal != 0, mask != nullptr, s);
 }
 

@@ -215,8 +215,10 @@ def test_bwd_invalid_arguments(kw, code):
     assert bwd_validate(desc(), desc(h=2), desc(h=2), **kw) == code
 
 
-def test_bwd_unsupported_head_dim_and_long_masked_sequences():
-    assert bwd_validate(desc(d=256), desc(h=2, d=256), desc(h=2, d=256)) == -2
+def test_bwd_head_dims_and_long_masked_sequences():
+    for d in (64, 128, 256):
+        assert bwd_validate(desc(d=d), desc(h=2, d=d), desc(h=2, d=d)) == 0
+    assert bwd_validate(desc(d=96), desc(h=2, d=96), desc(h=2, d=96)) == -2
     s = 128 * 16385  # more query blocks than the key kernel's column bitmap holds
     q, kv = desc(b=1, s=s, h=1), desc(b=1, s=s, h=1)
     m = AttnBlockMask(FAKE, 128, 128, 16385, 513, 0, 0)

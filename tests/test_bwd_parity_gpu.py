@@ -32,6 +32,9 @@ DENSE = [
     ("b_gqa", 44, 1, 257, 8, 2, 128, True),
     ("b_d64_causal", 45, 2, 389, 4, 1, 64, True),
     ("b_short", 46, 3, 17, 2, 1, 128, True),
+    ("b_d256_causal_ragged", 58, 2, 300, 4, 2, 256, True),
+    ("b_d256_noncausal", 59, 1, 257, 2, 1, 256, False),
+    ("b_d256_gqa_short", 60, 2, 45, 8, 2, 256, True),
 ]
 
 
@@ -49,6 +52,7 @@ VARLEN = [
     ("bv_mixed_causal", 48, [1, 127, 128, 129, 300, 64], 4, 2, 128, True),
     ("bv_mixed_dense", 49, [200, 0, 65, 256], 2, 2, 64, False),
     ("bv_gqa_d64", 50, [513, 31, 128], 8, 2, 64, True),
+    ("bv_gqa_d256", 61, [400, 1, 129, 260], 4, 2, 256, True),
 ]
 
 
@@ -77,6 +81,8 @@ MASKED = [
     ("bm_dense_shared", 52, 1, 600, 2, 2, 64, False, False, False, 0.4, None),
     ("bm_varlen", 53, 0, 0, 4, 2, 128, True, True, True, 0.6, [300, 513, 129]),
     ("bm_sparse", 54, 1, 1100, 2, 1, 128, False, False, False, 0.15, None),
+    ("bm_d256_causal_heads", 62, 2, 520, 4, 2, 256, True, True, True, 0.5, None),
+    ("bm_d256_varlen", 63, 0, 0, 2, 1, 256, False, True, False, 0.6, [300, 140]),
 ]
 
 
@@ -98,8 +104,9 @@ def test_bwd_mask_empty_rows_and_columns():
     assert np.all(dk[256:384] == 0) and np.all(dv[256:384] == 0)
 
 
-def test_bwd_deterministic():
-    w = W.make_dense("b_det", 56, 2, 333, 4, 2, 128, True)
+@pytest.mark.parametrize("d", [128, 256])
+def test_bwd_deterministic(d):
+    w = W.make_dense("b_det", 56, 2, 333, 4, 2, d, True)
     runs = P.run_gpu_bwd(w, W.make_dout(w), repeat=2)
     for a, b in zip(runs[0], runs[1]):
         assert np.array_equal(a, b)
