@@ -64,15 +64,20 @@ struct EntParams {
 enum { kPowGeneral = 0, kPowLinear = 1, kPowSquare = 2 };
 
 // u^e for u > 0 (0 otherwise)
+// (products without a branch; the transcendental pair behind one, which
+// skips it whenever no lane of the wave has u > 0 -- most scores, since only
+// those within 1/(alpha-1) of the row max can carry weight)
 template <int PK>
 __device__ __forceinline__ float powpos(float u, float e) {
-  if (!(u > 0.f)) return 0.f;
-  if constexpr (PK == kPowLinear)
-    return u;
-  else if constexpr (PK == kPowSquare)
-    return u * u;
-  else
+  if constexpr (PK == kPowLinear) {
+    return fmaxf(u, 0.f);
+  } else if constexpr (PK == kPowSquare) {
+    const float up = fmaxf(u, 0.f);
+    return up * up;
+  } else {
+    if (!(u > 0.f)) return 0.f;
     return __builtin_amdgcn_exp2f(e * __builtin_amdgcn_logf(u));
+  }
 }
 
 template <int kLoads>
@@ -174,9 +179,10 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
     asm volatile("" : "+v"(kabs[dc]));
   }
 
-  // S^T of one K tile: s[kt][i] is the score of key kv0 + 32 kt + 8 (i/4) +
-  // 4 hi + i%4 for this lane's row; keys past kv_end, after the row (causal)
-  // or rows past the end get -inf
+  // S^T of one K tile: s[kt][i] is q.k (unscaled: each pass folds the scale
+  // into its one FMA per score) of key kv0 + 32 kt + 8 (i/4) + 4 hi + i%4 for
+  // this lane's row; keys past kv_end, after the row (causal) or rows past the
+  // end get -inf, on the tiles that have such keys (the diagonal and tail)
   auto scores = [&](const int buf_off, int kv0, floatx16_t (&s)[kKt]) {
     {
       // operand reads (K tile at byte buf_off of the LDS) run kRing MFMAs
@@ -207,13 +213,17 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
         __builtin_amdgcn_sched_barrier(0);
       });
     }
+    const bool need_mask = (kv0 + kBN > kv_end) || (p.causal && kv0 + kBN - 1 > q0 + wave * 32) ||
+                           (q0 + wave * 32 + 32 > len);
+    if (need_mask) {
+      // key kv0 + 4 hi + o (o a compile-time offset) is visible when o <= lim
+      const int lim = (live ? (p.causal ? min(qrow, kv_end - 1) : kv_end - 1) : -1) - kv0 - hi * 4;
 #pragma unroll
-    for (int kt = 0; kt < kKt; ++kt)
+      for (int kt = 0; kt < kKt; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kv0 + kt * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-        s[kt][i] = (key >= kv_end || (p.causal && key > qrow) || !live) ? -INFINITY : s[kt][i] * p.scale;
-      }
+        for (int i = 0; i < 16; ++i)
+          if (kt * 32 + (i >> 2) * 8 + (i & 3) > lim) s[kt][i] = -INFINITY;
+    }
   };
 
   // One dense pass over the KV tiles: f(kv0, s) for each.
@@ -239,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) m = fmaxf(m, s[kt][i]);
   });
-  m = half_max(m);
+  m = half_max(m) * p.scale;  // (scale > 0)
   const int n_allowed = p.causal ? qrow + 1 : len;
 
   // ---- pass 2: histogram of the window [m - W, m]
@@ -248,15 +258,20 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   __syncthreads();
   const float base = m - W;
   const float inv_bw = kBins / W;
+  // bin of score z: (z - base) / bin width = fma(qk, scale / width, -base / width);
+  // bin b of a row sits at word b ^ (row % 32) of the row's kBins words, so
+  // the lanes of a wave that hit the same bin hit different LDS banks
+  const float h_mul = p.scale * inv_bw, h_add = -base * inv_bw;
+  const int swz = row & (kBins - 1);
   dense_pass([&](int, floatx16_t(&s)[kKt]) {
 #pragma unroll
     for (int kt = 0; kt < kKt; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float t = (s[kt][i] - base) * inv_bw;  // -inf for masked scores
+        const float t = __builtin_fmaf(s[kt][i], h_mul, h_add);  // -inf for masked scores
         if (t >= 0.f) {
           const int bin = min((int)t, kBins - 1);
-          atomicAdd(&hist[row * kBins + bin], 1u);
+          atomicAdd(&hist[row * kBins + (bin ^ swz)], 1u);
         }
       }
   });
@@ -264,7 +279,7 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   // the same counts, so both compute the same tau_h)
   float cnt[kBins];
 #pragma unroll
-  for (int bb = 0; bb < kBins; ++bb) cnt[bb] = (float)hist[row * kBins + bb];
+  for (int bb = 0; bb < kBins; ++bb) cnt[bb] = (float)hist[row * kBins + (bb ^ swz)];
   float lo = a1 * base - 1.f, hi_t = a1 * m;
   for (int it = 0; it < 30; ++it) {
     const float mid = 0.5f * (lo + hi_t);
@@ -287,11 +302,37 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
                                                      __builtin_amdgcn_logf((float)max(n_allowed, 1))),
                     tau_h + (1.f / kBins) * (1.f + 1e-4f) + 1e-6f * fabsf(tau_h));
   if (!(bhi > blo)) bhi = blo + 1e-6f * fmaxf(1.f, fabsf(blo));
-  float t = tau_h;
+  // Starting point: the histogram's root with every score counted at its
+  // bin's midpoint (between the lower- and upper-edge placements, so within
+  // [tau_h, tau_h + 1/B]), found by bisection in that bracket: an estimate
+  // close enough that one Halley or Newton step usually finishes the row.
+  float t;
+  {
+    float mlo = blo, mhi = bhi;
+    for (int it = 0; it < 14; ++it) {
+      const float mid = 0.5f * (mlo + mhi);
+      float sum = 0.f;
+#pragma unroll
+      for (int bb = 0; bb < kBins; ++bb)
+        sum += cnt[bb] * powpos<PK>(a1 * (base + (bb + 0.5f) * (W / kBins)) - mid, e);
+      if (sum >= 1.f)
+        mlo = mid;
+      else
+        mhi = mid;
+    }
+    t = 0.5f * (mlo + mhi);
+  }
   // regula falsi state (alpha > 2): g at the bracket ends, and which end moved last
   float glo = 0.f, ghi = 0.f;
   int side = 0;
   const float kTol = 4e-6f;  // |sum p - 1| at which a row counts as converged (fp32 sums)
+  // Newton (alpha <= 2) and Halley (alpha <= 1.5) converge quadratically and
+  // cubically: once |sum p - 1| is below this at the current tau, the step
+  // taken from it lands within fp32 rounding of the root, so the row takes it
+  // and stops without another pass to confirm it.
+  const float kStepTol = p.alpha <= 1.5f ? 1e-2f : 2e-3f;
+  const float zs = a1 * p.scale;  // (alpha - 1) z = zs * q.k
+  bool final_step = false;  // the row took its last step
   const int m_words = (n_kblk + 31) / 32;
   for (int r = 0; r < p.n_iter; ++r) {
     const bool first = r == 0;
@@ -307,33 +348,33 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
       for (int kt = 0; kt < kKt; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float u = a1 * s[kt][i] - t;
+          const float u = __builtin_fmaf(s[kt][i], zs, -t);
           tmax = fmaxf(tmax, s[kt][i]);
-          if (u > 0.f) {
-            // s0 = sum u^e, s1 = sum u^(e-1), s2 = sum u^(e-2) (the last two
-            // only where the step uses them)
-            if constexpr (PK == kPowSquare) {
-              s0 += u * u;
-              s1 += u;
-              s2 += 1.f;
-            } else if constexpr (PK == kPowLinear) {
-              s0 += u;
-              s1 += 1.f;
-            } else {
-              const float pu = powpos<PK>(u, e);
-              s0 += pu;
-              if (p.alpha <= 2.f) {
-                const float ru = __builtin_amdgcn_rcpf(u);
-                const float r1 = pu * ru;
-                s1 += r1;
-                if (p.alpha <= 1.5f) s2 += r1 * ru;
-              }
+          // s0 = sum u^e, s1 = sum u^(e-1), s2 = sum u^(e-2) over u > 0 (the
+          // last two only where the step uses them), without branches
+          const float up = fmaxf(u, 0.f);
+          const float pos = u > 0.f ? 1.f : 0.f;
+          if constexpr (PK == kPowSquare) {
+            s0 = __builtin_fmaf(up, up, s0);
+            s1 += up;
+            s2 += pos;
+          } else if constexpr (PK == kPowLinear) {
+            s0 += up;
+            s1 += pos;
+          } else if (u > 0.f) {
+            const float pu = powpos<PK>(u, e);
+            s0 += pu;
+            if (p.alpha <= 2.f) {
+              const float ru = __builtin_amdgcn_rcpf(u);
+              const float r1 = pu * ru;
+              s1 += r1;
+              if (p.alpha <= 1.5f) s2 += r1 * ru;
             }
           }
-          if (p.alpha > 2.f && first) shi += powpos<PK>(a1 * s[kt][i] - bhi, e);  // g at the upper end
+          if (p.alpha > 2.f && first) shi += powpos<PK>(__builtin_fmaf(s[kt][i], zs, -bhi), e);  // g at the upper end
         }
       // mark the 128-key block if some live row's scores clear t_mask
-      const bool any = __builtin_amdgcn_ballot_w64(live && a1 * tmax > t_mask) != 0;
+      const bool any = __builtin_amdgcn_ballot_w64(live && zs * tmax > t_mask) != 0;
       if (any && lane == 0) atomicOr(&mbits[kv0 / kListBlock / 32], 1u << ((kv0 / kListBlock) % 32));
     });
     s0 = half_sum(s0);
@@ -341,36 +382,44 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
     s2 = half_sum(s2);
     const float g = s0 - 1.f;
     if (p.alpha > 2.f && first) ghi = half_sum(shi) - 1.f;
-    const bool conv = fabsf(g) <= kTol;  // converged: keep t (the bracket may have closed on it)
-    // the workgroup stops once every live row has converged
-    const bool wave_done = __builtin_amdgcn_ballot_w64(live && !conv) == 0;
+    // converged: keep t (the bracket may have closed on it); a row that took
+    // its final step keeps the t that step gave; a bracket closed to fp32
+    // resolution cannot narrow further
+    const bool conv = final_step || fabsf(g) <= kTol || bhi - blo <= 4e-7f * fmaxf(1.f, fabsf(t));
+    // close enough for one more Newton / Halley step to land on the root
+    const bool last = !conv && p.alpha <= 2.f && fabsf(g) <= kStepTol;
+    if (!conv) {
+      if (g > 0.f) {
+        blo = t;
+        glo = g;
+        if (side == 1) ghi *= 0.5f;  // Illinois: the other end stayed twice
+        side = 1;
+      } else {
+        bhi = t;
+        ghi = g;
+        if (side == -1) glo *= 0.5f;
+        side = -1;
+      }
+      float t_new;
+      if (p.alpha <= 1.5f) {  // Halley
+        const float g1 = -e * s1, g2 = e * (e - 1.f) * s2;
+        t_new = t - 2.f * g * g1 / (2.f * g1 * g1 - g * g2);
+      } else if (p.alpha <= 2.f) {  // Newton
+        t_new = t - g / (-e * s1);
+      } else {  // secant through the bracket ends (regula falsi)
+        t_new = ghi < glo ? blo - glo * (bhi - blo) / (ghi - glo) : 0.5f * (blo + bhi);
+      }
+      const bool inside = t_new >= blo && t_new <= bhi;
+      t = inside ? t_new : 0.5f * (blo + bhi);  // bisection fallback (then not a last step)
+      final_step = last && inside;
+    }
+    // the workgroup stops once every live row has converged or taken its last step
+    const bool wave_done = __builtin_amdgcn_ballot_w64(live && !conv && !final_step) == 0;
     if (lane == 0) done_flag[wave] = wave_done ? 1u : 0u;
     __syncthreads();
     const bool all_done = done_flag[0] & done_flag[1] & done_flag[2] & done_flag[3];
     if (all_done) break;
-    if (conv) continue;
-    if (g > 0.f) {
-      blo = t;
-      glo = g;
-      if (side == 1) ghi *= 0.5f;  // Illinois: the other end stayed twice
-      side = 1;
-    } else {
-      bhi = t;
-      ghi = g;
-      if (side == -1) glo *= 0.5f;
-      side = -1;
-    }
-    float t_new;
-    if (p.alpha <= 1.5f) {  // Halley
-      const float g1 = -e * s1, g2 = e * (e - 1.f) * s2;
-      t_new = t - 2.f * g * g1 / (2.f * g1 * g1 - g * g2);
-    } else if (p.alpha <= 2.f) {  // Newton
-      t_new = t - g / (-e * s1);
-    } else {  // secant through the bracket ends (regula falsi)
-      t_new = ghi < glo ? blo - glo * (bhi - blo) / (ghi - glo) : 0.5f * (blo + bhi);
-    }
-    if (!(t_new >= blo && t_new <= bhi)) t_new = 0.5f * (blo + bhi);  // bisection fallback
-    t = t_new;
+    // (the flags are rewritten only after the next pass's barriers)
   }
   __syncthreads();  // the mask is complete
 
@@ -420,7 +469,7 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
     for (int kt = 0; kt < kKt; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = powpos<PK>(a1 * s[kt][i] - t, e);
+        const float pv = powpos<PK>(__builtin_fmaf(s[kt][i], zs, -t), e);
         l += pv;
         pb[kt][i >> 3][i & 7] = (__bf16)pv;
       }
