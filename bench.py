@@ -328,6 +328,78 @@ def time_backward(attn, torch, w, q, k, v, cu, sp, out, lse, flops, n, settle_ms
             "kernels": "attn_bwd_dq_kernel then attn_bwd_dkdv_kernel"}
 
 
+def results_table(attn, torch, P, settle_ms: float):
+    """One measured row per workload (tiny, mha, gqa, varlen D=64/128/256, the 128K
+    block list and its dense leg): errors against the fp64 oracle, kernel time
+    warm (back to back) and cold (caches evicted), TFLOP/s and % of the bf16
+    peak, and the oracle's CPU time.  Printed as a markdown table.
+
+    Parity is over every output for tiny, mha and gqa; for the packed varlen
+    workloads over every row of one query head per KV head (the oracle time is
+    that of those heads, scaled by Hq / Hkv to all heads); for the 128K list over
+    its 256 checked rows on all heads (scaled by counted pairs to the full run).
+    """
+    import oracle
+
+    threads = oracle.default_threads()
+    rows_md = []
+    for name in ("tiny", "mha", "gqa", "varlen_d64", "varlen_d128", "varlen_d256", "sparse"):
+        w = W.make(name)
+        t = P.to_device(w)
+        q, cu = t[0], t[3]
+        out = torch.empty_like(q)
+        lse = lse_buffer(torch, w, q, cu)
+        legs = [("", fwd_step(attn, w, t, out, lse), W.counted_flops(w))]
+        if name == "sparse":
+            wd = W.Workload(w.name, w.seed, w.batch, w.seqlen, w.hq, w.hkv, w.d, w.causal, w.scale, w.q, w.k, w.v)
+            legs.append((" (dense causal, same inputs)", fwd_step(attn, w, t, out, lse, dense=True),
+                         W.counted_flops(wd)))
+        timing = []
+        for label, step, flops in legs:
+            settle(torch, step, settle_ms)
+            one = time_back_to_back(torch, step, 1)
+            warm = time_back_to_back(torch, step, max(3, min(200, int(300.0 / max(one, 1e-3)))))
+            cold = time_cold(torch, step, 5, q.device)
+            timing.append((label, flops, warm, cold))
+        # parity: the run of the workload's own step (the first leg)
+        legs[0][1]()
+        torch.cuda.synchronize()
+        o, l = P.run_gpu(w, tensors=t)
+        t0 = time.perf_counter()
+        if name in ("tiny", "mha", "gqa"):
+            o_ref, l_ref = oracle.run_workload(w, nthreads=threads)
+            cpu_s = time.perf_counter() - t0
+            st = P.compare(o, l, o_ref, l_ref, name)
+            cpu_note = f"{cpu_s:.1f} s"
+        elif name.startswith("varlen"):
+            heads = P.one_head_per_kv_head(w)
+            o_ref, l_ref = P.oracle_heads(w, heads, nthreads=threads)
+            cpu_s = (time.perf_counter() - t0) * w.hq / len(heads)
+            st = P.compare(o[:, heads], l[:, heads], o_ref, l_ref, name)
+            cpu_note = f"{cpu_s:.0f} s (from {len(heads)} of {w.hq} heads)"
+        else:
+            rows = w.sample_rows
+            o_ref, l_ref = oracle.run_workload(w, rows=rows, nthreads=threads)
+            spent = time.perf_counter() - t0
+            cpu_s = spent * (W.counted_flops(w) / (4.0 * w.d * w.hq)) / float(row_pairs(w, rows).sum())
+            st = P.compare(o[rows], l[rows], o_ref, l_ref, name)
+            cpu_note = f"{spent:.1f} s for {len(rows)} rows; {cpu_s:.0f} s full run (extrapolated)"
+        for i, (label, flops, warm, cold) in enumerate(timing):
+            tf = flops / warm / 1e9
+            err = (f"{st['o_max_abs']:.2e} | {st['o_mean_abs']:.2e} | {st['lse_max_abs']:.2e}" if i == 0
+                   else "— | — | —")
+            rows_md.append(f"| {name}{label} | {err} | {warm:.4f} / {cold[0]:.4f} | {tf:.1f} | "
+                           f"{100 * tf / PEAK_BF16_TFLOPS:.1f} | {cpu_note if i == 0 else '—'} |")
+            log(rows_md[-1])
+        del t, q, out, lse
+        torch.cuda.empty_cache()
+    head = ("| config | O max abs err | O mean abs err | LSE max abs err | kernel ms warm / cold (median) | "
+            "TFLOP/s (warm) | % of bf16 peak | CPU oracle time (" + str(threads) + " threads) |\n"
+            "|---|---|---|---|---|---|---|---|")
+    print(head)
+    print("\n".join(rows_md), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -350,6 +422,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    ap.add_argument("--results-table", action="store_true",
+                    help="measure every workload once (errors against the oracle, warm and cold kernel time, "
+                         "TFLOP/s, CPU oracle time) and print a markdown table instead of the JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention forward here is a "
@@ -375,6 +450,9 @@ def main():
     from tests import _parity as P
 
     log(f"library {attn.LIB_PATH} built from sources {attn.source_sha()} (forward kernel {kernel_hash()})")
+    if args.results_table:
+        results_table(attn, torch, P, args.settle_ms)
+        return
     t_gen = time.perf_counter()
     w = W.make(args.workload)
     flops = W.counted_flops(w)
