@@ -151,23 +151,42 @@ __device__ __forceinline__ void decode_tile(const Params &p, bool heavy_first, i
 // Direct global -> LDS loads of the rows of one K or V tile.  Each wave-wide
 // load writes 64 consecutive 16 B LDS slots; each lane fetches the global
 // chunk that the swizzled layout places in its slot.  The per-lane part of the
-// global offset (off: row lrow of the tile) is fixed for the whole kernel; only
-// the tile's start row changes.  In a tile that runs past the end of the
-// sequence the missing rows re-read the last row (finite data; those keys are
-// masked).
+// global offset (off, in bytes: row lrow0 + n * (64 / kChunks) of the tile for
+// load n) is fixed for the whole kernel and fits 32 bits (the host bounds the
+// row stride); only the tile's start address t0, uniform over the wave,
+// changes, so each load takes one 32-bit register offset from a scalar base.
+// In a tile that runs past the end of the sequence the missing rows re-read
+// the last row (finite data; those keys are masked).
 template <class C>
-__device__ __forceinline__ void issue_rows(char *dst, const uint16_t *t0, const int64_t *off,
-                                           const int *lrow, int64_t ss, int rows_left) {
+__device__ __forceinline__ void issue_rows(char *dst, const char *t0, const uint32_t *off, int lrow0,
+                                           uint32_t ss_bytes, int rows_left) {
   constexpr int kLoads = C::kLoads;
+  constexpr int kRowStep = 64 / (C::D / 8);  // tile rows between a lane's consecutive loads
+  // (the empty asm keeps each offset a 32-bit value at its load: widened
+  // outside the loop it would take a register pair and the 64-bit address form)
   if (rows_left >= C::kBN) {
 #pragma unroll
-    for (int n = 0; n < kLoads; ++n)
-      __builtin_amdgcn_global_load_lds(t0 + off[n], (lds_void_t *)(dst + n * 1024), 16, 0, 0);
+    for (int n = 0; n < kLoads; ++n) {
+      uint32_t o = off[n];
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(t0 + o, (lds_void_t *)(dst + n * 1024), 16, 0, 0);
+    }
   } else {
+    // Rows from r_last + 1 on re-read row r_last (the sequence's last row,
+    // relative to t0).  A tile that starts at or past the end (a sub-tile of a
+    // ragged last block of a block list or mask: rows_left <= 0) has r_last < 0;
+    // its base then moves back to that row, so that every lane steps back by
+    // at most its own row and the unsigned offset stays >= 0.
+    const int r_last = rows_left - 1;
+    const int base_row = min(r_last, 0);
+    const char *const tb = t0 + (int64_t)base_row * ss_bytes;
 #pragma unroll
     for (int n = 0; n < kLoads; ++n) {
-      const int64_t back = min(rows_left - 1 - lrow[n], 0);  // rows to step back
-      __builtin_amdgcn_global_load_lds(t0 + off[n] + back * ss, (lds_void_t *)(dst + n * 1024), 16, 0, 0);
+      const int lrow = lrow0 + n * kRowStep;
+      const uint32_t back = (uint32_t)(max(lrow - r_last, 0) + base_row);  // 0 <= back <= lrow
+      uint32_t o = off[n] - back * ss_bytes;
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(tb + o, (lds_void_t *)(dst + n * 1024), 16, 0, 0);
     }
   }
 }
@@ -194,13 +213,17 @@ __device__ __forceinline__ void stage_q_rows(char *dst, const uint16_t *qg, int6
 
 // One KV tile (K then V) into one LDS buffer.
 template <class C>
-__device__ __forceinline__ void issue_tile(char *kb, char *vb, const uint16_t *kt0,
-                                           const uint16_t *vt0, const int64_t *koff,
-                                           const int64_t *voff, const int *lrow, int64_t k_ss,
-                                           int64_t v_ss, int rows_left) {
-  issue_rows<C>(kb, kt0, koff, lrow, k_ss, rows_left);
-  issue_rows<C>(vb, vt0, voff, lrow, v_ss, rows_left);
+__device__ __forceinline__ void issue_tile(char *kb, char *vb, const char *kt0, const char *vt0,
+                                           const uint32_t *koff, const uint32_t *voff, int lrow0,
+                                           uint32_t k_ssb, uint32_t v_ssb, int rows_left) {
+  issue_rows<C>(kb, kt0, koff, lrow0, k_ssb, rows_left);
+  issue_rows<C>(vb, vt0, voff, lrow0, v_ssb, rows_left);
 }
+
+// Byte distance between the V operand offsets of output tile dt and of tile
+// dt % kVRegs (the V pair swizzle repeats every kVRegs tiles of 32 columns).
+template <int kVRegs>
+__host__ __device__ constexpr int v_imm(int dt) { return (dt / kVRegs) * kVRegs * 64; }
 
 // Operand steps of one MFMA phase of the pipelined dense loop: scores of one
 // tile and PV of the previous one interleaved (kBoth), or one of them alone.
@@ -365,20 +388,26 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   // changes.  In a tile that runs past the end of the sequence the missing
   // rows re-read the last row (finite data; those keys are masked).
   constexpr int kLoads = C::kLoads;
-  int64_t koff[kLoads], voff[kLoads];
-  int lrow[kLoads];
+  static_assert(64 % L::kChunks == 0, "a wave-wide load covers whole rows");
+  uint32_t koff[kLoads], voff[kLoads];  // byte offsets within a tile's rows
   // waves past the loading ones issue no loads (their offsets are unused)
   const bool loader = C::NW <= C::kLoadWaves || wave < C::kLoadWaves;
   const int lwave = wave % C::kLoadWaves;
   const int slot_byte0 = lwave * kLoads * 1024;  // this wave's first LDS slot in a tile
+  const int lrow0 = (lwave * kLoads * 64 + lane) / L::kChunks;  // row of this lane's first load
+  const uint32_t k_ssb = (uint32_t)p.k_ss * 2u, v_ssb = (uint32_t)p.v_ss * 2u;  // row strides in bytes
 #pragma unroll
   for (int n = 0; n < kLoads; ++n) {
     const int slot = (lwave * kLoads + n) * 64 + lane;
     const int r = slot / L::kChunks, pc = slot % L::kChunks;
-    lrow[n] = r;
-    koff[n] = (int64_t)r * p.k_ss + (pc ^ L::kswz(r)) * 8;
-    voff[n] = (int64_t)r * p.v_ss + L::v_logical_chunk(r, pc) * 8;
+    koff[n] = (uint32_t)r * k_ssb + (uint32_t)(pc ^ L::kswz(r)) * 16u;
+    voff[n] = (uint32_t)r * v_ssb + (uint32_t)L::v_logical_chunk(r, pc) * 16u;
   }
+  // tile base addresses (bytes), uniform over the workgroup
+  const char *const kgb = reinterpret_cast<const char *>(kg);
+  const char *const vgb = reinterpret_cast<const char *>(vg);
+  auto kt_at = [&](int pos) { return kgb + (int64_t)pos * k_ssb; };
+  auto vt_at = [&](int pos) { return vgb + (int64_t)pos * v_ssb; };
 
   floatx16_t oacc[kDt];
 #pragma unroll
@@ -450,13 +479,13 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   if constexpr (kPipe) {
     if (n_iter > 0) {
       walk(lp[0], mp[1]);
-      if (loader) issue_rows<C>(smem + kslot(0) + slot_byte0, kg + (int64_t)lp[0] * p.k_ss, koff, lrow, p.k_ss, len - lp[0]);
+      if (loader) issue_rows<C>(smem + kslot(0) + slot_byte0, kt_at(lp[0]), koff, lrow0, k_ssb, len - lp[0]);
     }
   } else {
     kv_cur = n_iter > 0 ? kv_start(0) : -1;
     if (kv_cur >= 0 && loader)
-      issue_tile<C>(smem + slot_byte0, smem + kTileBytes + slot_byte0, kg + (int64_t)kv_cur * p.k_ss,
-                    vg + (int64_t)kv_cur * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_cur);
+      issue_tile<C>(smem + slot_byte0, smem + kTileBytes + slot_byte0, kt_at(kv_cur), vt_at(kv_cur), koff, voff,
+                    lrow0, k_ssb, v_ssb, len - kv_cur);
   }
 
   // ---- Q rows of this wave, the MFMA B operand (lane l32 holds head-dim
@@ -481,10 +510,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         if (n_iter > 1) {
           walk(lp[1], mp[2]);
           if (loader)
-            issue_rows<C>(smem + kslot(1) + slot_byte0, kg + (int64_t)lp[1] * p.k_ss, koff, lrow, p.k_ss, len - lp[1]);
+            issue_rows<C>(smem + kslot(1) + slot_byte0, kt_at(lp[1]), koff, lrow0, k_ssb, len - lp[1]);
         }
         if (loader)
-          issue_rows<C>(smem + vslot(0) + slot_byte0, vg + (int64_t)lp[0] * p.v_ss, voff, lrow, p.v_ss, len - lp[0]);
+          issue_rows<C>(smem + vslot(0) + slot_byte0, vt_at(lp[0]), voff, lrow0, v_ssb, len - lp[0]);
       }
     }
   } else {
@@ -502,21 +531,44 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   // rows (V), so every other read is one of these plus a compile-time row
   // offset.  The empty asm keeps each offset in one register (otherwise the
   // compiler re-splits it into row and chunk parts and re-adds them per read).
-  int kaddr[kDc], vaddr[kDt];
-  uint32_t klds[kDc], vlds[kDt];
+  // K: k-step dc reads chunk 2 dc + hi of row l32, stored at chunk
+  // (2 dc + hi) ^ swz = (hi ^ swz) ^ 2 dc; the row part of the offset has no
+  // bits below the row size, so k-step dc's offset is k-step 0's with dc << 5
+  // XORed in.  At head_dim 256 (16 k-steps, one wave per SIMD, where every
+  // register counts) the reads form it so, one XOR each; the other head dims
+  // keep one register per k-step.
+  // V: the pair swizzle takes kPairSwz values, so the offsets of output tiles
+  // dt and dt + kPairSwz differ by a constant: kPairSwz registers suffice.
+  constexpr bool kKXor = D == 256;
+  constexpr int kKRegs = kKXor ? 1 : kDc;
+  constexpr int kVRegs = L::kPairSwz < kDt ? L::kPairSwz : kDt;
+  int kaddr[kKRegs];
+  uint32_t klds[kKRegs], vlds[kVRegs];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char_t *)smem;
 #pragma unroll
-  for (int dc = 0; dc < kDc; ++dc) {
+  for (int dc = 0; dc < kKRegs; ++dc) {
     kaddr[dc] = L::kq(l32, dc * 2 + hi);
     asm volatile("" : "+v"(kaddr[dc]));
     klds[dc] = smem_lds + (uint32_t)kaddr[dc];
   }
 #pragma unroll
-  for (int dt = 0; dt < kDt; ++dt) {
-    vaddr[dt] = L::vv(4 * hi + (j16 >> 2), 2 * dt + (l32 >> 4), (j16 & 3) * 8);
-    asm volatile("" : "+v"(vaddr[dt]));
-    vlds[dt] = smem_lds + (kPipe ? (uint32_t)vslot(0) : 0u) + (uint32_t)vaddr[dt];
+  for (int dt = 0; dt < kVRegs; ++dt) {
+    int vaddr = L::vv(4 * hi + (j16 >> 2), 2 * dt + (l32 >> 4), (j16 & 3) * 8);
+    asm volatile("" : "+v"(vaddr));
+    vlds[dt] = smem_lds + (kPipe ? (uint32_t)vslot(0) : 0u) + (uint32_t)vaddr;
   }
+  // Offset of k-step dc's K operand from the start of a K tile, given k0 =
+  // klds[0] (with kKXor the caller passes a copy made opaque in its own loop
+  // body, so that the XORs are not hoisted out into kDc live registers).
+  auto k_at = [&](uint32_t k0, int dc) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (kKXor) return k0 ^ (uint32_t)(dc << 5);
+    else return klds[dc];
+  };
+  auto k_base = [&]() __attribute__((always_inline)) -> uint32_t {
+    uint32_t k0 = klds[0];
+    if constexpr (kKXor) asm volatile("" : "+v"(k0));
+    return k0;
+  };
 
   // ---- online softmax of one score tile whose first key is kv0 (base 2,
   // scale folded into c): masks the causal diagonal and the sequence tail
@@ -607,12 +659,15 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     // were issued one iteration before the loads of iteration j-1, which may
     // stay in flight (2 kLoads per loading wave when that iteration issued
     // both tiles); with two, they are the last loads issued.
+    // The barrier is a bare s_barrier (a compiler memory barrier, no fence):
+    // the waits above are the ones the ring needs, and a workgroup fence makes
+    // the compiler wait for every load in flight (vmcnt(0)) as well.
     auto sync = [&](const int j) __attribute__((always_inline)) {
       if (kStages == 3 && loader && j + 1 < n_iter)
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * C::kLoads));
       else
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      __syncthreads();
+      asm volatile("s_barrier" ::: "memory");
     };
     // iteration j's loads: K(j + kStages - 1) (walking on to that tile) and
     // V(j + kStages - 2)
@@ -621,12 +676,12 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       if (j + kAhead < n_iter) {
         walk(lp[kAhead], mp[kAhead + 1]);
         if (loader)
-          issue_rows<C>(smem + kslot((j + kAhead) % kStages) + slot_byte0, kg + (int64_t)lp[kAhead] * p.k_ss,
-                        koff, lrow, p.k_ss, len - lp[kAhead]);
+          issue_rows<C>(smem + kslot((j + kAhead) % kStages) + slot_byte0, kt_at(lp[kAhead]), koff, lrow0, k_ssb,
+                        len - lp[kAhead]);
       }
       if (j + kAhead - 1 < n_iter && loader)
-        issue_rows<C>(smem + vslot((j + kAhead - 1) % kStages) + slot_byte0, vg + (int64_t)lp[kAhead - 1] * p.v_ss,
-                      voff, lrow, p.v_ss, len - lp[kAhead - 1]);
+        issue_rows<C>(smem + vslot((j + kAhead - 1) % kStages) + slot_byte0, vt_at(lp[kAhead - 1]), voff, lrow0,
+                      v_ssb, len - lp[kAhead - 1]);
     };
     // end of iteration j: tile j + 1 becomes the current one
     auto shift = [&]() __attribute__((always_inline)) {
@@ -646,13 +701,14 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       static_assert(kW != kBoth || kNs == kNp, "score and PV steps must pair up");
       constexpr int kN = kW == kBoth ? kNs + kNp : (kW == kOnlyS ? kNs : kNp);
       constexpr int kRing = 4;
+      const uint32_t k0 = k_base();
       auto load = [&](auto T) __attribute__((always_inline)) -> bf16x8_t {
         constexpr int t = decltype(T)::value;
         constexpr int x = step_idx(kW, t);
         if constexpr (step_kind(kW, t) == 0)
-          return ld_b128<kKb * kTileBytes + (x % kKt) * 32 * L::kRowBytes>(klds[x / kKt]);
+          return ld_b128<kKb * kTileBytes + (x % kKt) * 32 * L::kRowBytes>(k_at(k0, x / kKt));
         else
-          return tr_pair<kVb * kTileBytes + tr_off<L, kDt>(x), 8 * L::kRowBytes>(vlds[x % kDt]);
+          return tr_pair<kVb * kTileBytes + tr_off<L, kDt>(x) + v_imm<kVRegs>(x % kDt), 8 * L::kRowBytes>(vlds[(x % kDt) % kVRegs]);
       };
       bf16x8_t ring[kRing];
       static_for<kRing>([&](auto T) {
@@ -683,7 +739,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     issue(0);
 #pragma unroll
     for (int dc = 0; dc < kDc; ++dc)
-      qreg[dc] = *reinterpret_cast<const bf16x8_t *>(q_stage + kaddr[dc]);
+      qreg[dc] = *reinterpret_cast<const bf16x8_t *>(q_stage + (kKXor ? (kaddr[0] ^ (dc << 5)) : kaddr[dc]));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     phase(BufTag<0>{}, BufTag<0>{}, std::integral_constant<int, kOnlyS>{});
     // Calls body(BufTag<j % kStages>) (the slots of an iteration are
@@ -719,7 +775,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         float rs = 0.f;
         auto load = [&](auto T) __attribute__((always_inline)) -> bf16x8_t {
           constexpr int t = decltype(T)::value;
-          return tr_pair<kVb * kTileBytes + tr_off<L, kDt>(t), 8 * L::kRowBytes>(vlds[t % kDt]);
+          return tr_pair<kVb * kTileBytes + tr_off<L, kDt>(t) + v_imm<kVRegs>(t % kDt), 8 * L::kRowBytes>(vlds[(t % kDt) % kVRegs]);
         };
         bf16x8_t ring[kRing];
         static_for<kRing>([&](auto T) { ring[decltype(T)::value] = load(T); });
@@ -732,7 +788,11 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
           if constexpr (kPd >= 0) {
             static_for<kE>([&](auto E) {
               constexpr int e = i * kE + decltype(E)::value;  // score e % 16 of tile e / 16
-              const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e / 16][e % 16], p.c, -m_use));
+              float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e / 16][e % 16], p.c, -m_use));
+              // (the volatile asm pins the exp2 here: on a wave's first tiles its
+              // result is dropped for the slow path's, and the compiler would
+              // otherwise move all of them into a branch after the MFMAs)
+              asm volatile("" : "+v"(pv));
               rs += pv;
               pp[kPd][e / 16][(e % 16) >> 3][e & 7] = (__bf16)pv;
             });
@@ -828,8 +888,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         kv_nxt = kv_start(it + 1);
         if (kv_nxt >= 0) {
           char *buf = smem + (1 - kBuf) * kBufBytes;
-          issue_tile<C>(buf + slot_byte0, buf + kTileBytes + slot_byte0, kg + (int64_t)kv_nxt * p.k_ss,
-                        vg + (int64_t)kv_nxt * p.v_ss, koff, voff, lrow, p.k_ss, p.v_ss, len - kv_nxt);
+          issue_tile<C>(buf + slot_byte0, buf + kTileBytes + slot_byte0, kt_at(kv_nxt), vt_at(kv_nxt), koff, voff,
+                        lrow0, k_ssb, v_ssb, len - kv_nxt);
         }
       }
       const int kv0 = kv_cur;
@@ -846,9 +906,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         // latency nor the MFMA dependency latency is exposed
         constexpr int kRing = 4;
         constexpr int kSteps = kKt * kDc;  // step i: kt = i % kKt, dc = i / kKt
+        const uint32_t k0 = k_base();
         auto load = [&](auto T) __attribute__((always_inline)) -> bf16x8_t {
           constexpr int t = decltype(T)::value;
-          return ld_b128<kBuf * kBufBytes + (t % kKt) * 32 * L::kRowBytes>(klds[t / kKt]);
+          return ld_b128<kBuf * kBufBytes + (t % kKt) * 32 * L::kRowBytes>(k_at(k0, t / kKt));
         };
         bf16x8_t ring[kRing];
         static_for<kRing>([&](auto T) { ring[decltype(T)::value] = load(T); });
@@ -880,7 +941,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         bf16x8_t ring[kRing];
         static_for<kRing>([&](auto I) {
           constexpr int i = decltype(I)::value;
-          ring[i] = tr_pair<kVOff + tr_off<L, kDt>(i), 8 * L::kRowBytes>(vlds[i % kDt]);
+          ring[i] = tr_pair<kVOff + tr_off<L, kDt>(i) + v_imm<kVRegs>(i % kDt), 8 * L::kRowBytes>(vlds[(i % kDt) % kVRegs]);
         });
         static_for<kSteps>([&](auto I) {
           constexpr int i = decltype(I)::value;
@@ -890,7 +951,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
           lgkm_wait<2 * (kSteps - 1 - i < kRing - 1 ? kSteps - 1 - i : kRing - 1)>(ring[i % kRing]);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % kRing], pb[kt][c], oacc[dt], 0, 0, 0);
           if constexpr (i + kRing < kSteps)
-            ring[i % kRing] = tr_pair<kVOff + tr_off<L, kDt>(i + kRing), 8 * L::kRowBytes>(vlds[(i + kRing) % kDt]);
+            ring[i % kRing] = tr_pair<kVOff + tr_off<L, kDt>(i + kRing) + v_imm<kVRegs>((i + kRing) % kDt), 8 * L::kRowBytes>(
+                vlds[((i + kRing) % kDt) % kVRegs]);
           __builtin_amdgcn_sched_barrier(0);
         });
       }
@@ -995,6 +1057,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
 // ---------------------------------------------------------------------------
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 bool stride_ok(int64_t s) { return ((s * 2) % 16) == 0; }
+// K and V row strides: the kernels address a tile's rows with 32-bit byte
+// offsets from the tile's first row
+constexpr int64_t kMaxKvRowStride = int64_t(1) << 24;  // elements
 
 int validate(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
              const int32_t *cu_seqlens, int causal, float scale, const attn_block_list_t *bl,
@@ -1034,6 +1099,8 @@ int validate(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t
     if (!stride_ok(t->stride_seq) || !stride_ok(t->stride_head)) return ATTN_ERR_UNSUPPORTED;
     if (!cu_seqlens && !stride_ok(t->stride_batch)) return ATTN_ERR_UNSUPPORTED;
   }
+  for (const attn_tensor_t *t : {k, v})
+    if (t->stride_seq < 0 || t->stride_seq >= kMaxKvRowStride) return ATTN_ERR_UNSUPPORTED;
   if (!empty) {
     const int64_t tiles = (q->seqlen + 127) / 128;
     if (tiles * (int64_t)q->batch * q->heads > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;

@@ -131,6 +131,7 @@ enum {
  *                         non-finite scale, bad block-list descriptor
  *   ATTN_ERR_UNSUPPORTED  head_dim not in {64, 128, 256}; scale <= 0; data
  *                         pointer or any stride*2 not a multiple of 16 bytes;
+ *                         a k or v stride_seq outside [0, 2^24) elements;
  *                         block sizes other than 128; a block list combined
  *                         with cu_seqlens or batch > 1; a launch grid beyond
  *                         2^31 - 1 workgroups

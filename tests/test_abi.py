@@ -72,6 +72,9 @@ def validate(q, k, v, cu=None, causal=1, scale=0.125, bl=None, out=None):
 
 def test_valid_arguments_pass():
     assert validate(desc(), desc(h=2), desc(h=2)) == 0
+    k, v = desc(h=2), desc(h=2)
+    k.stride_seq = v.stride_seq = (1 << 24) - 8  # the largest K/V row stride accepted
+    assert validate(desc(), k, v) == 0
     assert validate(desc(layout="bhsd"), desc(h=8, layout="bhsd"), desc(h=8, layout="bhsd")) == 0
     for d in (64, 128, 256):
         assert validate(desc(d=d), desc(d=d, h=4), desc(d=d, h=4)) == 0
@@ -87,6 +90,8 @@ def test_valid_arguments_pass():
     (lambda q, k, v: [setattr(t, "head_dim", 96) for t in (q, k, v)], -2),  # unsupported D (out too)
     (lambda q, k, v: setattr(q, "data", FAKE + 8), -2),       # misaligned pointer
     (lambda q, k, v: setattr(k, "stride_seq", 2 * 128 + 4), -2),  # stride*2 not multiple of 16
+    (lambda q, k, v: setattr(k, "stride_seq", 1 << 24), -2),   # K rows too far apart for 32-bit offsets
+    (lambda q, k, v: setattr(v, "stride_seq", -256), -2),      # negative V row stride
     (lambda q, k, v: setattr(q, "batch", -1), -1),
 ])
 def test_invalid_arguments(mut, code):
