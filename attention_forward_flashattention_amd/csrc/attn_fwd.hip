@@ -148,6 +148,16 @@ __device__ __forceinline__ void decode_tile(const Params &p, bool heavy_first, i
   tile = heavy_first ? p.n_tiles - 1 - rank : rank;
 }
 
+// A wave-uniform read of the block list or the block mask, through the
+// constant address space: neither is written while a kernel runs, so the
+// compiler may use a scalar load.  (A plain load in the main loop, after
+// direct-to-LDS loads that it cannot tell from stores, becomes a vector load
+// that the wave waits for at once: a full memory latency per list entry.)
+template <class T>
+__device__ __forceinline__ T ld_uniform(const T *base, int64_t i) {
+  return ((const __attribute__((address_space(4))) T *)base)[i];
+}
+
 // Direct global -> LDS loads of the rows of one K or V tile.  Each wave-wide
 // load writes 64 consecutive 16 B LDS slots; each lane fetches the global
 // chunk that the swizzled layout places in its slot.  The per-lane part of the
@@ -258,14 +268,14 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   // own, so a wave can write out its rows while others still read K/V.
   constexpr bool kOwnStage = C::kMinBlocks == 1;
   constexpr int kStageBytes = C::NW * 32 * D * 2;
-  constexpr int kFlagBytes = OSK ? 16 : 0;  // one stop flag per wave
+  constexpr int kFlagBytes = OSK ? 4 * C::NW : 0;  // one stop flag per wave
   // Problems with two waves per SIMD from one workgroup (dense, or the
-  // paired block-list and block-mask kernels) run the software-pipelined loop
-  // below, and so does head_dim 256 (one wave per SIMD, in its solo form); the
-  // other kernels (ordered skipping, and block lists of unpaired heads) the
-  // plain one.
+  // paired block-list, block-mask and ordered-skipping kernels) run the
+  // software-pipelined loop below, and so does head_dim 256 (one wave per
+  // SIMD, in its solo form); the other kernels (block lists of unpaired heads,
+  // ordered skipping at head_dim 256 or unpaired) the plain one.
   constexpr bool kSolo = !OSK && C::NW == 4 && D == 256;
-  constexpr bool kPipe = (!OSK && C::NW >= 8) || kSolo;
+  constexpr bool kPipe = C::NW >= 8 || kSolo;
   // K/V tiles in LDS.  Pipelined loop: a ring of kStages slots, all K tiles
   // first (slot b at b * kTileBytes), then all V tiles (slot b at
   // kStages * kTileBytes + b * kTileBytes), so that every operand read's
@@ -282,11 +292,11 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   auto kslot = [](int b) { return b * kTileBytes; };
   auto vslot = [](int b) { return kStages * kTileBytes + b * kTileBytes; };
 
-  // Query heads per workgroup: the pipelined block-list and block-mask kernels
-  // take two query heads of one GQA group, 128 rows (one query block) each;
-  // the two share the KV head and the block set, so every K/V tile staged in
-  // LDS serves both, as a 256-row dense tile does.
-  constexpr int kHpw = (LIST && !OSK && C::NW == 8) ? 2 : 1;
+  // Query heads per workgroup: the pipelined block-list, block-mask and
+  // ordered-skipping kernels take two query heads of one GQA group, 128 rows
+  // (one query block) each; the two share the KV head and the block set, so
+  // every K/V tile staged in LDS serves both, as a 256-row dense tile does.
+  constexpr int kHpw = (LIST && C::NW == 8) ? 2 : 1;
   constexpr int kWph = C::NW / kHpw;  // waves per query head
   constexpr int kRows = kBM / kHpw;   // query rows per workgroup and head
   static_assert(!LIST || kRows == kListBlock, "one query block per workgroup and head");
@@ -368,14 +378,14 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       if (it % kSub == 0) {
         while (m_bits == 0) {
           if (++m_w >= m_words) return -1;
-          m_bits = mrow[m_w] & m_valid(m_w);
+          m_bits = ld_uniform(mrow, m_w) & m_valid(m_w);
         }
         m_blk = 32 * m_w + __builtin_ctz(m_bits);
         m_bits &= m_bits - 1u;
       }
       return m_blk * kListBlock + (it % kSub) * kBN;
     }
-    const int cb = p.col_idx[e0 + it / kSub];
+    const int cb = ld_uniform(p.col_idx, e0 + it / kSub);
     if (cb < 0 || cb >= n_kvblk) return -1;
     if (CAUSAL && cb * kListBlock > q0 + kRows - 1) return -1;
     return cb * kListBlock + (it % kSub) * kBN;
@@ -440,10 +450,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   int w_ent = -1;       // list: current entry
   int w_blk = 0;        // current block
   bool w_ok = true;     // it lies in the sequence
-  int w_raw = (kPipe && MODE == kList && n_ent > 0) ? p.col_idx[e0] : 0;  // id of entry w_ent + 1
+  int w_raw = (kPipe && (MODE == kList || OSK) && n_ent > 0) ? ld_uniform(p.col_idx, e0) : 0;  // id of entry w_ent + 1
   int mw_w = -1;        // mask: word being walked
   uint32_t mw_bits = 0u;  // its set bits not yet visited
-  uint32_t mw_pf = (kPipe && MODE == kMask && m_words > 0) ? (mrow[0] & m_valid(0)) : 0u;  // word mw_w + 1
+  uint32_t mw_pf = (kPipe && MODE == kMask && m_words > 0) ? (ld_uniform(mrow, 0) & m_valid(0)) : 0u;  // word mw_w + 1
   auto walk = [&](int &lpos, int &mpos) __attribute__((always_inline)) {
     if constexpr (MODE == kDense) {
       lpos = mpos = w_t * kBN;
@@ -451,16 +461,16 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
     } else {
       if (w_sub == kSub) {
         w_sub = 0;
-        if constexpr (MODE == kList) {
+        if constexpr (MODE == kList || OSK) {
           ++w_ent;
           w_ok = w_raw >= 0 && w_raw < n_kvblk;
           w_blk = w_ok ? w_raw : 0;
-          if (w_ent + 1 < n_ent) w_raw = p.col_idx[e0 + w_ent + 1];
+          if (w_ent + 1 < n_ent) w_raw = ld_uniform(p.col_idx, e0 + w_ent + 1);
         } else {
           while (mw_bits == 0u && mw_w + 1 < m_words) {
             ++mw_w;
             mw_bits = mw_pf;
-            mw_pf = mw_w + 1 < m_words ? (mrow[mw_w + 1] & m_valid(mw_w + 1)) : 0u;
+            mw_pf = mw_w + 1 < m_words ? (ld_uniform(mrow, mw_w + 1) & m_valid(mw_w + 1)) : 0u;
           }
           w_ok = mw_bits != 0u;  // (always, for the counted tiles)
           w_blk = w_ok ? 32 * mw_w + __builtin_ctz(mw_bits) : 0;
@@ -833,41 +843,114 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
         shift();
       }
     } else {
-      if (!lagged) softmax(s, mp_cur, pb);
+      // Ordered skipping (paired kernel): end_h[x] is the last tile whose
+      // scores head x counts (x = 0: waves 0-3; x = 1: the lagged waves 4-7),
+      // n_iter - 1 until the head stops.  A head's waves post their stop flags
+      // after the softmax of an entry's last tile (head 1 one iteration later
+      // than head 0, being lagged) and every wave reads them after the next
+      // barrier, so both heads' decisions are the same in every wave.  A
+      // stopped head still runs the PV of its last tile (in the iteration
+      // after it), then only joins the barriers and the loads; the workgroup
+      // leaves the loop at the start of an iteration (its loads all landed)
+      // once both heads are past their last PV.
+      int end_h[2] = {n_iter - 1, n_iter - 1};
+      const int hx = lagged ? 1 : 0;
+      bool quit = false;
+      // after the softmax of tile t: at an entry's end, this wave's flag (all
+      // its rows pass: the entries still to come, if each adds at most what
+      // this one added, would add at most tau of the row's mass)
+      auto osk_mark = [&](const int t) __attribute__((always_inline)) {
+        if constexpr (OSK) {
+          if (t % kSub != kSub - 1) return;
+          const float share = half_sum(d_run);
+          const float mass = half_sum(l_run);
+          const float left = (float)(n_ent - (t / kSub + 1));  // entries not yet visited
+          const bool fail = __builtin_amdgcn_ballot_w64(left * share > p.osk_tau * mass) != 0;
+          if (lane == 0) osk_flag[wave] = fail ? 0u : 1u;
+          // (the loop's barrier is a bare s_barrier: the flag must be written first)
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          d_run = 0.f;
+        }
+      };
+      // after the barrier of iteration j: the heads' decisions (head 0 on the
+      // entry that ended with tile j - 1, head 1 on the one that ended with
+      // tile j - 2)
+      auto osk_check = [&](const int j) __attribute__((always_inline)) {
+        if constexpr (OSK) {
+          if (j < n_iter) {
+            if (end_h[0] == n_iter - 1 && j % kSub == 0 && j / kSub >= p.osk_min_visit &&
+                (osk_flag[0] & osk_flag[1] & osk_flag[2] & osk_flag[3]))
+              end_h[0] = j - 1;
+            if (end_h[1] == n_iter - 1 && j % kSub == 1 && (j - 1) / kSub >= p.osk_min_visit &&
+                (osk_flag[4] & osk_flag[5] & osk_flag[6] & osk_flag[7]))
+              end_h[1] = j - 2;
+          }
+          quit = j >= max(end_h[0], end_h[1]) + 2;
+        }
+      };
+      if (!lagged) {
+        softmax(s, mp_cur, pb);
+        osk_mark(0);
+      }
       shift();
       int j = 1;
       auto body = [&](auto kb_tag) __attribute__((always_inline)) {
         constexpr int kKb = decltype(kb_tag)::value;  // = j % kStages
-        sync(j);
-        issue(j);
-        if (lagged) softmax(s, mp_prv, pb);
-        phase(kb_tag, BufTag<(kKb + kStages - 1) % kStages>{}, std::integral_constant<int, kBoth>{});
-        if (!lagged) softmax(s, mp_cur, pb);
+        constexpr int kVb = (kKb + kStages - 1) % kStages;
+        if constexpr (OSK) {
+          if (quit) return;
+          sync(j);
+          osk_check(j);
+          if (quit) return;
+          issue(j);
+          const int e = end_h[hx];
+          if (lagged && j - 1 <= e) {
+            softmax(s, mp_prv, pb);
+            osk_mark(j - 1);
+          }
+          // (with the PV of a stopped head's last tile comes the scores of
+          // the next one, which it never uses: one phase, one copy of its code)
+          if (j - 1 <= e) phase(kb_tag, BufTag<kVb>{}, std::integral_constant<int, kBoth>{});
+          if (!lagged && j <= e) {
+            softmax(s, mp_cur, pb);
+            osk_mark(j);
+          }
+        } else {
+          sync(j);
+          issue(j);
+          if (lagged) softmax(s, mp_prv, pb);
+          phase(kb_tag, BufTag<kVb>{}, std::integral_constant<int, kBoth>{});
+          if (!lagged) softmax(s, mp_cur, pb);
+        }
         shift();
         ++j;
       };
       // iterations 1 .. n_own - 1, kStages per trip (j % kStages = 1, .., 0)
-      while (j + kStages - 1 < n_own) {
+      while (j + kStages - 1 < n_own && !quit) {
         static_for<kStages>([&](auto I) { body(BufTag<(decltype(I)::value + 1) % kStages>{}); });
       }
       static_for<kStages - 1>([&](auto I) {
         if (j < n_own) body(BufTag<decltype(I)::value + 1>{});
       });
-      // iteration n_own: PV of the wave's last tile
-      sync(n_own);
-      issue(n_own);
-      if (lagged) softmax(s, mp_prv, pb);
-      auto last = [&](auto vb_tag) __attribute__((always_inline)) {
-        phase(BufTag<0>{}, vb_tag, std::integral_constant<int, kOnlyPV>{});
-      };
-      dispatch(n_own - 1, last);
-      shift();
-      // the other waves' remaining iterations: barriers and loads only
-      for (int jj = n_own + 1; jj <= n_iter; ++jj) {
-        sync(jj);
-        issue(jj);
+      if (!quit) {
+        // iteration n_own: PV of the wave's last tile
+        sync(n_own);
+        issue(n_own);
+        const int e = OSK ? end_h[hx] : n_own - 1;
+        if (lagged && n_own - 1 <= e) softmax(s, mp_prv, pb);
+        auto last = [&](auto vb_tag) __attribute__((always_inline)) {
+          phase(BufTag<0>{}, vb_tag, std::integral_constant<int, kOnlyPV>{});
+        };
+        if (n_own - 1 <= e) dispatch(n_own - 1, last);
         shift();
+        // the other waves' remaining iterations: barriers and loads only
+        for (int jj = n_own + 1; jj <= n_iter; ++jj) {
+          sync(jj);
+          issue(jj);
+          shift();
+        }
       }
+      if constexpr (OSK) n_done = end_h[hx] + 1;
     }
    }
   } else {
@@ -989,7 +1072,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       }
     }
   }
-  if (OSK && p.visited && tid == 0) p.visited[(int64_t)h * p.n_tiles + tile] = n_done / kSub;
+  if (OSK && p.visited && lane == 0 && wave % kWph == 0) p.visited[(int64_t)h * p.n_tiles + tile] = n_done / kSub;
 
   // ---- epilogue: O = acc / l (bf16, round to nearest even), LSE in natural log.
   // O goes out through LDS: each wave writes its 32 x D tile there (16 B
@@ -1111,7 +1194,7 @@ int validate(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t
 template <class C, bool CAUSAL, int MODE>
 int launch(Params p, hipStream_t stream) {
   // query heads per workgroup: two for the paired block-list / block-mask kernels
-  const int hpw = (MODE == kList || MODE == kMask) && C::NW == 8 ? 2 : 1;
+  const int hpw = (MODE == kList || MODE == kMask || MODE == kOsk) && C::NW == 8 ? 2 : 1;
   const int rows = C::kBM / hpw;
   p.n_tiles = (p.seqlen + rows - 1) / rows;
   p.n_units = p.batch * (p.hq / hpw);
@@ -1143,8 +1226,12 @@ int launch_d(const Params &p, bool causal, int mode, hipStream_t s) {
     if (paired) return causal ? launch<Paired, true, kMask>(p, s) : launch<Paired, false, kMask>(p, s);
     return causal ? launch<Listed, true, kMask>(p, s) : launch<Listed, false, kMask>(p, s);
   }
-  if (mode == kOsk)
+  if (mode == kOsk) {
+    // (head_dim 256 and odd groups: one head per workgroup, plain loop)
+    if (D != 256 && p.group % 2 == 0)
+      return causal ? launch<Paired, true, kOsk>(p, s) : launch<Paired, false, kOsk>(p, s);
     return causal ? launch<Listed, true, kOsk>(p, s) : launch<Listed, false, kOsk>(p, s);
+  }
   return causal ? launch<Dense, true, kDense>(p, s) : launch<Dense, false, kDense>(p, s);
 }
 

@@ -18,8 +18,15 @@ from tests import _parity as P
 pytestmark = pytest.mark.gpu
 
 
-def small(seed=31, s=6144, mu=6.0, budget=0.5):
-    return W.make_osk("osk_small", seed, s, 4, 2, 128, budget=budget, mu=mu)
+def small(seed=31, s=6144, mu=6.0, budget=0.5, hq=4, hkv=2, d=128):
+    return W.make_osk("osk_small", seed, s, hq, hkv, d, budget=budget, mu=mu)
+
+
+# head configurations: pairs of query heads of one GQA group per workgroup
+# (the pipelined loop, head_dim 64 and 128), an odd group and head_dim 256
+# (one query head per workgroup, the plain loop)
+SHAPES = [("pair_d128", 4, 2, 128, 6144), ("pair_d64", 4, 2, 64, 6144),
+          ("single_g3_d128", 3, 1, 128, 4096), ("single_d256", 2, 1, 256, 3072)]
 
 
 def static_list(w, row_ptr=None, col_idx=None):
@@ -34,10 +41,7 @@ def static_list(w, row_ptr=None, col_idx=None):
     return out.float().cpu().numpy().reshape(w.seqlen, w.hq, w.d), lse.cpu().numpy()[0].T
 
 
-@pytest.mark.parametrize("tau,min_visit", [(1e-3, 2), (1e-2, 2), (5e-2, 3), (3e-1, 2)])
-def test_osk_valid_stops_and_prefix_parity(tau, min_visit):
-    w = small()
-    print(f"osk small tau={tau} min_visit={min_visit}", flush=True)
+def _stops_and_prefix(w, tau, min_visit):
     o, l, vis = P.run_gpu_osk(w, tau, min_visit)
     n_qblk = len(w.row_ptr) - 1
     qbs = np.arange(n_qblk)
@@ -51,16 +55,35 @@ def test_osk_valid_stops_and_prefix_parity(tau, min_visit):
     print(f"  skipped {skip:.3f} of the listed entries; {stats}", flush=True)
 
 
-def test_osk_tau_zero_is_the_static_list():
-    w = small(seed=32)
+@pytest.mark.parametrize("tau,min_visit", [(1e-3, 2), (1e-2, 2), (5e-2, 3), (3e-1, 2)])
+def test_osk_valid_stops_and_prefix_parity(tau, min_visit):
+    print(f"osk small tau={tau} min_visit={min_visit}", flush=True)
+    _stops_and_prefix(small(), tau, min_visit)
+
+
+@pytest.mark.parametrize("shape", SHAPES[1:], ids=[c[0] for c in SHAPES[1:]])
+def test_osk_shapes_valid_stops_and_prefix_parity(shape):
+    name, hq, hkv, d, s = shape
+    print(f"osk {name} tau=1e-2", flush=True)
+    _stops_and_prefix(small(seed=35, s=s, hq=hq, hkv=hkv, d=d), 1e-2, 2)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[c[0] for c in SHAPES])
+def test_osk_tau_zero_is_the_static_list(shape):
+    name, hq, hkv, d, s = shape
+    print(f"osk {name} tau=0", flush=True)
+    w = small(seed=32, s=s, hq=hq, hkv=hkv, d=d)
     o, l, vis = P.run_gpu_osk(w, 0.0, 1)
     assert np.array_equal(vis, np.broadcast_to(np.diff(w.row_ptr), vis.shape))
     o_s, l_s = static_list(w)
     assert np.array_equal(o, o_s) and np.array_equal(l, l_s)
 
 
-def test_osk_huge_tau_is_the_cut_list():
-    w = small(seed=33)
+@pytest.mark.parametrize("shape", SHAPES, ids=[c[0] for c in SHAPES])
+def test_osk_huge_tau_is_the_cut_list(shape):
+    name, hq, hkv, d, s = shape
+    print(f"osk {name} huge tau", flush=True)
+    w = small(seed=33, s=s, hq=hq, hkv=hkv, d=d)
     mv = 3
     o, l, vis = P.run_gpu_osk(w, 1e30, mv)
     want = np.minimum(np.diff(w.row_ptr), mv)
