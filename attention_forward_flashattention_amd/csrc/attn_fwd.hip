@@ -1209,6 +1209,8 @@ int launch(Params p, hipStream_t stream) {
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+constexpr float kOskPairedMaxTau = 1e-2f;  // ordered skipping: the paired kernel up to this tau
+
 template <int D>
 int launch_d(const Params &p, bool causal, int mode, hipStream_t s) {
   using Dense = Config<D, D == 64 ? 12 : (D == 128 ? 8 : 4)>;
@@ -1227,8 +1229,13 @@ int launch_d(const Params &p, bool causal, int mode, hipStream_t s) {
     return causal ? launch<Listed, true, kMask>(p, s) : launch<Listed, false, kMask>(p, s);
   }
   if (mode == kOsk) {
-    // (head_dim 256 and odd groups: one head per workgroup, plain loop)
-    if (D != 256 && p.group % 2 == 0)
+    // Two heads per workgroup when most of each list is walked.  With a larger
+    // tau the walks are short, a pair's per-workgroup cost weighs more and the
+    // pair waits for its slower head (128K planted-relevance workload: the
+    // paired kernel 5-7% faster at tau <= 1e-3, even at 3e-3 and 1e-2, 2-3%
+    // slower at 3e-2 and 1e-1).  Head_dim 256 and odd groups: one head per
+    // workgroup, plain loop.
+    if (D != 256 && p.group % 2 == 0 && p.osk_tau <= kOskPairedMaxTau)
       return causal ? launch<Paired, true, kOsk>(p, s) : launch<Paired, false, kOsk>(p, s);
     return causal ? launch<Listed, true, kOsk>(p, s) : launch<Listed, false, kOsk>(p, s);
   }
