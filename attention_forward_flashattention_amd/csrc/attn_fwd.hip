@@ -2,11 +2,13 @@
 //
 // One workgroup computes a tile of query rows of one (sequence, query head):
 // for dense and packed problems 256 rows in eight wave64s (head_dim 128), 384
-// rows in twelve (head_dim 64) or 128 rows in four (head_dim 256); 128 rows in
-// four wave64s for the block-list kernel (one query block of the list).  Each
-// wave owns 32 rows and keeps them in registers for the whole kernel.  KV tiles of
-// BN keys (64; 32 at head_dim 256) are streamed into double-buffered LDS with
-// direct global-to-LDS loads; for each tile a wave computes the transposed
+// rows in twelve (head_dim 64) or 128 rows in four (head_dim 256).  The
+// block-list, block-mask and ordered-skipping kernels take one 128-row query
+// block of the list or mask, for two query heads of a GQA group in eight
+// wave64s (or for one head in four).  Each wave owns 32 rows and keeps them in
+// registers for the whole kernel.  KV tiles of BN keys (64; 32 at head_dim
+// 256) are streamed into a ring of LDS slots with direct global-to-LDS loads;
+// for each tile a wave computes the transposed
 // score tile S^T = K Q^T with 32x32x16 bf16 MFMAs, so that every lane holds
 // the scores of ONE query row (the softmax row statistics then need one
 // exchange between the two lane halves instead of a 32-lane reduction), runs
@@ -70,9 +72,9 @@ struct Params {
 // head_dim 128 (two per SIMD, 256-row tiles: every K/V tile staged in LDS
 // serves 256 query rows) and 12 at head_dim 64 (three per SIMD: the
 // pipelined loop needs under 168 VGPRs there, so a third wave fits and hides
-// more of each wave's serial barrier and load-issue time); the block-list
-// kernel uses 4 waves so a workgroup covers exactly one 128-row query block
-// of the list.
+// more of each wave's serial barrier and load-issue time); the block-list,
+// block-mask and ordered-skipping kernels use 8 waves for one 128-row query
+// block of two query heads of a GQA group, or 4 for one head.
 template <int D_, int NW_>
 struct Config {
   static constexpr int D = D_;
@@ -110,16 +112,15 @@ __device__ __forceinline__ float exp_tile(const floatx16_t (&s)[kKt], float c, f
 // one (or, for the paired block-sparse kernels, two) query heads.  Workgroups
 // are dealt round-robin over the 8 XCDs (each with its own L2).  When the
 // units split evenly, the `unit_group` units that share one KV head stay
-// together and those groups are dealt round-robin over the XCDs.  Within an
-// XCD, when every CU gets many workgroups, the groups follow one another
-// (all tiles of a group before the next), so the workgroups in flight on an
-// XCD read the same K/V prefix and it stays in the XCD's L2 (packed D=256:
-// +9%); with few workgroups per CU the tiles go tile by tile over all of the
-// XCD's units, heaviest first everywhere, which balances the CUs (dense MHA
-// S=2048: the group order there is 28% slower),
-// so every XCD gets the same mix of sequences (packed batches stay balanced)
-// and the heads that read the same K/V share one L2.  Within an XCD, causal
-// and block-list tiles are issued heaviest first.
+// together and those groups are dealt round-robin over the XCDs, so every XCD
+// gets the same mix of sequences (packed batches stay balanced) and the heads
+// that read the same K/V share one L2.  Within an XCD, when every CU gets many
+// workgroups, the groups follow one another (all tiles of a group before the
+// next), so the workgroups in flight on an XCD read the same K/V prefix and it
+// stays in the XCD's L2 (packed D=256: +9%); with few workgroups per CU the
+// tiles go tile by tile over all of the XCD's units, which balances the CUs
+// (dense MHA S=2048: the group order there is 28% slower).  Causal and
+// block-list tiles are issued heaviest first.
 __device__ __forceinline__ void decode_tile(const Params &p, bool heavy_first, int &tile,
                                             int &unit) {
   const int w = blockIdx.x;
