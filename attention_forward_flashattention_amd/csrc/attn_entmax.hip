@@ -9,14 +9,15 @@
 // LDS with direct global-to-LDS loads and forming the transposed score tile
 // S^T = K Q^T with 32x32x16 bf16 MFMAs (lane = query row, as in the softmax
 // kernel):
-//   1. the row maximum m;
-//   2. a histogram of the scores in the window [m - W, m], W = 1/(alpha-1)
-//      (only those can carry weight), kBins bins per row in LDS; each score
+//   1. the row maximum m and, in the same pass, a histogram of the scores
+//      in the window [m - W, m], W = 1/(alpha-1) (only those can carry
+//      weight): kBins bins per row in LDS of width W/(kBins-1) on a fixed
+//      grid, kept as a ring that follows the running maximum; each score
 //      counts at its bin's lower edge, so the root tau_h of the histogram's
 //      mass equation is a lower bound of the true tau; each lane solves it
 //      by bisection over the bins;
-//   3. up to n_iter refinement passes (fewer once every row of the workgroup
-//      has |sum p - 1| <= 4e-6), each forming the power sums the update needs
+//   2. up to n_iter refinement passes (fewer once every row of the workgroup
+//      has converged or taken its last step), each forming the power sums the update needs
 //      at the current tau and taking one step of the hybrid solver (Halley
 //      for alpha <= 1.5, Newton for alpha <= 2, a secant through the bracket
 //      ends (regula falsi, Illinois rule) above), with a
@@ -25,7 +26,7 @@
 //      bit-packed block mask, each 128-key block whose scores can clear the
 //      bracket's lower end at the start of the pass (so every block with a
 //      non-zero weight at the final tau is marked);
-//   4. the output pass, which visits only the marked blocks (walking the
+//   3. the output pass, which visits only the marked blocks (walking the
 //      mask's set bits), forms p in registers and accumulates O^T += V^T P^T
 //      with V^T from LDS transpose reads; O is divided by sum p.
 // tau (fp32) and the bit-packed block mask can be written out.
@@ -78,6 +79,22 @@ __device__ __forceinline__ float powpos(float u, float e) {
     if (!(u > 0.f)) return 0.f;
     return __builtin_amdgcn_exp2f(e * __builtin_amdgcn_logf(u));
   }
+}
+
+// LDS read-modify-writes and stores of the histogram and the block mask,
+// written as inline assembly: the compiler would order each of its own LDS
+// accesses after every direct-to-LDS load in flight (vmcnt(0): it cannot tell
+// their addresses apart), which made every tile wait for the next tile's K
+// before its first histogram count.  No K/V load writes the histogram or the
+// mask; each pass waits for these (lgkmcnt(0)) before its closing barrier.
+__device__ __forceinline__ void lds_add_u32(uint32_t addr, uint32_t v) {
+  asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_or_b32(uint32_t addr, uint32_t v) {
+  asm volatile("ds_or_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_write_b32(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
 template <int kLoads>
@@ -238,73 +255,107 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
       f(it * kBN, s);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the pass's histogram / mask updates
     __syncthreads();
   };
 
-  // ---- pass 1: row maximum
-  float m = -INFINITY;
-  dense_pass([&](int, floatx16_t(&s)[kKt]) {
-#pragma unroll
-    for (int kt = 0; kt < kKt; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, s[kt][i]);
-  });
-  m = half_max(m) * p.scale;  // (scale > 0)
-  const int n_allowed = p.causal ? qrow + 1 : len;
-
-  // ---- pass 2: histogram of the window [m - W, m]
+  // ---- pass 1: the row maximum and the histogram of the window below it,
+  // in one pass.  Bins have width bw = W / (kBins - 1) on a grid of integer
+  // multiples of bw (bin b holds b bw <= z < (b + 1) bw, b counted from a
+  // per-row integer anchor taken at the first tile, so the bin arithmetic
+  // stays small); the kBins bins top - kBins + 1 .. top, top the bin of the
+  // running maximum, cover the window [m - W, m] whatever m turns out to be.
+  // They live in a ring of kBins slots per row (bin b in slot b mod kBins):
+  // when a tile raises top, the slots of the bins that leave the window are
+  // cleared for the bins that enter it.  Scores below the window (at the
+  // time they are seen, so also at the end) cannot carry weight and are not
+  // counted.  A row's ring is rotated by row % 32 (bin b at word
+  // (b + row) mod kBins of the row's kBins words), so the lanes of a wave that
+  // hit the same bin hit different banks; the rotation is folded into the
+  // score's FMA, which then yields the word index directly.
+  static_assert(kBins == 32, "one ring slot per LDS bank");
   for (int i = tid; i < kBM * kBins; i += 256) hist[i] = 0u;
   for (int i = tid; i < (n_kblk + 31) / 32; i += 256) mbits[i] = 0u;
   __syncthreads();
-  const float base = m - W;
-  const float inv_bw = kBins / W;
-  // bin of score z: (z - base) / bin width = fma(qk, scale / width, -base / width);
-  // bin b of a row sits at word b ^ (row % 32) of the row's kBins words, so
-  // the lanes of a wave that hit the same bin hit different LDS banks
-  const float h_mul = p.scale * inv_bw, h_add = -base * inv_bw;
+  const float c_h = p.scale * (float)(kBins - 1) * a1;  // z / bw per unit of q.k
   const int swz = row & (kBins - 1);
-  dense_pass([&](int, floatx16_t(&s)[kKt]) {
+  uint32_t *hrow = hist + row * kBins;
+  const uint32_t hrow_lds = (uint32_t)(uintptr_t)(lds_char_t *)hrow;
+  // The anchor sits kAnchorBelow bins below the first maximum, so every bin
+  // in the window has a positive index (truncation is the floor there).
+  constexpr float kAnchorBelow = 2.f * kBins;
+  float m_raw = -INFINITY;  // running row maximum of q.k (both lane halves)
+  float anchor = 0.f;       // bin index of the grid origin (an integer)
+  float topf = -1e30f;      // bin of the running maximum, from the anchor
+  dense_pass([&](int kv0, floatx16_t(&s)[kKt]) {
+    float tm = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < kKt; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tm = fmaxf(tm, s[kt][i]);
+    tm = half_max(tm);
+    // every live row sees key 0, so its first tile has a finite maximum
+    if (kv0 == 0 && tm > -INFINITY) anchor = floorf(tm * c_h) - kAnchorBelow;
+    m_raw = fmaxf(m_raw, tm);
+    const float ntop = tm > -INFINITY ? floorf(__builtin_fmaf(tm, c_h, -anchor)) : topf;
+    const float rise = fminf(ntop - topf, (float)kBins);  // kBins on the first tile
+    if (__builtin_amdgcn_ballot_w64(rise > 0.f) != 0) {
+      const int n_clr = rise > 0.f ? (int)rise : 0;
+      const int itop = rise > 0.f ? (int)ntop : 0;
+      // (as many steps as the wave's largest rise: one or two bins once the
+      // maximum has settled, kBins on the first tile)
+      for (int c = 0; __builtin_amdgcn_ballot_w64(c < n_clr) != 0; ++c)
+        if (c < n_clr) lds_write_b32(hrow_lds + (((itop - c + swz) & (kBins - 1)) << 2), 0u);
+      topf = fmaxf(topf, ntop);
+    }
+    // t = bin + rotation; counted when bin >= topf - (kBins - 1)
+    const float lo_t = topf - (float)(kBins - 1) + (float)swz;
+    const float anchor_r = anchor - (float)swz;
 #pragma unroll
     for (int kt = 0; kt < kKt; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float t = __builtin_fmaf(s[kt][i], h_mul, h_add);  // -inf for masked scores
-        if (t >= 0.f) {
-          const int bin = min((int)t, kBins - 1);
-          atomicAdd(&hist[row * kBins + (bin ^ swz)], 1u);
-        }
+        const float t = __builtin_fmaf(s[kt][i], c_h, -anchor_r);  // -inf for masked scores
+        if (t >= lo_t) lds_add_u32(hrow_lds + ((((int)t) & (kBins - 1)) << 2), 1u);
       }
   });
+  const float m = m_raw * p.scale;  // (scale > 0)
+  const int n_allowed = p.causal ? qrow + 1 : len;
   // the histogram's root by bisection (both lane halves hold the same row and
-  // the same counts, so both compute the same tau_h)
+  // the same counts, so both compute the same tau_h): bin top - kBins + 1 + bb
+  // counts at u = (alpha-1) z of its lower edge, ebase + bb * ebw
+  const bool counted = topf > -1e29f;  // (rows past the end count nothing)
+  const int ilo = counted ? (int)topf - (kBins - 1) : 0;
   float cnt[kBins];
 #pragma unroll
-  for (int bb = 0; bb < kBins; ++bb) cnt[bb] = (float)hist[row * kBins + (bb ^ swz)];
-  float lo = a1 * base - 1.f, hi_t = a1 * m;
+  for (int bb = 0; bb < kBins; ++bb) cnt[bb] = (float)hrow[(ilo + bb + swz) & (kBins - 1)];
+  const float ebw = 1.f / (float)(kBins - 1);  // (alpha-1) bw
+  const float ebase = (anchor + (float)ilo) * ebw;
+  float lo = a1 * m - 2.f, hi_t = a1 * m;
   for (int it = 0; it < 30; ++it) {
     const float mid = 0.5f * (lo + hi_t);
     float sum = 0.f;
 #pragma unroll
-    for (int bb = 0; bb < kBins; ++bb) sum += cnt[bb] * powpos<PK>(a1 * (base + bb * (W / kBins)) - mid, e);
+    for (int bb = 0; bb < kBins; ++bb) sum += cnt[bb] * powpos<PK>(__builtin_fmaf((float)bb, ebw, ebase) - mid, e);
     if (sum >= 1.f)
       lo = mid;
     else
       hi_t = mid;
   }
   const float tau_h = lo;  // lo keeps sum >= 1: a lower bound of the histogram's root
-  // ---- pass 3: refinement.  Bracket [blo, bhi] of the true tau: tau_h is
+  // ---- pass 2: refinement.  Bracket [blo, bhi] of the true tau: tau_h is
   // below it; counting every score at its bin's upper edge instead would
-  // raise every score by at most W/B and the root by at most (alpha-1) W/B =
-  // 1/B, so tau_h + 1/B is above it (with a little room for fp32 rounding);
+  // raise every score by at most bw and the root by at most (alpha-1) bw =
+  // ebw, so tau_h + ebw is above it (with a little room for fp32 rounding);
   // and at (alpha-1) m - n^(1-alpha) every weight is at most 1/n.
   float blo = tau_h;
   float bhi = fminf(a1 * m - __builtin_amdgcn_exp2f((1.f - p.alpha) *
                                                      __builtin_amdgcn_logf((float)max(n_allowed, 1))),
-                    tau_h + (1.f / kBins) * (1.f + 1e-4f) + 1e-6f * fabsf(tau_h));
+                    tau_h + ebw * (1.f + 1e-4f) + 1e-6f * fabsf(tau_h));
   if (!(bhi > blo)) bhi = blo + 1e-6f * fmaxf(1.f, fabsf(blo));
   // Starting point: the histogram's root with every score counted at its
   // bin's midpoint (between the lower- and upper-edge placements, so within
-  // [tau_h, tau_h + 1/B]), found by bisection in that bracket: an estimate
+  // [tau_h, tau_h + ebw]), found by bisection in that bracket: an estimate
   // close enough that one Halley or Newton step usually finishes the row.
   float t;
   {
@@ -314,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
       float sum = 0.f;
 #pragma unroll
       for (int bb = 0; bb < kBins; ++bb)
-        sum += cnt[bb] * powpos<PK>(a1 * (base + (bb + 0.5f) * (W / kBins)) - mid, e);
+        sum += cnt[bb] * powpos<PK>(__builtin_fmaf((float)bb + 0.5f, ebw, ebase) - mid, e);
       if (sum >= 1.f)
         mlo = mid;
       else
@@ -328,9 +379,12 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   const float kTol = 4e-6f;  // |sum p - 1| at which a row counts as converged (fp32 sums)
   // Newton (alpha <= 2) and Halley (alpha <= 1.5) converge quadratically and
   // cubically: once |sum p - 1| is below this at the current tau, the step
-  // taken from it lands within fp32 rounding of the root, so the row takes it
-  // and stops without another pass to confirm it.
-  const float kStepTol = p.alpha <= 1.5f ? 1e-2f : 2e-3f;
+  // taken from it lands close enough to the root that the row takes it and
+  // stops without another pass to confirm it.  Newton from 2e-3 lands within
+  // fp32 rounding; Halley from 0.1 within |sum p - 1| ~ 2e-4 at worst (a key
+  // entering the support next to the root), which moves O by at most that
+  // times max |v - O| (O is divided by sum p), a tenth of O's tolerance.
+  const float kStepTol = p.alpha <= 1.5f ? 1e-1f : 2e-3f;
   const float zs = a1 * p.scale;  // (alpha - 1) z = zs * q.k
   bool final_step = false;  // the row took its last step
   const int m_words = (n_kblk + 31) / 32;
@@ -342,6 +396,8 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
     for (int w = tid; w < m_words; w += 256) mbits[w] = 0u;
     __syncthreads();
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, shi = 0.f;
+    // alpha = 2: the u of the nearest key above t and at or below it
+    float gap_up = INFINITY, gap_dn = -INFINITY;
     dense_pass([&](int kv0, floatx16_t(&s)[kKt]) {
       float tmax = -INFINITY;
 #pragma unroll
@@ -361,6 +417,8 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
           } else if constexpr (PK == kPowLinear) {
             s0 += up;
             s1 += pos;
+            gap_up = fminf(gap_up, u > 0.f ? u : INFINITY);
+            gap_dn = fmaxf(gap_dn, u > 0.f ? -INFINITY : u);
           } else if (u > 0.f) {
             const float pu = powpos<PK>(u, e);
             s0 += pu;
@@ -375,11 +433,16 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
         }
       // mark the 128-key block if some live row's scores clear t_mask
       const bool any = __builtin_amdgcn_ballot_w64(live && zs * tmax > t_mask) != 0;
-      if (any && lane == 0) atomicOr(&mbits[kv0 / kListBlock / 32], 1u << ((kv0 / kListBlock) % 32));
+      if (any && lane == 0)
+        lds_or_b32((uint32_t)(uintptr_t)(lds_char_t *)(mbits + kv0 / kListBlock / 32), 1u << ((kv0 / kListBlock) % 32));
     });
     s0 = half_sum(s0);
     s1 = half_sum(s1);
     s2 = half_sum(s2);
+    if constexpr (PK == kPowLinear) {
+      gap_up = -half_max(-gap_up);
+      gap_dn = half_max(gap_dn);
+    }
     const float g = s0 - 1.f;
     if (p.alpha > 2.f && first) ghi = half_sum(shi) - 1.f;
     // converged: keep t (the bracket may have closed on it); a row that took
@@ -410,8 +473,13 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
         t_new = ghi < glo ? blo - glo * (bhi - blo) / (ghi - glo) : 0.5f * (blo + bhi);
       }
       const bool inside = t_new >= blo && t_new <= bhi;
+      // alpha = 2: the mass is linear in tau while no key enters or leaves the
+      // support, so a Newton step that stays between the nearest keys on
+      // either side of t lands on the root (to rounding) whatever g was
+      bool exact = false;
+      if constexpr (PK == kPowLinear) exact = t_new - t < gap_up && t_new - t > gap_dn;
       t = inside ? t_new : 0.5f * (blo + bhi);  // bisection fallback (then not a last step)
-      final_step = last && inside;
+      final_step = (last || exact) && inside;
     }
     // the workgroup stops once every live row has converged or taken its last step
     const bool wave_done = __builtin_amdgcn_ballot_w64(live && !conv && !final_step) == 0;
@@ -423,7 +491,7 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   }
   __syncthreads();  // the mask is complete
 
-  // ---- pass 4: output over the marked blocks
+  // ---- pass 3: output over the marked blocks
   floatx16_t oacc[kDt];
 #pragma unroll
   for (int dt = 0; dt < kDt; ++dt)

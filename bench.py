@@ -300,7 +300,7 @@ def time_entmax(attn, torch, w, q, k, v, softmax_ms, n, settle_ms, alpha=1.5):
     return {"workload": DESCRIPTIONS.get(w.name, w.name), "alpha": alpha, "ms_per_call": round(ms_e, 5),
             "calls": n, "time_vs_softmax_forward": round(ms_e / softmax_ms, 3),
             "output_pass_block_fraction": round(visited / blocks, 4),
-            "kernel": "attn_entmax_kernel (max, histogram, refinement passes to convergence, sparse output pass)"}
+            "kernel": "attn_entmax_kernel (max and histogram pass, refinement passes to convergence, sparse output pass)"}
 
 
 def time_backward(attn, torch, w, q, k, v, cu, sp, out, lse, flops, n, settle_ms):

@@ -221,14 +221,18 @@ int attn_fwd_osk_validate(const attn_tensor_t *q, const attn_tensor_t *k, const 
  * masking),
  *     p_j = [(alpha - 1) z_j - tau]_+ ^ (1 / (alpha - 1)),   sum_j p_j = 1,
  *     O = sum_j p_j v_j,
- * so most weights are exactly zero.  tau has no closed form: the kernel bins
- * the scores of the window [m - 1/(alpha-1), m] (m the row max) into a
- * histogram whose root is a lower bound of tau, then takes steps of a hybrid
- * root finder (Halley for alpha <= 1.5, Newton for alpha <= 2, a secant
- * through the bracket ends above) with a bisection fallback -- until every
- * row of a 128-row tile has |sum p - 1| <= 4e-6 or n_iter steps are done --
- * and finally visits only the 128 x 128 blocks that can hold a non-zero
- * weight.  O is divided by sum p at the final tau (1 when tau has converged).
+ * so most weights are exactly zero.  tau has no closed form: in one pass
+ * that also finds the row max m, the kernel bins the scores of the window
+ * [m - 1/(alpha-1), m] into a histogram (32 bins of width 1/(31 (alpha-1))
+ * on a fixed grid) whose root is a lower bound of tau within 1/31 of it, then
+ * takes steps of a hybrid root finder (Halley for alpha <= 1.5, Newton for
+ * alpha <= 2, a secant through the bracket ends above) with a bisection
+ * fallback -- until every row of a 128-row tile has |sum p - 1| <= 4e-6, has
+ * taken a last Halley step from |sum p - 1| <= 0.1 or Newton step from
+ * 2e-3, has taken a sparsemax (alpha = 2) Newton step that no key crosses
+ * (exact), or n_iter steps are done -- and finally visits only the 128 x 128
+ * blocks that can hold a non-zero weight.  O is divided by sum p at the
+ * final tau.
  *
  *   q [B, S, Hq, D], k, v [B, S, Hkv, D] bf16 (fixed-length batches)
  *   alpha        in [1.05, 3] (above 3 the weights rise too steeply from the

@@ -26,12 +26,17 @@
  *
  * Histogram lower bound (the same explainer, section 2: solving for tau on a
  * histogram of the scores gives tau_h <= tau*): only scores above
- * m - 1/(alpha-1) can carry weight once tau >= (alpha-1) m - 1, so the
- * window [m - W, m], W = 1/(alpha-1), is cut into B equal bins and each score
- * in it is counted at its bin's lower edge (scores below the window are
- * dropped).  Every score is then replaced by something no larger, so the
- * histogram's g_h <= g everywhere and its root tau_h <= tau*.  The bin of a
- * score z is floor((z - (m - W)) * B / W), clamped to B - 1.
+ * m - 1/(alpha-1) can carry weight once tau >= (alpha-1) m - 1, so only the
+ * window [m - W, m], W = 1/(alpha-1), is binned.  The bins have width
+ * bw = W / (B - 1) on the grid of integer multiples of bw (bin k holds
+ * k bw <= z < (k + 1) bw); with top = floor(m / bw), the B bins top - B + 1
+ * .. top cover the window, and each score in them is counted at its bin's
+ * lower edge k bw (lower scores are dropped).  Every score is then replaced
+ * by something no larger, so the histogram's g_h <= g everywhere and its
+ * root tau_h <= tau*; placing them at upper edges instead would raise each
+ * by at most bw, so tau* <= tau_h + (alpha-1) bw = tau_h + 1/(B-1).  (A grid
+ * fixed in z, rather than one anchored at m - W, lets a single pass over the
+ * scores bin them while it is still finding m.)
  *
  * Block mask: bit kb % 32 of word kb / 32 of query block qb's row (for each
  * sequence and query head) is set when some row of the query block gives
@@ -93,26 +98,26 @@ static double solve_tau(const double *z, int64_t n, double alpha, double m) {
 static double solve_tau_hist(const double *z, int64_t n, double alpha, double m, int bins,
                              double *cnt) {
   const double W = 1.0 / (alpha - 1.0);
-  const double base = m - W;
+  const double bw = W / (bins - 1);
+  const double top = floor(m / bw);
+  const double k0 = top - (bins - 1); /* grid index of the lowest bin */
   for (int b = 0; b < bins; ++b) cnt[b] = 0.0;
   for (int64_t j = 0; j < n; ++j) {
-    if (z[j] < base) continue;
-    int b = (int)floor((z[j] - base) * bins / W);
-    if (b >= bins) b = bins - 1;
-    if (b < 0) continue;
-    cnt[b] += 1.0;
+    const double k = floor(z[j] / bw);
+    if (k < k0) continue;
+    cnt[(int)(k - k0)] += 1.0;
   }
   const double e = 1.0 / (alpha - 1.0);
-  /* bracket: at (alpha-1) base the lowest bin alone would need... use the
-     exact bracket of the scores, which also brackets the histogram's root */
-  double lo = (alpha - 1.0) * base - 1.0;
+  /* the histogram's root lies between (alpha-1) m - 2 (where the top bin
+     alone, at most bw below m, already has mass >= 1) and (alpha-1) m */
+  double lo = (alpha - 1.0) * m - 2.0;
   double hi = (alpha - 1.0) * m;
   for (int it = 0; it < 400; ++it) {
     const double mid = 0.5 * (lo + hi);
     if (!(mid > lo && mid < hi)) break;
     double s = 0.0;
     for (int b = 0; b < bins; ++b) {
-      const double u = (alpha - 1.0) * (base + b * W / bins) - mid;
+      const double u = (alpha - 1.0) * ((k0 + b) * bw) - mid;
       if (u > 0.0 && cnt[b] > 0.0) s += cnt[b] * pow(u, e);
     }
     if (s >= 1.0)
@@ -196,7 +201,7 @@ static void *eworker(void *arg) {
 /*
  * oracle_entmax_fwd — exact alpha-entmax attention forward.
  *   q [T][hq][d], k, v [T][hkv][d] float64; cu [n_seqs+1] int32 (host)
- *   alpha > 1; bins >= 1 (histogram of tau_hist)
+ *   alpha > 1; bins >= 2 (histogram of tau_hist)
  *   out [T][hq][d], tau [T][hq] (exact normaliser), tau_hist [T][hq] or NULL
  *   mask NULL or uint32 [n_seqs][hq][n_qblk][words] (zeroed here), blocks of blk
  */
@@ -205,7 +210,7 @@ int oracle_entmax_fwd(const double *q, const double *k, const double *v, const i
                       int bins, double *out, double *tau, double *tau_hist, uint32_t *mask,
                       int blk, int n_qblk, int words, int nthreads) {
   if (!q || !k || !v || !cu || !out || !tau || n_seqs < 1 || hq < 1 || hkv < 1 || d < 1 ||
-      hq % hkv != 0 || !(alpha > 1.0) || bins < 1)
+      hq % hkv != 0 || !(alpha > 1.0) || bins < 2)
     return ENT_EINVAL;
   if (mask && (blk < 1 || n_qblk < 1 || words < 1)) return ENT_EINVAL;
   if (mask) memset(mask, 0, sizeof(uint32_t) * (size_t)n_seqs * hq * n_qblk * words);

@@ -5,7 +5,8 @@ bisection to rounding) at the forward's tolerances.  The GPU's tau must
 solve the normalisation: sum_j [(alpha-1) z_j - tau]_+^(1/(alpha-1)),
 recomputed in fp64 at the GPU's tau, within MASS_TOL of 1; for alpha <= 2 it
 must also lie within TAU_ABS of the exact root.  The histogram start must
-keep its bound tau* - 1/32 <= tau_h <= tau* (plus fp32 rounding), and the
+keep its bound tau* - 1/31 <= tau_h <= tau* (32 bins of width W/31, W =
+1/(alpha-1); plus fp32 rounding), and the
 GPU's block mask must contain every block the exact weights touch.
 """
 import numpy as np
@@ -76,7 +77,7 @@ def check(w, alpha, n_iter, layout="bshd"):
     assert merr <= MASS_TOL, (w.name, alpha, merr)
     if alpha <= 2:
         assert terr <= TAU_ABS, (w.name, alpha, terr)
-    assert np.all(tau0 <= tau_ref + TAU_H_SLACK) and np.all(tau0 >= tau_ref - 1.0 / 32 - TAU_H_SLACK)
+    assert np.all(tau0 <= tau_ref + TAU_H_SLACK) and np.all(tau0 >= tau_ref - 1.0 / 31 - TAU_H_SLACK)
     assert np.array_equal(mask & mask_ref, mask_ref), "a block with non-zero weight was not visited"
     n_vis, n_need = int(np.unpackbits(mask.view(np.uint8)).sum()), int(np.unpackbits(mask_ref.view(np.uint8)).sum())
     stats.update(tau_max_abs=terr, mass_err=merr, blocks_visited=n_vis, blocks_needed=n_need)

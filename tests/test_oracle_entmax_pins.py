@@ -14,7 +14,8 @@ what mathematics fixes:
   adding one vector to every key shifts every score of a row equally, leaving
   O unchanged and moving tau by (alpha-1) times the shift; GQA equals MHA with
   repeated K/V; packed equals per-sequence.
-* the histogram bound: tau* - 1/B <= tau_h <= tau* for B bins.
+* the histogram bound: tau* - 1/(B-1) <= tau_h <= tau* for B bins of width
+  W/(B-1), W = 1/(alpha-1).
 * the block mask: bit set exactly where some row of the query block gives
   some key of the key block a positive weight (from the brentq taus).
 Planted mistakes in a numpy copy (exponent 1/alpha, (alpha-1) factor
@@ -151,7 +152,7 @@ def test_histogram_bound(alpha, bins):
     q, k, v, cu, causal = case(*CASES[1])
     _, tau, tau_h = oracle.entmax_fwd(q, k, v, cu, causal, 1.3, alpha, bins=bins)
     assert np.all(tau_h <= tau + 1e-12)
-    assert np.all(tau_h >= tau - 1.0 / bins - 1e-12)
+    assert np.all(tau_h >= tau - 1.0 / (bins - 1) - 1e-12)
 
 
 def test_block_mask_marks_positive_weights():
