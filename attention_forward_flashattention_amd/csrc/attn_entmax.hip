@@ -25,7 +25,9 @@
 //      from the signs seen so far; every pass also marks, in an LDS
 //      bit-packed block mask, each 128-key block whose scores can clear the
 //      bracket's lower end at the start of the pass (so every block with a
-//      non-zero weight at the final tau is marked);
+//      non-zero weight at the final tau is marked); above alpha = 2 the
+//      first of them also gathers each row's few keys above the bracket's
+//      lower end and solves the mass equation on them exactly;
 //   3. the output pass, which visits only the marked blocks (walking the
 //      mask's set bits), forms p in registers and accumulates O^T += V^T P^T
 //      with V^T from LDS transpose reads; O is divided by sum p.
@@ -95,6 +97,14 @@ __device__ __forceinline__ void lds_or_b32(uint32_t addr, uint32_t v) {
 }
 __device__ __forceinline__ void lds_write_b32(uint32_t addr, uint32_t v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+// LDS counter increment that returns the old value (waited for in the same
+// assembly block)
+__device__ __forceinline__ uint32_t lds_inc_rtn(uint32_t addr) {
+  uint32_t old;
+  const uint32_t one = 1u;
+  asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(old) : "v"(addr), "v"(one) : "memory");
+  return old;
 }
 
 template <int kLoads>
@@ -388,8 +398,23 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   const float zs = a1 * p.scale;  // (alpha - 1) z = zs * q.k
   bool final_step = false;  // the row took its last step
   const int m_words = (n_kblk + 31) / 32;
+  // alpha > 2 (a support of a few keys): the first refinement pass also
+  // gathers each row's keys above the bracket's lower end -- every key of the
+  // support at the root is one -- and a row with at most kCand of them solves
+  // the mass equation on them exactly (bisection in registers to fp32
+  // resolution) and stops; near a key entering the support, where the
+  // iterative steps crawl, this needs no further pass.  The row's histogram
+  // words, free once the counts are in registers, hold a counter (word swz)
+  // and the gathered (alpha-1) z (words swz + 1 + i, mod kBins).
+  constexpr int kCand = 8;
+  const bool gather = PK == kPowGeneral && p.alpha > 2.f;
+  const uint32_t cnt_lds = hrow_lds + ((uint32_t)swz << 2);
+  if (gather) lds_write_b32(cnt_lds, 0u);  // (after this lane's reads of the counts)
   for (int r = 0; r < p.n_iter; ++r) {
     const bool first = r == 0;
+    // u = (alpha-1) z - t above this: the key is above the bracket's lower end
+    // (less a margin for the rounding of u)
+    const float c_lo = blo - t - 1e-5f * fmaxf(1.f, fabsf(blo));
     const float t_mask = blo;  // <= every later tau
     // every pass rebuilds the block mask, so the mask of the pass the loop
     // ends after covers the final tau
@@ -398,7 +423,12 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, shi = 0.f;
     // alpha = 2: the u of the nearest key above t and at or below it
     float gap_up = INFINITY, gap_dn = -INFINITY;
-    dense_pass([&](int kv0, floatx16_t(&s)[kKt]) {
+    // one tile of the pass; kFirstGt2: the first pass at alpha > 2, which
+    // also forms g at the upper bracket end and gathers the keys above the
+    // lower one (a separate instantiation keeps those per-score branches out
+    // of every other pass)
+    auto refine_tile = [&](auto first_gt2_tag, int kv0, floatx16_t(&s)[kKt]) __attribute__((always_inline)) {
+      constexpr bool kFirstGt2 = decltype(first_gt2_tag)::value;
       float tmax = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < kKt; ++kt)
@@ -429,13 +459,31 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
               if (p.alpha <= 1.5f) s2 += r1 * ru;
             }
           }
-          if (p.alpha > 2.f && first) shi += powpos<PK>(__builtin_fmaf(s[kt][i], zs, -bhi), e);  // g at the upper end
+          if constexpr (kFirstGt2) {
+            shi += powpos<PK>(__builtin_fmaf(s[kt][i], zs, -bhi), e);  // g at the upper end
+            if (u > c_lo) {
+              const uint32_t idx = lds_inc_rtn(cnt_lds);
+              if (idx < (uint32_t)kCand)
+                lds_write_b32(hrow_lds + (((swz + 1 + (int)idx) & (kBins - 1)) << 2), __float_as_uint(s[kt][i] * zs));
+            }
+          }
         }
       // mark the 128-key block if some live row's scores clear t_mask
       const bool any = __builtin_amdgcn_ballot_w64(live && zs * tmax > t_mask) != 0;
       if (any && lane == 0)
         lds_or_b32((uint32_t)(uintptr_t)(lds_char_t *)(mbits + kv0 / kListBlock / 32), 1u << ((kv0 / kListBlock) % 32));
-    });
+    };
+    auto plain_pass = [&]() __attribute__((always_inline)) {
+      dense_pass([&](int kv0, floatx16_t(&s)[kKt]) { refine_tile(std::false_type{}, kv0, s); });
+    };
+    if constexpr (PK == kPowGeneral) {
+      if (gather && first)
+        dense_pass([&](int kv0, floatx16_t(&s)[kKt]) { refine_tile(std::true_type{}, kv0, s); });
+      else
+        plain_pass();
+    } else {
+      plain_pass();
+    }
     s0 = half_sum(s0);
     s1 = half_sum(s1);
     s2 = half_sum(s2);
@@ -480,6 +528,28 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
       if constexpr (PK == kPowLinear) exact = t_new - t < gap_up && t_new - t > gap_dn;
       t = inside ? t_new : 0.5f * (blo + bhi);  // bisection fallback (then not a last step)
       final_step = (last || exact) && inside;
+      if (gather && first) {
+        const uint32_t n_c = hrow[swz];
+        if (n_c <= (uint32_t)kCand) {  // the exact root on the gathered keys
+          float cv[kCand];
+#pragma unroll
+          for (int i = 0; i < kCand; ++i)
+            cv[i] = (uint32_t)i < n_c ? __uint_as_float(hrow[(swz + 1 + i) & (kBins - 1)]) : -INFINITY;
+          float xlo = blo, xhi = bhi;
+          for (int it = 0; it < 24; ++it) {
+            const float mid = 0.5f * (xlo + xhi);
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < kCand; ++i) sum += powpos<PK>(cv[i] - mid, e);
+            if (sum >= 1.f)
+              xlo = mid;
+            else
+              xhi = mid;
+          }
+          t = 0.5f * (xlo + xhi);
+          final_step = true;
+        }
+      }
     }
     // the workgroup stops once every live row has converged or taken its last step
     const bool wave_done = __builtin_amdgcn_ballot_w64(live && !conv && !final_step) == 0;

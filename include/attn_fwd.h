@@ -230,7 +230,9 @@ int attn_fwd_osk_validate(const attn_tensor_t *q, const attn_tensor_t *k, const 
  * fallback -- until every row of a 128-row tile has |sum p - 1| <= 4e-6, has
  * taken a last Halley step from |sum p - 1| <= 0.1 or Newton step from
  * 2e-3, has taken a sparsemax (alpha = 2) Newton step that no key crosses
- * (exact), or n_iter steps are done -- and finally visits only the 128 x 128
+ * (exact), has (alpha > 2) at most 8 keys above the histogram bound and
+ * solved the mass equation on them exactly, or n_iter steps are done --
+ * and finally visits only the 128 x 128
  * blocks that can hold a non-zero weight.  O is divided by sum p at the
  * final tau.
  *
