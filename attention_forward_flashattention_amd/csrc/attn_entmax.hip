@@ -331,9 +331,18 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   });
   const float m = m_raw * p.scale;  // (scale > 0)
   const int n_allowed = p.causal ? qrow + 1 : len;
-  // the histogram's root by bisection (both lane halves hold the same row and
-  // the same counts, so both compute the same tau_h): bin top - kBins + 1 + bb
-  // counts at u = (alpha-1) z of its lower edge, ebase + bb * ebw
+  // The histogram's root tau_h (both lane halves hold the same row and the
+  // same counts, so both compute the same value).  Bin ilo + bb counts at
+  // u = (alpha-1) z of its lower edge E_bb = ebase + bb * ebw.  Measured in
+  // bins from edge E_k, bin bb > k sits at j = bb - k, so the histogram's
+  // mass at E_k is ebw^e G_k with G_k = sum_{bb > k} cnt[bb] j^e: G_k falls
+  // with k, G_0 >= 31^e (the top bin holds the maximum) and G_31 = 0, so the
+  // root lies in the bin [E_ks, E_ks + ebw) of the largest ks with
+  // G_ks >= R = 31^e.  Inside it the mass has no kink: with tau = E_ks + y ebw
+  // the root solves H(y) = sum_{bb > ks} cnt[bb] (j - y)^e - R = 0 on [0, 1],
+  // in closed form for alpha = 2, by Newton from y = 0 for e >= 1 (H convex
+  // and falling: the iterates rise to the root from below, each a lower
+  // bound), and by bisection for e < 1.
   const bool counted = topf > -1e29f;  // (rows past the end count nothing)
   const int ilo = counted ? (int)topf - (kBins - 1) : 0;
   float cnt[kBins];
@@ -341,18 +350,78 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   for (int bb = 0; bb < kBins; ++bb) cnt[bb] = (float)hrow[(ilo + bb + swz) & (kBins - 1)];
   const float ebw = 1.f / (float)(kBins - 1);  // (alpha-1) bw
   const float ebase = (anchor + (float)ilo) * ebw;
-  float lo = a1 * m - 2.f, hi_t = a1 * m;
-  for (int it = 0; it < 30; ++it) {
-    const float mid = 0.5f * (lo + hi_t);
-    float sum = 0.f;
+  // d^e and d^(e-1) for d > 0
+  auto pw_e = [&](float d) __attribute__((always_inline)) -> float {
+    if constexpr (PK == kPowSquare) return d * d;
+    else if constexpr (PK == kPowLinear) return d;
+    else return __builtin_amdgcn_exp2f(e * __builtin_amdgcn_logf(d));
+  };
+  float pw[kBins];  // j^e
 #pragma unroll
-    for (int bb = 0; bb < kBins; ++bb) sum += cnt[bb] * powpos<PK>(__builtin_fmaf((float)bb, ebw, ebase) - mid, e);
-    if (sum >= 1.f)
-      lo = mid;
-    else
-      hi_t = mid;
+  for (int j = 0; j < kBins; ++j) pw[j] = j == 0 ? 0.f : pw_e((float)j);
+  const float R = pw[kBins - 1];
+  int ks = 0;
+#pragma unroll
+  for (int k = 1; k < kBins - 1; ++k) {
+    float g = 0.f;
+#pragma unroll
+    for (int bb = k + 1; bb < kBins; ++bb) g = __builtin_fmaf(cnt[bb], pw[bb - k], g);
+    if (g >= R) ks = k;
   }
-  const float tau_h = lo;  // lo keeps sum >= 1: a lower bound of the histogram's root
+  float wcnt[kBins], jd[kBins];  // counts of the bins above ks, and their j
+#pragma unroll
+  for (int bb = 0; bb < kBins; ++bb) {
+    wcnt[bb] = bb > ks ? cnt[bb] : 0.f;
+    jd[bb] = (float)(bb - ks);
+  }
+  float y;
+  if constexpr (PK == kPowLinear) {
+    float s_c = 0.f, s_j = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < kBins; ++bb) {
+      s_c += wcnt[bb];
+      s_j = __builtin_fmaf(wcnt[bb], jd[bb], s_j);
+    }
+    y = (s_j - R) / s_c;
+  } else if (e >= 1.f) {
+    y = 0.f;
+    for (int it = 0; it < 6; ++it) {
+      float h = -R, dh = 0.f;
+#pragma unroll
+      for (int bb = 0; bb < kBins; ++bb) {
+        const float d = fmaxf(jd[bb] - y, 1e-30f);
+        float de, dm;
+        if constexpr (PK == kPowSquare) {
+          dm = d;
+          de = d * d;
+        } else {
+          const float l = __builtin_amdgcn_logf(d);
+          de = __builtin_amdgcn_exp2f(e * l);
+          dm = __builtin_amdgcn_exp2f((e - 1.f) * l);
+        }
+        h = __builtin_fmaf(wcnt[bb], de, h);
+        dh = __builtin_fmaf(wcnt[bb], dm, dh);
+      }
+      y += h / (e * dh);
+    }
+  } else {
+    float ylo = 0.f, yhi = 1.f;
+    for (int it = 0; it < 20; ++it) {
+      const float mid = 0.5f * (ylo + yhi);
+      float h = -R;
+#pragma unroll
+      for (int bb = 0; bb < kBins; ++bb) h = __builtin_fmaf(wcnt[bb], pw_e(fmaxf(jd[bb] - mid, 1e-30f)), h);
+      if (h >= 0.f)
+        ylo = mid;
+      else
+        yhi = mid;
+    }
+    y = ylo;
+  }
+  y = counted ? fminf(fmaxf(y, 0.f), 1.f) : 0.f;
+  // less a few ulps, so that rounding leaves it below the histogram's root
+  const float tau_h0 = __builtin_fmaf((float)ks + y, ebw, ebase);
+  const float tau_h = tau_h0 - 2.5e-7f * fmaxf(1.f, fabsf(tau_h0));
   // ---- pass 2: refinement.  Bracket [blo, bhi] of the true tau: tau_h is
   // below it; counting every score at its bin's upper edge instead would
   // raise every score by at most bw and the root by at most (alpha-1) bw =
@@ -364,25 +433,11 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
                     tau_h + ebw * (1.f + 1e-4f) + 1e-6f * fabsf(tau_h));
   if (!(bhi > blo)) bhi = blo + 1e-6f * fmaxf(1.f, fabsf(blo));
   // Starting point: the histogram's root with every score counted at its
-  // bin's midpoint (between the lower- and upper-edge placements, so within
-  // [tau_h, tau_h + ebw]), found by bisection in that bracket: an estimate
-  // close enough that one Halley or Newton step usually finishes the row.
-  float t;
-  {
-    float mlo = blo, mhi = bhi;
-    for (int it = 0; it < 14; ++it) {
-      const float mid = 0.5f * (mlo + mhi);
-      float sum = 0.f;
-#pragma unroll
-      for (int bb = 0; bb < kBins; ++bb)
-        sum += cnt[bb] * powpos<PK>(__builtin_fmaf((float)bb + 0.5f, ebw, ebase) - mid, e);
-      if (sum >= 1.f)
-        mlo = mid;
-      else
-        mhi = mid;
-    }
-    t = 0.5f * (mlo + mhi);
-  }
+  // bin's midpoint, between the lower- and upper-edge placements: that
+  // histogram is the lower-edge one moved up by half a bin, so its root is
+  // tau_h + ebw / 2 -- close enough that one Halley or Newton step usually
+  // finishes the row.
+  float t = fminf(fmaxf(tau_h0 + 0.5f * ebw, blo), bhi);
   // regula falsi state (alpha > 2): g at the bracket ends, and which end moved last
   float glo = 0.f, ghi = 0.f;
   int side = 0;

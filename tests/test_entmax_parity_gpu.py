@@ -94,6 +94,7 @@ CASES = [
     ("e_secant", 65, 1, 390, 4, 4, 128, True, 3.0, 32),
     ("e_secant_mid", 69, 1, 260, 2, 1, 64, False, 2.5, 32),
     ("e_newton", 66, 2, 129, 2, 1, 128, False, 1.75, 16),
+    ("e_alpha_low", 70, 1, 200, 2, 1, 64, True, 1.05, 16),   # e = 20: the steepest weights allowed
 ]
 
 
