@@ -137,10 +137,11 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   // in the V half of buffer 0 when it fits there (it is read into registers
   // before the output pass loads V).
   constexpr bool kHistInV = kTileBytes >= kHistBytes;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes + kMaskBytes + 16 + (kHistInV ? 0 : kHistBytes)];
+  // (the flags take 128 bytes, so that the histogram's rows stay 128-byte aligned)
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes + kMaskBytes + 128 + (kHistInV ? 0 : kHistBytes)];
   uint32_t *mbits = reinterpret_cast<uint32_t *>(smem + 2 * kBufBytes);
   uint32_t *done_flag = mbits + kMaxKBlocks / 32;  // one per wave
-  uint32_t *hist = reinterpret_cast<uint32_t *>(kHistInV ? smem + kTileBytes : smem + 2 * kBufBytes + kMaskBytes + 16);
+  uint32_t *hist = reinterpret_cast<uint32_t *>(kHistInV ? smem + kTileBytes : smem + 2 * kBufBytes + kMaskBytes + 128);
 
   const int n_units = p.batch * p.hq;
   const int rank = blockIdx.x / n_units;
@@ -284,6 +285,8 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   // hit the same bin hit different banks; the rotation is folded into the
   // score's FMA, which then yields the word index directly.
   static_assert(kBins == 32, "one ring slot per LDS bank");
+  static_assert(((kHistInV ? kTileBytes : 2 * kBufBytes + kMaskBytes + 128) % 128) == 0,
+                "histogram rows start on 128-byte boundaries");
   for (int i = tid; i < kBM * kBins; i += 256) hist[i] = 0u;
   for (int i = tid; i < (n_kblk + 31) / 32; i += 256) mbits[i] = 0u;
   __syncthreads();
@@ -318,15 +321,20 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
         if (c < n_clr) lds_write_b32(hrow_lds + (((itop - c + swz) & (kBins - 1)) << 2), 0u);
       topf = fmaxf(topf, ntop);
     }
-    // t = bin + rotation; counted when bin >= topf - (kBins - 1)
-    const float lo_t = topf - (float)(kBins - 1) + (float)swz;
-    const float anchor_r = anchor - (float)swz;
+    // t4 = 4 (bin + rotation), exactly four times the unscaled FMA (scaling
+    // by 4 commutes with rounding); counted when bin >= topf - (kBins - 1).
+    // Truncating t4 gives 4 floor(t4 / 4) plus 0..3, so masking it with
+    // 4 (kBins - 1) yields the byte offset of the word (bin + rotation) mod
+    // kBins directly (t4 > 0 in the window; the row base is 128-byte aligned).
+    const float lo_t4 = 4.f * (topf - (float)(kBins - 1) + (float)swz);
+    const float anchor_r4 = 4.f * (anchor - (float)swz);
+    const float c_h4 = 4.f * c_h;
 #pragma unroll
     for (int kt = 0; kt < kKt; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float t = __builtin_fmaf(s[kt][i], c_h, -anchor_r);  // -inf for masked scores
-        if (t >= lo_t) lds_add_u32(hrow_lds + ((((int)t) & (kBins - 1)) << 2), 1u);
+        const float t4 = __builtin_fmaf(s[kt][i], c_h4, -anchor_r4);  // -inf for masked scores
+        if (t4 >= lo_t4) lds_add_u32(((uint32_t)(int)t4 & (uint32_t)(4 * (kBins - 1))) | hrow_lds, 1u);
       }
   });
   const float m = m_raw * p.scale;  // (scale > 0)
@@ -476,6 +484,7 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
     for (int w = tid; w < m_words; w += 256) mbits[w] = 0u;
     __syncthreads();
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, shi = 0.f;
+    uint32_t n_pos = 0;  // alpha = 1.5: keys with u > 0 (s2), counted as an integer
     // alpha = 2: the u of the nearest key above t and at or below it
     float gap_up = INFINITY, gap_dn = -INFINITY;
     // one tile of the pass; kFirstGt2: the first pass at alpha > 2, which
@@ -498,7 +507,7 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
           if constexpr (PK == kPowSquare) {
             s0 = __builtin_fmaf(up, up, s0);
             s1 += up;
-            s2 += pos;
+            n_pos += u > 0.f ? 1u : 0u;
           } else if constexpr (PK == kPowLinear) {
             s0 += up;
             s1 += pos;
@@ -541,6 +550,7 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
     }
     s0 = half_sum(s0);
     s1 = half_sum(s1);
+    if constexpr (PK == kPowSquare) s2 = (float)n_pos;
     s2 = half_sum(s2);
     if constexpr (PK == kPowLinear) {
       gap_up = -half_max(-gap_up);
