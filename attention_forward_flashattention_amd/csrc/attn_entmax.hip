@@ -98,14 +98,7 @@ __device__ __forceinline__ void lds_or_b32(uint32_t addr, uint32_t v) {
 __device__ __forceinline__ void lds_write_b32(uint32_t addr, uint32_t v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
-// LDS counter increment that returns the old value (waited for in the same
-// assembly block)
-__device__ __forceinline__ uint32_t lds_inc_rtn(uint32_t addr) {
-  uint32_t old;
-  const uint32_t one = 1u;
-  asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(old) : "v"(addr), "v"(one) : "memory");
-  return old;
-}
+
 
 template <int kLoads>
 __device__ __forceinline__ void issue_rows(char *l, const uint16_t *g, const int64_t *off,
@@ -131,17 +124,20 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   constexpr int kTileBytes = kBN * kRowBytes;
   constexpr int kBufBytes = 2 * kTileBytes;  // K then V
   constexpr int kLoads = kTileBytes / 1024 / kNW;
-  constexpr int kHistBytes = kBM * kBins * 4;
+  // Histogram: every lane keeps its own kBins words (a row's two lane halves
+  // count separately), word b of lane l of a wave at b * 64 + l of the
+  // wave's 8 KB: the lanes of one LDS instruction always hit distinct banks,
+  // whatever bins they count, and no word is shared.
+  constexpr int kWaveHistBytes = 64 * kBins * 4;
+  constexpr int kHistBytes = kNW * kWaveHistBytes;
   constexpr int kMaskBytes = kMaxKBlocks / 8;
-  // The passes before the output pass load K only, so the histogram can live
-  // in the V half of buffer 0 when it fits there (it is read into registers
-  // before the output pass loads V).
-  constexpr bool kHistInV = kTileBytes >= kHistBytes;
-  // (the flags take 128 bytes, so that the histogram's rows stay 128-byte aligned)
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes + kMaskBytes + 128 + (kHistInV ? 0 : kHistBytes)];
-  uint32_t *mbits = reinterpret_cast<uint32_t *>(smem + 2 * kBufBytes);
+  // The passes before the output pass load K only, so the histograms can live
+  // in the V halves of the two buffers (two waves' each) when they fit there
+  // (they are read into registers before the output pass loads V).
+  constexpr bool kHistInV = kTileBytes >= 2 * kWaveHistBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes + (kHistInV ? 0 : kHistBytes) + kMaskBytes + 16];
+  uint32_t *mbits = reinterpret_cast<uint32_t *>(smem + 2 * kBufBytes + (kHistInV ? 0 : kHistBytes));
   uint32_t *done_flag = mbits + kMaxKBlocks / 32;  // one per wave
-  uint32_t *hist = reinterpret_cast<uint32_t *>(kHistInV ? smem + kTileBytes : smem + 2 * kBufBytes + kMaskBytes + 128);
 
   const int n_units = p.batch * p.hq;
   const int rank = blockIdx.x / n_units;
@@ -284,16 +280,18 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   // (b + row) mod kBins of the row's kBins words), so the lanes of a wave that
   // hit the same bin hit different banks; the rotation is folded into the
   // score's FMA, which then yields the word index directly.
-  static_assert(kBins == 32, "one ring slot per LDS bank");
-  static_assert(((kHistInV ? kTileBytes : 2 * kBufBytes + kMaskBytes + 128) % 128) == 0,
-                "histogram rows start on 128-byte boundaries");
-  for (int i = tid; i < kBM * kBins; i += 256) hist[i] = 0u;
+  static_assert(kBins == 32 && kWaveHistBytes == 8192, "a lane's word of bin b sits at b << 8 of its base");
+  static_assert(kTileBytes % kWaveHistBytes == 0 && (2 * kBufBytes) % kWaveHistBytes == 0,
+                "wave histograms start on 8 KB boundaries");
+  uint32_t *hwave = reinterpret_cast<uint32_t *>(
+      kHistInV ? smem + (wave >> 1) * kBufBytes + kTileBytes + (wave & 1) * kWaveHistBytes
+               : smem + 2 * kBufBytes + wave * kWaveHistBytes);
+  for (int i = lane; i < 64 * kBins; i += 64) hwave[i] = 0u;
   for (int i = tid; i < (n_kblk + 31) / 32; i += 256) mbits[i] = 0u;
   __syncthreads();
   const float c_h = p.scale * (float)(kBins - 1) * a1;  // z / bw per unit of q.k
-  const int swz = row & (kBins - 1);
-  uint32_t *hrow = hist + row * kBins;
-  const uint32_t hrow_lds = (uint32_t)(uintptr_t)(lds_char_t *)hrow;
+  // this lane's words: bin b at hl + (b << 8); the other half of the row's at hl ^ 128
+  const uint32_t hl = (uint32_t)(uintptr_t)(lds_char_t *)hwave + (uint32_t)lane * 4u;
   // The anchor sits kAnchorBelow bins below the first maximum, so every bin
   // in the window has a positive index (truncation is the floor there).
   constexpr float kAnchorBelow = 2.f * kBins;
@@ -311,30 +309,35 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
     if (kv0 == 0 && tm > -INFINITY) anchor = floorf(tm * c_h) - kAnchorBelow;
     m_raw = fmaxf(m_raw, tm);
     const float ntop = tm > -INFINITY ? floorf(__builtin_fmaf(tm, c_h, -anchor)) : topf;
-    const float rise = fminf(ntop - topf, (float)kBins);  // kBins on the first tile
-    if (__builtin_amdgcn_ballot_w64(rise > 0.f) != 0) {
+    // bins (topf, ntop] enter the window: clear their slots (none on the
+    // first tile, where every slot is still zero), as many steps as the
+    // wave's largest rise (one or two bins once the maximum has settled)
+    const float rise = fminf(ntop - topf, (float)kBins);
+    if (__builtin_amdgcn_ballot_w64(kv0 > 0 && rise > 0.f) != 0) {
       const int n_clr = rise > 0.f ? (int)rise : 0;
       const int itop = rise > 0.f ? (int)ntop : 0;
-      // (as many steps as the wave's largest rise: one or two bins once the
-      // maximum has settled, kBins on the first tile)
       for (int c = 0; __builtin_amdgcn_ballot_w64(c < n_clr) != 0; ++c)
-        if (c < n_clr) lds_write_b32(hrow_lds + (((itop - c + swz) & (kBins - 1)) << 2), 0u);
-      topf = fmaxf(topf, ntop);
+        if (c < n_clr) lds_write_b32(hl + ((uint32_t)((itop - c) & (kBins - 1)) << 8), 0u);
     }
-    // t4 = 4 (bin + rotation), exactly four times the unscaled FMA (scaling
-    // by 4 commutes with rounding); counted when bin >= topf - (kBins - 1).
-    // Truncating t4 gives 4 floor(t4 / 4) plus 0..3, so masking it with
-    // 4 (kBins - 1) yields the byte offset of the word (bin + rotation) mod
-    // kBins directly (t4 > 0 in the window; the row base is 128-byte aligned).
-    const float lo_t4 = 4.f * (topf - (float)(kBins - 1) + (float)swz);
-    const float anchor_r4 = 4.f * (anchor - (float)swz);
-    const float c_h4 = 4.f * c_h;
+    topf = fmaxf(topf, ntop);
+    // t8 = 256 bin, exactly 256 times the unscaled FMA (scaling by a power of
+    // two commutes with rounding); counted when bin >= topf - (kBins - 1).
+    // Truncating t8 gives 256 floor(t8 / 256) plus 0..255, so masking it
+    // with (kBins - 1) << 8 yields the byte offset of the bin's word (mod
+    // kBins) directly (t8 > 0 in the window; hl has no bits 8..12).
+    const float lo_t8 = 256.f * (topf - (float)(kBins - 1));
+    const float anchor8 = 256.f * anchor;
+    const float c_h8 = 256.f * c_h;
 #pragma unroll
     for (int kt = 0; kt < kKt; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float t4 = __builtin_fmaf(s[kt][i], c_h4, -anchor_r4);  // -inf for masked scores
-        if (t4 >= lo_t4) lds_add_u32(((uint32_t)(int)t4 & (uint32_t)(4 * (kBins - 1))) | hrow_lds, 1u);
+        const float t8 = __builtin_fmaf(s[kt][i], c_h8, -anchor8);  // -inf for masked scores
+        // every lane adds, 0 for a score below the window (at the window's
+        // lowest bin): no branch and exec-mask change per score
+        const uint32_t inc = t8 >= lo_t8 ? 1u : 0u;
+        const float t8c = fmaxf(t8, lo_t8);
+        lds_add_u32(((uint32_t)(int)t8c & (uint32_t)((kBins - 1) << 8)) | hl, inc);
       }
   });
   const float m = m_raw * p.scale;  // (scale > 0)
@@ -355,7 +358,10 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   const int ilo = counted ? (int)topf - (kBins - 1) : 0;
   float cnt[kBins];
 #pragma unroll
-  for (int bb = 0; bb < kBins; ++bb) cnt[bb] = (float)hrow[(ilo + bb + swz) & (kBins - 1)];
+  for (int bb = 0; bb < kBins; ++bb) {
+    const int w = ((ilo + bb) & (kBins - 1)) * 64;
+    cnt[bb] = (float)(hwave[w + lane] + hwave[w + (lane ^ 32)]);
+  }
   const float ebw = 1.f / (float)(kBins - 1);  // (alpha-1) bw
   const float ebase = (anchor + (float)ilo) * ebw;
   // d^e and d^(e-1) for d > 0
@@ -466,13 +472,13 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   // support at the root is one -- and a row with at most kCand of them solves
   // the mass equation on them exactly (bisection in registers to fp32
   // resolution) and stops; near a key entering the support, where the
-  // iterative steps crawl, this needs no further pass.  The row's histogram
-  // words, free once the counts are in registers, hold a counter (word swz)
-  // and the gathered (alpha-1) z (words swz + 1 + i, mod kBins).
+  // iterative steps crawl, this needs no further pass.  Each lane writes the
+  // (alpha-1) z of its own such keys to its histogram words 1, 2, ... (free
+  // once the counts are in registers) and counts them in a register; the
+  // row's list is its two lane halves' lists together.
   constexpr int kCand = 8;
   const bool gather = PK == kPowGeneral && p.alpha > 2.f;
-  const uint32_t cnt_lds = hrow_lds + ((uint32_t)swz << 2);
-  if (gather) lds_write_b32(cnt_lds, 0u);  // (after this lane's reads of the counts)
+  uint32_t n_own = 0;  // keys this lane gathered
   for (int r = 0; r < p.n_iter; ++r) {
     const bool first = r == 0;
     // u = (alpha-1) z - t above this: the key is above the bracket's lower end
@@ -526,9 +532,8 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
           if constexpr (kFirstGt2) {
             shi += powpos<PK>(__builtin_fmaf(s[kt][i], zs, -bhi), e);  // g at the upper end
             if (u > c_lo) {
-              const uint32_t idx = lds_inc_rtn(cnt_lds);
-              if (idx < (uint32_t)kCand)
-                lds_write_b32(hrow_lds + (((swz + 1 + (int)idx) & (kBins - 1)) << 2), __float_as_uint(s[kt][i] * zs));
+              if (n_own < (uint32_t)kCand) lds_write_b32(hl + ((n_own + 1u) << 8), __float_as_uint(s[kt][i] * zs));
+              ++n_own;
             }
           }
         }
@@ -558,6 +563,8 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
     }
     const float g = s0 - 1.f;
     if (p.alpha > 2.f && first) ghi = half_sum(shi) - 1.f;
+    uint32_t n_part = 0;  // keys the other half of the row gathered
+    if (gather && first) n_part = (uint32_t)half_sum((float)n_own) - n_own;
     // converged: keep t (the bracket may have closed on it); a row that took
     // its final step keeps the t that step gave; a bracket closed to fp32
     // resolution cannot narrow further
@@ -594,12 +601,15 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
       t = inside ? t_new : 0.5f * (blo + bhi);  // bisection fallback (then not a last step)
       final_step = (last || exact) && inside;
       if (gather && first) {
-        const uint32_t n_c = hrow[swz];
+        const uint32_t n_c = n_own + n_part;
         if (n_c <= (uint32_t)kCand) {  // the exact root on the gathered keys
           float cv[kCand];
 #pragma unroll
-          for (int i = 0; i < kCand; ++i)
-            cv[i] = (uint32_t)i < n_c ? __uint_as_float(hrow[(swz + 1 + i) & (kBins - 1)]) : -INFINITY;
+          for (int i = 0; i < kCand; ++i) {
+            const uint32_t j = (uint32_t)i < n_own ? (uint32_t)i : (uint32_t)i - n_own;
+            const int src = (uint32_t)i < n_own ? lane : (lane ^ 32);
+            cv[i] = (uint32_t)i < n_c ? __uint_as_float(hwave[(int)(j + 1u) * 64 + src]) : -INFINITY;
+          }
           float xlo = blo, xhi = bhi;
           for (int it = 0; it < 24; ++it) {
             const float mid = 0.5f * (xlo + xhi);
