@@ -11,11 +11,11 @@
 // kernel):
 //   1. the row maximum m and, in the same pass, a histogram of the scores
 //      in the window [m - W, m], W = 1/(alpha-1) (only those can carry
-//      weight): kBins bins per row in LDS of width W/(kBins-1) on a fixed
-//      grid, kept as a ring that follows the running maximum; each score
+//      weight): kBins bins in LDS of width W/(kBins-1) on a fixed grid,
+//      kept per lane as a ring that follows the running maximum; each score
 //      counts at its bin's lower edge, so the root tau_h of the histogram's
-//      mass equation is a lower bound of the true tau; each lane solves it
-//      by bisection over the bins;
+//      mass equation is a lower bound of the true tau; each lane finds the
+//      bin that holds it and solves inside that bin;
 //   2. up to n_iter refinement passes (fewer once every row of the workgroup
 //      has converged or taken its last step), each forming the power sums the update needs
 //      at the current tau and taking one step of the hybrid solver (Halley
@@ -272,14 +272,11 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   // per-row integer anchor taken at the first tile, so the bin arithmetic
   // stays small); the kBins bins top - kBins + 1 .. top, top the bin of the
   // running maximum, cover the window [m - W, m] whatever m turns out to be.
-  // They live in a ring of kBins slots per row (bin b in slot b mod kBins):
-  // when a tile raises top, the slots of the bins that leave the window are
-  // cleared for the bins that enter it.  Scores below the window (at the
-  // time they are seen, so also at the end) cannot carry weight and are not
-  // counted.  A row's ring is rotated by row % 32 (bin b at word
-  // (b + row) mod kBins of the row's kBins words), so the lanes of a wave that
-  // hit the same bin hit different banks; the rotation is folded into the
-  // score's FMA, which then yields the word index directly.
+  // They live in a ring of kBins slots (bin b in slot b mod kBins) per lane,
+  // each half of a row counting its own keys (the layout above): when a
+  // tile raises top, the slots of the bins that leave the window are cleared
+  // for the bins that enter it.  Scores below the window (at the time they
+  // are seen, so also at the end) cannot carry weight and are not counted.
   static_assert(kBins == 32 && kWaveHistBytes == 8192, "a lane's word of bin b sits at b << 8 of its base");
   static_assert(kTileBytes % kWaveHistBytes == 0 && (2 * kBufBytes) % kWaveHistBytes == 0,
                 "wave histograms start on 8 KB boundaries");
