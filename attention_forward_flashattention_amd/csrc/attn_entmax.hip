@@ -110,12 +110,15 @@ __device__ __forceinline__ void issue_rows(char *l, const uint16_t *g, const int
   }
 }
 
+// Two workgroups per CU; one at head_dim 256, whose Q rows and O
+// accumulators need more than the 256 registers of two waves per SIMD.
 template <int D, int PK>
-__global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
+__global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void attn_entmax_kernel(EntParams p) {
   using L = Lds<D>;
   constexpr int kNW = 4;
   constexpr int kBM = 128;
-  constexpr int kBN = 64;
+  constexpr int kBN = D == 256 ? 32 : 64;  // keys per tile (32 at head_dim 256: registers)
+  constexpr int kTpb = kListBlock / kBN;    // tiles per 128-key block
   constexpr int kRowBytes = D * 2;
   constexpr int kChunks = D / 8;
   constexpr int kDc = D / 16;
@@ -642,17 +645,17 @@ __global__ __launch_bounds__(256, 2) void attn_entmax_kernel(EntParams p) {
   float l = 0.f;
   int n_blk = 0;
   for (int w = 0; w < m_words; ++w) n_blk += __builtin_popcount(mbits[w]);
-  const int n_out = 2 * n_blk;  // two 64-key tiles per block
+  const int n_out = kTpb * n_blk;
   int c_w = -1;
   uint32_t c_bits = 0;
   int c_blk = 0;
   auto out_kv = [&](int it) -> int {  // in order
-    if ((it & 1) == 0) {
+    if (it % kTpb == 0) {
       while (c_bits == 0) c_bits = mbits[++c_w];
       c_blk = 32 * c_w + __builtin_ctz(c_bits);
       c_bits &= c_bits - 1u;
     }
-    return c_blk * kListBlock + (it & 1) * kBN;
+    return c_blk * kListBlock + (it % kTpb) * kBN;
   };
   uint32_t vlds[kDt];
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_char_t *)smem;
@@ -751,7 +754,6 @@ extern "C" int attn_entmax_fwd_validate(const attn_tensor_t *q, const attn_tenso
   // forward's tolerances (a key 1e-6 above the edge already weighs 0.03 at
   // alpha = 5); below 1.05 the window 1/(alpha-1) outgrows fp32 range use.
   if (alpha > 3.f || alpha < 1.05f) return ATTN_ERR_UNSUPPORTED;
-  if (q->head_dim == 256) return ATTN_ERR_UNSUPPORTED;
   const int64_t n_blk = (q->seqlen + kListBlock - 1) / kListBlock;
   if (n_blk > kMaxKBlocks) return ATTN_ERR_UNSUPPORTED;
   if (mask_words < 0) return ATTN_ERR_INVALID_ARG;
@@ -794,14 +796,17 @@ extern "C" int attn_entmax_fwd(const attn_tensor_t *q, const attn_tensor_t *k,
   // integer exponents (alpha = 2: e = 1; alpha = 1.5: e = 2) take the
   // instantiation without transcendentals
   const int pk = alpha == 2.f ? kPowLinear : (alpha == 1.5f ? kPowSquare : kPowGeneral);
-  const void *fns[2][3] = {
+  const void *fns[3][3] = {
       {reinterpret_cast<const void *>(&attn_entmax_kernel<64, kPowGeneral>),
        reinterpret_cast<const void *>(&attn_entmax_kernel<64, kPowLinear>),
        reinterpret_cast<const void *>(&attn_entmax_kernel<64, kPowSquare>)},
       {reinterpret_cast<const void *>(&attn_entmax_kernel<128, kPowGeneral>),
        reinterpret_cast<const void *>(&attn_entmax_kernel<128, kPowLinear>),
-       reinterpret_cast<const void *>(&attn_entmax_kernel<128, kPowSquare>)}};
-  const void *fn = fns[q->head_dim == 64 ? 0 : 1][pk];
+       reinterpret_cast<const void *>(&attn_entmax_kernel<128, kPowSquare>)},
+      {reinterpret_cast<const void *>(&attn_entmax_kernel<256, kPowGeneral>),
+       reinterpret_cast<const void *>(&attn_entmax_kernel<256, kPowLinear>),
+       reinterpret_cast<const void *>(&attn_entmax_kernel<256, kPowSquare>)}};
+  const void *fn = fns[q->head_dim == 64 ? 0 : (q->head_dim == 128 ? 1 : 2)][pk];
   const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;

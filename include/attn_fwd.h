@@ -249,8 +249,8 @@ int attn_fwd_osk_validate(const attn_tensor_t *q, const attn_tensor_t *k, const 
  *   tau_init     NULL, or float32 [B, Hq, S]: the histogram lower bound
  * Returns what attn_fwd returns for q, k, v, out (no cu_seqlens, no list), or
  * ATTN_ERR_INVALID_ARG for alpha <= 1 or not finite, n_iter outside 1..32, or
- * too few mask words; ATTN_ERR_UNSUPPORTED for alpha outside [1.05, 3],
- * head_dim 256, or more than 16384 blocks of 128 per sequence.
+ * too few mask words; ATTN_ERR_UNSUPPORTED for alpha outside [1.05, 3] or
+ * more than 16384 blocks of 128 per sequence.
  */
 int attn_entmax_fwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
                     int causal, float scale, float alpha, int n_iter, attn_tensor_t *out,

@@ -276,7 +276,8 @@ def test_entmax_argument_checks():
     assert val(alpha=1.0) == -1 and val(alpha=float("nan")) == -1 and val(alpha=float("inf")) == -1
     assert val(n_iter=0) == -1 and val(n_iter=33) == -1
     assert val(alpha=1.01) == -2 and val(alpha=3.5) == -2
-    assert val(qd=desc(b=2, s=256, h=4, d=256), kd=desc(b=2, s=256, h=2, d=256)) == -2
+    assert val(qd=desc(b=2, s=256, h=4, d=256), kd=desc(b=2, s=256, h=2, d=256)) == 0
+    assert val(qd=desc(b=2, s=256, h=4, d=96), kd=desc(b=2, s=256, h=2, d=96)) == -2
     s = 128 * 33                                        # 33 blocks need 2 mask words
     assert val(words=1, qd=desc(b=1, s=s, h=4), kd=desc(b=1, s=s, h=2)) == -1
     assert val(words=2, qd=desc(b=1, s=s, h=4), kd=desc(b=1, s=s, h=2)) == 0

@@ -95,6 +95,8 @@ CASES = [
     ("e_secant_mid", 69, 1, 260, 2, 1, 64, False, 2.5, 32),
     ("e_newton", 66, 2, 129, 2, 1, 128, False, 1.75, 16),
     ("e_alpha_low", 70, 1, 200, 2, 1, 64, True, 1.05, 16),   # e = 20: the steepest weights allowed
+    ("e_d256_causal", 71, 2, 300, 4, 2, 256, True, 1.5, 16),  # head_dim 256: 32-key tiles
+    ("e_d256_secant", 72, 1, 230, 2, 1, 256, False, 2.5, 32),
 ]
 
 

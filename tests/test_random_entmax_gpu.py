@@ -1,7 +1,7 @@
 """Seeded random sweep of alpha-entmax attention against the fp64 oracle.
 
 Each case draws alpha (1.5 and 2, which have kernels of their own, or a
-value uniform in [1.05, 3]), head_dim 64 or 128, the KV head count and GQA
+value uniform in [1.05, 3]), head_dim 64, 128 or 256, the KV head count and GQA
 group, the causal flag, the softmax scale, the memory order and a length
 that mixes tile edges with arbitrary values; the checks are those of
 tests/test_entmax_parity_gpu.py (O at the forward's tolerances, the
@@ -16,7 +16,7 @@ import pytest
 
 import attn_workloads as W
 
-HEAD_DIMS = (64, 128)
+HEAD_DIMS = (64, 128, 256)
 ALPHA_KINDS = ("1.5", "2", "below 2", "above 2")
 N_CASES = 3 * len(HEAD_DIMS) * len(ALPHA_KINDS)
 EDGES = (1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 384, 385)
