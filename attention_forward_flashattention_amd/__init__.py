@@ -96,6 +96,8 @@ def load_library(path: str = LIB_PATH):
                                           T, P, ctypes.c_size_t]
         lib.attn_bwd_noalloc.restype = ctypes.c_int
         lib.attn_bwd_noalloc.argtypes = [T, T, T, T, T, P, P, ctypes.c_int, ctypes.c_float, BM, T, T, T, P]
+        lib.attn_block_list_to_mask.restype = ctypes.c_int
+        lib.attn_block_list_to_mask.argtypes = [BL, ctypes.c_int, P, ctypes.c_int, P]
         lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
         lib.attn_bwd_workspace_size.argtypes = [T]
         lib.attn_status_str.restype = ctypes.c_char_p
@@ -428,20 +430,47 @@ def _bwd_prepare(q, k, v, out, dout, lse, cu_seqlens, max_seqlen, block_mask, dq
     return descs, bm, cu_p, float(scale), (dq, dk, dv)
 
 
+def block_list_to_mask(block_list: Tuple, seqlen: int, stream=None):
+    """The bit-packed block mask of a block list's set (``attn_block_list_to_mask``):
+    int32 [1, 1, ceil(S/128), words], one sequence's mask shared by every KV head, the
+    form ``attn_bwd``'s ``block_mask`` takes for the backward of a forward that took
+    the list (ids outside the sequence are dropped, as the forward skips them)."""
+    import torch
+
+    lib = load_library()
+    _check_block_list(block_list, seqlen)
+    n_blk = (seqlen + 127) // 128
+    words = max(1, (n_blk + 31) // 32)
+    mask = torch.empty((1, 1, n_blk, words), dtype=torch.int32, device=block_list[0].device)
+    st = lib.attn_block_list_to_mask(ctypes.byref(_list_descriptor(block_list)), n_blk,
+                                     ctypes.c_void_p(mask.data_ptr()), words, ctypes.c_void_p(_stream_handle(stream)))
+    if st != ATTN_OK:
+        raise AttnError(st, status_str(st), "attn_block_list_to_mask")
+    return mask
+
+
 def attn_bwd(q, k, v, out, dout, lse, cu_seqlens=None, causal: bool = False,
              scale: Optional[float] = None, max_seqlen: Optional[int] = None, block_mask=None,
-             dq=None, dk=None, dv=None, workspace=None, stream=None):
+             dq=None, dk=None, dv=None, workspace=None, stream=None, block_list: Optional[Tuple] = None):
     """Gradients (dq, dk, dv) of sum(out * dout) for out, lse = attn_fwd(q, k, v, ...).
 
     q, out, dout: bf16 [B, S, Hq, D] (packed [T, Hq, D] with ``cu_seqlens``)
     k, v: bf16 [B, S, Hkv, D] (packed [T, Hkv, D]);  lse: the forward's fp32 LSE
     causal, scale, max_seqlen, block_mask: as for ``attn_fwd`` (the same values)
+    block_list: the forward's block list instead of a mask (batch 1, no cu_seqlens):
+        the backward runs on the mask of its set (``block_list_to_mask``)
     dq, dk, dv: optional bf16 outputs shaped like q, k, v
     workspace: optional device buffer of at least ``attn_bwd_workspace_size`` bytes
     """
     import torch
 
     lib = load_library()
+    if block_list is not None:
+        if block_mask is not None:
+            raise ValueError("give a block list or a block mask, not both")
+        if cu_seqlens is not None or q.dim() != 4 or q.shape[0] != 1:
+            raise ValueError("a block list goes with one fixed-length sequence (batch 1, no cu_seqlens)")
+        block_mask = block_list_to_mask(block_list, int(q.shape[1]), stream)
     descs, bm, cu_p, scale, grads = _bwd_prepare(q, k, v, out, dout, lse, cu_seqlens, max_seqlen, block_mask,
                                                  dq, dk, dv, scale)
     need = int(lib.attn_bwd_workspace_size(ctypes.byref(descs[0])))

@@ -1095,7 +1095,42 @@ void *scratch_address() {
   return g_scratch_ptr[dev];
 }
 
+// The mask row of one query block from its block list: cleared, then one
+// bit per listed id in range, in LDS; written out in full.  One workgroup
+// per query block.
+constexpr int kMaxMaskWords = kMaxQBlocks / 32;
+__global__ __launch_bounds__(256) void list_to_mask_kernel(const int32_t *row_ptr, const int32_t *col_idx,
+                                                           int n_kv_blocks, uint32_t *mask, int words) {
+  __shared__ uint32_t row[kMaxMaskWords];
+  const int qb = blockIdx.x;
+  for (int w = threadIdx.x; w < words; w += 256) row[w] = 0u;
+  __syncthreads();
+  const int e0 = row_ptr[qb], e1 = row_ptr[qb + 1];
+  for (int e = e0 + (int)threadIdx.x; e < e1; e += 256) {
+    const int kb = col_idx[e];
+    if (kb >= 0 && kb < n_kv_blocks) atomicOr(&row[kb >> 5], 1u << (kb & 31));
+  }
+  __syncthreads();
+  for (int w = threadIdx.x; w < words; w += 256) mask[(int64_t)qb * words + w] = row[w];
+}
+
 }  // namespace
+
+extern "C" int attn_block_list_to_mask(const attn_block_list_t *list, int n_kv_blocks, uint32_t *mask,
+                                       int mask_words, void *stream) {
+  if (!list || n_kv_blocks < 0 || list->num_q_blocks < 0 || mask_words < 0) return ATTN_ERR_INVALID_ARG;
+  if (list->block_q != kListBlock || list->block_k != kListBlock) return ATTN_ERR_UNSUPPORTED;
+  if (n_kv_blocks > kMaxQBlocks) return ATTN_ERR_UNSUPPORTED;
+  if (mask_words < (n_kv_blocks + 31) / 32 || mask_words > kMaxMaskWords) return ATTN_ERR_INVALID_ARG;
+  if (list->num_q_blocks == 0) return ATTN_OK;
+  if (!list->row_ptr || !list->col_idx || !mask || mask_words == 0) return ATTN_ERR_INVALID_ARG;
+  const int32_t *row_ptr = list->row_ptr, *col_idx = list->col_idx;
+  void *args[] = {&row_ptr, &col_idx, &n_kv_blocks, &mask, &mask_words};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&list_to_mask_kernel),
+                                       dim3((unsigned)list->num_q_blocks), dim3(256), args, 0,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
 
 extern "C" int attn_bwd(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
                         const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,

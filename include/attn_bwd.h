@@ -108,6 +108,35 @@ int attn_bwd_noalloc(const attn_tensor_t *q, const attn_tensor_t *k, const attn_
                      const attn_block_mask_t *mask, attn_tensor_t *dq, attn_tensor_t *dk,
                      attn_tensor_t *dv, void *stream);
 
+/*
+ * attn_block_list_to_mask — the bit-packed block mask of a block list's set,
+ * for the backward of a forward that took the list.  The backward navigates
+ * bit masks (the AdaSplash-2 explainer, section 2); the ordered list of the
+ * CoSA explainer's proxy (attn_fwd.h) is a visiting order over a block set,
+ * and the gradients depend on the set only, so a list's backward is the
+ * backward with the mask of its set.  Row qb of the output has bit kb % 32
+ * of word kb / 32 set exactly when kb is listed for query block qb and
+ * 0 <= kb < n_kv_blocks (ids outside that range are skipped, as the forward
+ * skips them); every other bit of words 0 .. mask_words-1 is cleared.
+ *
+ *   list         device row_ptr [num_q_blocks + 1] (non-decreasing, from
+ *                row_ptr[0] >= 0) and col_idx [row_ptr[num_q_blocks]], block
+ *                sizes 128 (the kernel trusts the contents, which live on the
+ *                device)
+ *   n_kv_blocks  key blocks per row, 0 .. 16384
+ *   mask         device uint32 [num_q_blocks, mask_words], written in full
+ *   mask_words   words per row, ceil(n_kv_blocks / 32) .. 512
+ * The result, as one sequence's mask shared by every KV head, is what
+ * attn_bwd's `mask` takes (num_q_blocks = ceil(S / 128), stride_seq =
+ * stride_head = 0, row_stride = mask_words).
+ * Returns ATTN_OK (nothing is launched for num_q_blocks == 0),
+ * ATTN_ERR_INVALID_ARG for a NULL list, pointer or mask, negative counts or
+ * too few or too many words, ATTN_ERR_UNSUPPORTED for block sizes other than
+ * 128 or more than 16384 key blocks, ATTN_ERR_LAUNCH if the launch fails.
+ */
+int attn_block_list_to_mask(const attn_block_list_t *list, int n_kv_blocks, uint32_t *mask,
+                            int mask_words, void *stream);
+
 /* The argument checks of attn_bwd alone: host code only, no HIP call. */
 int attn_bwd_validate(const attn_tensor_t *q, const attn_tensor_t *k, const attn_tensor_t *v,
                       const attn_tensor_t *out, const attn_tensor_t *dout, const float *lse,

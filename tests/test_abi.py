@@ -26,7 +26,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_noalloc", "attn_bwd_validate",
+    assert declared_functions() == ["attn_block_list_to_mask", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_validate",
                                     "attn_bwd_workspace_size", "attn_entmax_fwd", "attn_entmax_fwd_validate",
                                     "attn_fwd", "attn_fwd_mask", "attn_fwd_mask_validate", "attn_fwd_osk",
                                     "attn_fwd_osk_validate", "attn_fwd_validate", "attn_source_sha",
@@ -281,6 +281,27 @@ def test_entmax_argument_checks():
     s = 128 * 33                                        # 33 blocks need 2 mask words
     assert val(words=1, qd=desc(b=1, s=s, h=4), kd=desc(b=1, s=s, h=2)) == -1
     assert val(words=2, qd=desc(b=1, s=s, h=4), kd=desc(b=1, s=s, h=2)) == 0
+
+
+# ---------------------------------------------------------------------------
+# attn_block_list_to_mask argument checks (host only: every call here fails
+# its checks, or has no query block, before any launch)
+# ---------------------------------------------------------------------------
+def test_block_list_to_mask_argument_checks():
+    lib = attn.load_library()
+
+    def conv(bl, n_kv=4, words=1, mask=FAKE):
+        return lib.attn_block_list_to_mask(ctypes.byref(bl) if bl is not None else None, n_kv, mask, words, None)
+    assert conv(AttnBlockList(FAKE, FAKE, 128, 128, 0)) == 0                    # no query block: nothing to do
+    assert conv(None) == -1
+    assert conv(AttnBlockList(FAKE, FAKE, 128, 128, -1)) == -1
+    assert conv(AttnBlockList(FAKE, FAKE, 128, 128, 3), n_kv=-1) == -1
+    assert conv(AttnBlockList(FAKE, FAKE, 64, 128, 3)) == -2                    # block size
+    assert conv(AttnBlockList(FAKE, FAKE, 128, 128, 3), n_kv=16385, words=513) == -2
+    assert conv(AttnBlockList(FAKE, FAKE, 128, 128, 3), n_kv=33, words=1) == -1  # 33 blocks need 2 words
+    assert conv(AttnBlockList(FAKE, FAKE, 128, 128, 3), n_kv=4, words=513) == -1
+    assert conv(AttnBlockList(None, FAKE, 128, 128, 3)) == -1
+    assert conv(AttnBlockList(FAKE, FAKE, 128, 128, 3), mask=None) == -1
 
 
 # ---------------------------------------------------------------------------

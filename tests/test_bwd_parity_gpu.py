@@ -156,3 +156,60 @@ def test_bwd_full_size_sampled_units(name):
         rows = slice(b * S, (b + 1) * S)
         got = (dq[rows, c * g:(c + 1) * g], dk[rows, c:c + 1], dv[rows, c:c + 1])
         print(f"  unit b={b} kv={c}: {P.compare_grads(got, ref, name)}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# The backward of a forward that took a block list (the mask of the list's set)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed,s", [(60, 700), (61, 128), (62, 129), (63, 1100)])
+def test_block_list_to_mask_matches_host(seed, s):
+    """attn_block_list_to_mask against the host's packing of the list's set (bit-exact):
+    random order, ids above the diagonal and outside the sequence, repeated ids,
+    an empty row."""
+    import torch
+    import attention_forward_flashattention_amd as attn
+    from tests.test_parity_gpu import random_list
+
+    n = (s + 127) // 128
+    row_ptr, col_idx = random_list(seed, n, n, p=0.5, empty_row=1 if n > 1 else None)
+    if len(col_idx):                      # a repeated id in the first row
+        col_idx = np.insert(col_idx, row_ptr[1], col_idx[0]).astype(np.int32)
+        row_ptr = row_ptr.copy()
+        row_ptr[1:] += 1
+    dev = torch.device("cuda:0")
+    bl = (torch.from_numpy(row_ptr).to(dev), torch.from_numpy(col_idx.astype(np.int32)).to(dev))
+    got = attn.block_list_to_mask(bl, s).cpu().numpy().view(np.uint32).reshape(n, -1)
+    want = W.pack_block_mask(W.list_visibility(row_ptr, col_idx, n))
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_bwd_block_list(d):
+    """Forward with a block list, backward with the same list: equal bit for bit to the
+    backward with the mask of the list's set, and within the gradient bounds of the
+    oracle's backward on that set."""
+    import torch
+    import attention_forward_flashattention_amd as attn
+    from tests.test_parity_gpu import random_list
+
+    s = 650
+    w = W.make_dense(f"b_list_d{d}", 64, 1, s, 4, 2, d, True)
+    n = (s + 127) // 128
+    w.row_ptr, w.col_idx = random_list(65, n, n, p=0.5, empty_row=2)
+    print(f"bwd block list d={d}", flush=True)
+    do_bits = W.make_dout(w)
+    q, k, v, _, sp = P.to_device(w)
+    do = P.bf16_tensor(do_bits, q.device)
+    out, lse = attn.attn_fwd(q, k, v, causal=True, scale=w.scale, **sp)
+    g_list = attn.attn_bwd(q, k, v, out, do, lse, causal=True, scale=w.scale, block_list=sp["block_list"])
+    vis = W.list_visibility(w.row_ptr, w.col_idx, n)
+    mask = torch.from_numpy(W.pack_block_mask(vis[None, None]).view(np.int32)).to(q.device)
+    g_mask = attn.attn_bwd(q, k, v, out, do, lse, causal=True, scale=w.scale, block_mask=mask)
+    torch.cuda.synchronize()
+    for a, b in zip(g_list, g_mask):
+        assert torch.equal(a, b)
+    got = tuple(x.float().cpu().numpy().astype(np.float64).reshape(s, x.shape[-2], d) for x in g_list)
+    w.row_ptr = w.col_idx = None
+    w.block_mask = W.pack_block_mask(vis[None, None])
+    ref = P.oracle_bwd(w, do_bits)
+    print(f"  {P.compare_grads(got, ref, w.name)}", flush=True)
