@@ -61,7 +61,7 @@ struct Params {
   int n_tiles;   // query tiles per (sequence, head) = ceil(seqlen / BM)
   int n_units;   // batch * (hq / query heads per workgroup)
   int unit_group;  // units per KV head (group / query heads per workgroup)
-  int group_major; // 1: each XCD takes its groups one after another (see decode_tile)
+  int group_major; // 1: each XCD takes its groups one after another; 2: the chip takes them one after another (see decode_tile)
   int xcd_remap; // 1 when n_units % (8 * unit_group) == 0 (whole GQA groups dealt over the 8 XCDs)
   float c;       // scale * log2(e)
 };
@@ -119,8 +119,17 @@ __device__ __forceinline__ float exp_tile(const floatx16_t (&s)[kKt], float c, f
 // next), so the workgroups in flight on an XCD read the same K/V prefix and it
 // stays in the XCD's L2 (packed D=256: +9%); with few workgroups per CU the
 // tiles go tile by tile over all of the XCD's units, which balances the CUs
-// (dense MHA S=2048: the group order there is 28% slower).  Causal and
-// block-list tiles are issued heaviest first.
+// (dense MHA S=2048: the group order there is 28% slower).  The block-list
+// and block-mask kernels with many workgroups per CU take a third order: the
+// whole chip works on one KV head's group at a time (the group's tiles,
+// heaviest first, dealt round-robin over the XCDs, the units of one query
+// block on one XCD one after the other).  Their listed blocks lie anywhere
+// below the diagonal, so little of them is reused from an XCD's L2; with one
+// KV head in flight the K/V that the chip reads at a time is that head's
+// (64 MB at a 128K context), which the 256 MB Infinity Cache holds, where
+// eight heads in flight (one per XCD) would not fit (128K list and mask
+// workloads: 2-3% faster; ordered skipping keeps the per-XCD order, 1%
+// better there).  Causal and block-list tiles are issued heaviest first.
 __device__ __forceinline__ void decode_tile(const Params &p, bool heavy_first, int &tile,
                                             int &unit) {
   const int w = blockIdx.x;
@@ -129,7 +138,14 @@ __device__ __forceinline__ void decode_tile(const Params &p, bool heavy_first, i
     const int upx = p.n_units >> 3;  // units per XCD
     const int xcd = w & 7;
     const int local = w >> 3;
-    if (p.group_major) {
+    if (p.group_major == 2) {
+      // chip-wide: slot = (group, rank) in order; XCD = slot mod 8
+      const int ug = p.unit_group;
+      const int slot = (local / ug) * 8 + xcd;
+      const int g = slot / p.n_tiles;
+      rank = slot % p.n_tiles;
+      unit = g * ug + local % ug;
+    } else if (p.group_major) {
       // all tiles of one KV head's units (heaviest first), then the next
       const int per_group = p.unit_group * p.n_tiles;
       const int gi = local / per_group;
@@ -1204,6 +1220,7 @@ int launch(Params p, hipStream_t stream) {
   const int64_t n_blocks = (int64_t)p.n_tiles * p.n_units;
   constexpr int64_t kCUs = 256;  // compute units of an MI355X
   p.group_major = n_blocks >= 8 * kCUs ? 1 : 0;  // at least 8 workgroups per CU
+  if ((MODE == kList || MODE == kMask) && p.group_major) p.group_major = 2;
   void *args[] = {&p};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<C, CAUSAL, MODE>),
                                  dim3((unsigned)n_blocks), dim3(C::kThreads), args, 0, stream);
