@@ -367,6 +367,42 @@ def test_block_mask_workload_sampled():
     note(f"  {stats}")
 
 
+def _chip_wide(n_units, unit_group, n_tiles):
+    """Whether a block-list / block-mask launch of the paired kernel takes the chip-wide
+    KV-group order: whole GQA groups dealt over the 8 XCDs and at least 8 workgroups per
+    CU (the launch's own rule, restated for the test's shapes)."""
+    return n_units % (8 * unit_group) == 0 and n_units * n_tiles >= 8 * 256
+
+
+def test_block_list_chip_wide_order_full():
+    """A block list at a size where the workgroups take the chip-wide KV-group order
+    (S = 16384, 32 query heads in pairs over 8 KV heads: 16 units x 128 query blocks);
+    random visiting order, ids out of range, against the oracle on every output."""
+    s, hq, hkv, d = 16384, 32, 8, 64
+    n = s // 128
+    assert _chip_wide(hq // 2, (hq // hkv) // 2, n)
+    note(f"block list, chip-wide order: S={s} hq={hq} hkv={hkv} d={d}")
+    w = W.make_dense("list_chip", 40, 1, s, hq, hkv, d, True)
+    w.row_ptr, w.col_idx = random_list(41, n, n, p=0.08)
+    stats = P.check_workload(w)
+    note(f"  {stats}")
+
+
+def test_block_mask_chip_wide_order_packed_full():
+    """Per-sequence, per-KV-head masks over a packed batch at a size where the workgroups
+    take the chip-wide KV-group order (7 sequences x 16 units x 24 query blocks), an empty
+    and a one-token sequence included, against the oracle on every output."""
+    lengths = [2500, 1, 3000, 0, 700, 1900, 128]
+    hq, hkv, d = 32, 8, 64
+    n_qblk = (max(lengths) + 127) // 128
+    assert _chip_wide(len(lengths) * hq // 2, (hq // hkv) // 2, n_qblk)
+    note(f"block mask, chip-wide order: lengths={lengths} hq={hq} hkv={hkv} d={d}")
+    w = W.make_varlen("mask_chip", 42, lengths, hq, hkv, d, True)
+    w.block_mask = W.pack_block_mask(random_visibility(43, len(lengths), hkv, n_qblk, n_qblk, p=0.3))
+    stats = P.check_workload(w)
+    note(f"  {stats}")
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_late_large_score_raises_running_max(d):
     """A key late in the sequence scores far above every earlier key (P would be
