@@ -100,13 +100,38 @@ __device__ __forceinline__ void lds_write_b32(uint32_t addr, uint32_t v) {
 }
 
 
-template <int kLoads>
-__device__ __forceinline__ void issue_rows(char *l, const uint16_t *g, const int64_t *off,
-                                           const int *lrow, int64_t ss, int rows_left) {
+// Direct global -> LDS loads of one tile's rows: lane load n reads 16 B at byte
+// offset off[n] from the tile's first row t0 (row lrow0 + n * kRowStep of the
+// tile) into the n-th 1 KB of `l`.  The offsets are 32-bit (the row strides
+// accepted keep a tile's rows within 4 GB of its first) and stay so at the load
+// (the empty asm), so each load takes one register offset from a scalar base;
+// rows at or past the end of the sequence (rows_left rows remain from t0)
+// re-read its last row.
+template <int kLoads, int kRowStep, int kTileRows>
+__device__ __forceinline__ void issue_rows(char *l, const char *t0, const uint32_t *off, int lrow0,
+                                           uint32_t ss_bytes, int rows_left) {
+  if (rows_left >= kTileRows) {
 #pragma unroll
-  for (int n = 0; n < kLoads; ++n) {
-    const int64_t back = min(rows_left - 1 - lrow[n], 0);
-    __builtin_amdgcn_global_load_lds(g + off[n] + back * ss, (lds_void_t *)(l + n * 1024), 16, 0, 0);
+    for (int n = 0; n < kLoads; ++n) {
+      uint32_t o = off[n];
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(t0 + o, (lds_void_t *)(l + n * 1024), 16, 0, 0);
+    }
+  } else {
+    // r_last: the sequence's last row relative to t0 (negative for a sub-tile
+    // of a ragged last block that starts past the end; the base then moves
+    // back to it, so that no lane steps back by more than its own row)
+    const int r_last = rows_left - 1;
+    const int base_row = min(r_last, 0);
+    const char *const tb = t0 + (int64_t)base_row * ss_bytes;
+#pragma unroll
+    for (int n = 0; n < kLoads; ++n) {
+      const int lrow = lrow0 + n * kRowStep;
+      const uint32_t back = (uint32_t)(max(lrow - r_last, 0) + base_row);  // 0 <= back <= lrow
+      uint32_t o = off[n] - back * ss_bytes;
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(tb + o, (lds_void_t *)(l + n * 1024), 16, 0, 0);
+    }
   }
 }
 
@@ -172,21 +197,28 @@ __global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void attn_entmax_kernel(En
   const float W = e;  // window width 1/(alpha-1)
 
   // ---- K / V tile loads
-  int64_t koff[kLoads], voff[kLoads];
-  int lrow[kLoads];
+  // (byte offsets of this lane's loads within a tile's rows; row of load n:
+  // lrow0 + n * kRowStep)
+  constexpr int kRowStep = 64 / kChunks;
+  static_assert(64 % kChunks == 0, "a wave-wide load covers whole rows");
+  uint32_t koff[kLoads], voff[kLoads];
   const int slot_byte0 = wave * kLoads * 1024;
+  const int lrow0 = (wave * kLoads * 64 + lane) / kChunks;
+  const uint32_t k_ssb = (uint32_t)p.k_ss * 2u, v_ssb = (uint32_t)p.v_ss * 2u;  // row strides in bytes
 #pragma unroll
   for (int n = 0; n < kLoads; ++n) {
     const int slot = (wave * kLoads + n) * 64 + lane;
     const int r = slot / kChunks, pc = slot % kChunks;
-    lrow[n] = r;
-    koff[n] = (int64_t)r * p.k_ss + (pc ^ L::kswz(r)) * 8;
-    voff[n] = (int64_t)r * p.v_ss + L::v_logical_chunk(r, pc) * 8;
+    koff[n] = (uint32_t)r * k_ssb + (uint32_t)(pc ^ L::kswz(r)) * 16u;
+    voff[n] = (uint32_t)r * v_ssb + (uint32_t)L::v_logical_chunk(r, pc) * 16u;
   }
+  const char *const kgb = reinterpret_cast<const char *>(kg);
+  const char *const vgb = reinterpret_cast<const char *>(vg);
   auto issue = [&](int buf, int kv, bool with_v) {
     char *kb = smem + buf * kBufBytes + slot_byte0;
-    issue_rows<kLoads>(kb, kg + (int64_t)kv * p.k_ss, koff, lrow, p.k_ss, len - kv);
-    if (with_v) issue_rows<kLoads>(kb + kTileBytes, vg + (int64_t)kv * p.v_ss, voff, lrow, p.v_ss, len - kv);
+    issue_rows<kLoads, kRowStep, kBN>(kb, kgb + (int64_t)kv * k_ssb, koff, lrow0, k_ssb, len - kv);
+    if (with_v)
+      issue_rows<kLoads, kRowStep, kBN>(kb + kTileBytes, vgb + (int64_t)kv * v_ssb, voff, lrow0, v_ssb, len - kv);
   };
 
   // ---- Q rows (MFMA B operand), zero past the end
