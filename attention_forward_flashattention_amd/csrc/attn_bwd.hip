@@ -42,6 +42,7 @@ using namespace attn_detail;
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kMaxQBlocks = 16384;  // column bitmap capacity of the dK/dV kernel (mask mode)
+constexpr int64_t kMaxRowStride = int64_t(1) << 24;  // Q / dO row strides, elements (32-bit tile offsets)
 
 struct BwdParams {
   const uint16_t *q, *k, *v, *o, *g;  // g = dO
@@ -112,42 +113,56 @@ __device__ __forceinline__ float dot8(uint4_t a, uint4_t b) {
   return s;
 }
 
-// Direct global -> LDS loads of two 64-row tiles (each wave-wide load fills
-// 64 consecutive 16 B LDS slots; lane n of load i fetches the global chunk at
-// a + aoff[i] / b + boff[i]).  Rows at or beyond rows_left re-read row
-// rows_left - 1.  (A device function rather than a lambda: the LDS pointer
-// casts of the load builtin inside a lambda leave the kernel without its
-// host stub.)
-template <int kLoads>
-__device__ __forceinline__ void issue_pair(char *la, char *lb, const uint16_t *a, const uint16_t *b,
-                                           const int64_t *aoff, const int64_t *boff,
-                                           const int *lrow, int64_t a_ss, int64_t b_ss,
-                                           int rows_left) {
+// Direct global -> LDS loads of two tiles of rows (each wave-wide load fills
+// 64 consecutive 16 B LDS slots; lane load n fetches the 16 B at byte offset
+// aoff[n] / boff[n] from the tiles' first rows a / b, row lrow0 + n * kRowStep
+// of the tile).  The offsets are 32-bit (the row strides accepted keep a
+// tile's rows within 4 GB of its first) and stay so at the load (the empty
+// asm), so each load takes one register offset from a scalar base.  Rows at
+// or beyond rows_left re-read row rows_left - 1; a tile that starts at or
+// past the end (rows_left <= 0) moves its base back to that row, so that no
+// lane steps back by more than its own row.  (A device function rather than
+// a lambda: the LDS pointer casts of the load builtin inside a lambda leave
+// the kernel without its host stub.)
+template <int kLoads, int kRowStep>
+__device__ __forceinline__ void issue_pair(char *la, char *lb, const char *a, const char *b,
+                                           const uint32_t *aoff, const uint32_t *boff, int lrow0,
+                                           uint32_t a_ssb, uint32_t b_ssb, int rows_left) {
+  const int r_last = rows_left - 1;
+  const int base_row = min(r_last, 0);
+  const char *const ta = a + (int64_t)base_row * a_ssb;
+  const char *const tb = b + (int64_t)base_row * b_ssb;
 #pragma unroll
   for (int n = 0; n < kLoads; ++n) {
-    const int64_t back = min(rows_left - 1 - lrow[n], 0);
-    __builtin_amdgcn_global_load_lds(a + aoff[n] + back * a_ss, (lds_void_t *)(la + n * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(b + boff[n] + back * b_ss, (lds_void_t *)(lb + n * 1024), 16, 0, 0);
+    const int lrow = lrow0 + n * kRowStep;
+    const uint32_t back = (uint32_t)(max(lrow - r_last, 0) + base_row);  // 0 <= back <= lrow
+    uint32_t oa = aoff[n] - back * a_ssb, ob = boff[n] - back * b_ssb;
+    asm volatile("" : "+v"(oa), "+v"(ob));
+    __builtin_amdgcn_global_load_lds(ta + oa, (lds_void_t *)(la + n * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(tb + ob, (lds_void_t *)(lb + n * 1024), 16, 0, 0);
   }
 }
 
 // issue_pair for a tile wholly inside the sequence (no row clamping).
 template <int kLoads>
-__device__ __forceinline__ void issue_pair_full(char *la, char *lb, const uint16_t *a,
-                                                const uint16_t *b, const int64_t *aoff,
-                                                const int64_t *boff) {
+__device__ __forceinline__ void issue_pair_full(char *la, char *lb, const char *a, const char *b,
+                                                const uint32_t *aoff, const uint32_t *boff) {
 #pragma unroll
   for (int n = 0; n < kLoads; ++n) {
-    __builtin_amdgcn_global_load_lds(a + aoff[n], (lds_void_t *)(la + n * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(b + boff[n], (lds_void_t *)(lb + n * 1024), 16, 0, 0);
+    uint32_t oa = aoff[n], ob = boff[n];
+    asm volatile("" : "+v"(oa), "+v"(ob));
+    __builtin_amdgcn_global_load_lds(a + oa, (lds_void_t *)(la + n * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(b + ob, (lds_void_t *)(lb + n * 1024), 16, 0, 0);
   }
 }
 
 // Load n of a whole tile's rows (as issue_pair_full does for every n), for
 // callers that spread the loads over other work.
 template <int kN>
-__device__ __forceinline__ void issue_one(char *l, const uint16_t *g, const int64_t *off) {
-  __builtin_amdgcn_global_load_lds(g + off[kN], (lds_void_t *)(l + kN * 1024), 16, 0, 0);
+__device__ __forceinline__ void issue_one(char *l, const char *g, const uint32_t *off) {
+  uint32_t o = off[kN];
+  asm volatile("" : "+v"(o));
+  __builtin_amdgcn_global_load_lds(g + o, (lds_void_t *)(l + kN * 1024), 16, 0, 0);
 }
 
 // One dword per lane from global to 64 consecutive LDS dwords.
@@ -253,21 +268,31 @@ __global__ __launch_bounds__(256, dq_min_blocks<D>()) void attn_bwd_dq_kernel(Bw
   // ---- direct global -> LDS loads of one KV tile (K in the dual layout, V in
   // the row-read layout); rows past the end of the sequence re-read the last
   // row (finite data; those keys are masked)
-  int64_t koff[kLoads], voff[kLoads];
-  int lrow[kLoads];
+  // (byte offsets of this lane's loads within a tile's rows; row of load n:
+  // lrow0 + n * kRowStep)
+  constexpr int kRowStep = 64 / kChunks;
+  static_assert(64 % kChunks == 0, "a wave-wide load covers whole rows");
+  uint32_t koff[kLoads], voff[kLoads];
   const int slot_byte0 = wave * kLoads * 1024;
+  const int lrow0 = (wave * kLoads * 64 + lane) / kChunks;
+  const uint32_t k_ssb = (uint32_t)p.k_ss * 2u, v_ssb = (uint32_t)p.v_ss * 2u;  // row strides in bytes
 #pragma unroll
   for (int n = 0; n < kLoads; ++n) {
     const int slot = (wave * kLoads + n) * 64 + lane;
     const int r = slot / kChunks, pc = slot % kChunks;
-    lrow[n] = r;
-    koff[n] = (int64_t)r * p.k_ss + (pc ^ LK::f(r)) * 8;
-    voff[n] = (int64_t)r * p.v_ss + (pc ^ LV::kswz(r)) * 8;
+    koff[n] = (uint32_t)r * k_ssb + (uint32_t)(pc ^ LK::f(r)) * 16u;
+    voff[n] = (uint32_t)r * v_ssb + (uint32_t)(pc ^ LV::kswz(r)) * 16u;
   }
+  const char *const kgb = reinterpret_cast<const char *>(kg);
+  const char *const vgb = reinterpret_cast<const char *>(vg);
   auto issue = [&](int buf, int kv) {
     char *kb = smem + buf * kBufBytes + slot_byte0;
-    issue_pair<kLoads>(kb, kb + kTileBytes, kg + (int64_t)kv * p.k_ss, vg + (int64_t)kv * p.v_ss,
-                       koff, voff, lrow, p.k_ss, p.v_ss, len - kv);
+    const char *const kt = kgb + (int64_t)kv * k_ssb;
+    const char *const vt = vgb + (int64_t)kv * v_ssb;
+    if (len - kv >= kBN)
+      issue_pair_full<kLoads>(kb, kb + kTileBytes, kt, vt, koff, voff);
+    else
+      issue_pair<kLoads, kRowStep>(kb, kb + kTileBytes, kt, vt, koff, voff, lrow0, k_ssb, v_ssb, len - kv);
   };
 
   int kv_cur = n_iter > 0 ? kv_start(0) : -1;
@@ -593,31 +618,35 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
   // ---- direct global -> LDS loads of one query tile: Q and dO rows (dual
   // layout) and the workspace's lse2 and D of the same rows (waves 0 and 1,
   // one dword per lane); rows past the end re-read the last row
-  int64_t qoff[kLoads], goff[kLoads];
-  int lrow[kLoads];
+  // (byte offsets of this lane's loads within a tile's rows; row of load n:
+  // lrow0 + n * kRowStep)
+  constexpr int kRowStep = 64 / kChunks;
+  static_assert(64 % kChunks == 0, "a wave-wide load covers whole rows");
+  uint32_t qoff[kLoads], goff[kLoads];
   const int slot_byte0 = wave * kLoads * 1024;
+  const int lrow0 = (wave * kLoads * 64 + lane) / kChunks;
+  const uint32_t q_ssb = (uint32_t)p.q_ss * 2u, g_ssb = (uint32_t)p.g_ss * 2u;  // row strides in bytes
 #pragma unroll
   for (int n = 0; n < kLoads; ++n) {
     const int slot = (wave * kLoads + n) * 64 + lane;
     const int r = slot / kChunks, pc = slot % kChunks;
-    lrow[n] = r;
-    qoff[n] = (int64_t)r * p.q_ss + (pc ^ L::f(r)) * 8;
-    goff[n] = (int64_t)r * p.g_ss + (pc ^ L::f(r)) * 8;
+    qoff[n] = (uint32_t)r * q_ssb + (uint32_t)(pc ^ L::f(r)) * 16u;
+    goff[n] = (uint32_t)r * g_ssb + (uint32_t)(pc ^ L::f(r)) * 16u;
   }
   // Loads of the query tile at q0 of `head` into buffer buf: Q and dO rows
   // (unless `rows_deferred`: a whole tile whose rows the caller issues
   // itself, one load at a time) and the lse2 / D values.
   auto issue = [&](int buf, int q0, int head, bool rows_deferred = false) {
     char *bq = smem + buf * kBufBytes;
-    const uint16_t *qt = qbase + (int64_t)head * p.q_sh + (int64_t)q0 * p.q_ss;
-    const uint16_t *gt = gbase + (int64_t)head * p.g_sh + (int64_t)q0 * p.g_ss;
+    const char *qt = reinterpret_cast<const char *>(qbase + (int64_t)head * p.q_sh + (int64_t)q0 * p.q_ss);
+    const char *gt = reinterpret_cast<const char *>(gbase + (int64_t)head * p.g_sh + (int64_t)q0 * p.g_ss);
     const int rows_left = len - q0;
     if (rows_deferred) {
     } else if (rows_left >= kBQ)
       issue_pair_full<kLoads>(bq + slot_byte0, bq + kTileBytes + slot_byte0, qt, gt, qoff, goff);
     else
-      issue_pair<kLoads>(bq + slot_byte0, bq + kTileBytes + slot_byte0, qt, gt, qoff, goff, lrow,
-                         p.q_ss, p.g_ss, rows_left);
+      issue_pair<kLoads, kRowStep>(bq + slot_byte0, bq + kTileBytes + slot_byte0, qt, gt, qoff, goff, lrow0,
+                                   q_ssb, g_ssb, rows_left);
     if (wave < 2) {
       const int row = q0 + min(lane, rows_left - 1);
       const float *src = (wave == 0 ? p.ws_lse2 : p.ws_d) + ws_index(p, b, head, row);
@@ -692,8 +721,10 @@ __global__ __launch_bounds__(256, dkdv_min_blocks<D>()) void attn_bwd_dkdv_kerne
       spread = len - q_nxt >= kBQ;
       issue(1 - buf, q_nxt, head_nxt, spread);
     }
-    const uint16_t *const qt_n = qbase + (int64_t)head_nxt * p.q_sh + (int64_t)q_nxt * p.q_ss;
-    const uint16_t *const gt_n = gbase + (int64_t)head_nxt * p.g_sh + (int64_t)q_nxt * p.g_ss;
+    const char *const qt_n =
+        reinterpret_cast<const char *>(qbase + (int64_t)head_nxt * p.q_sh + (int64_t)q_nxt * p.q_ss);
+    const char *const gt_n =
+        reinterpret_cast<const char *>(gbase + (int64_t)head_nxt * p.g_sh + (int64_t)q_nxt * p.g_ss);
     char *const bq_n = smem + (1 - buf) * kBufBytes + slot_byte0;
     const int q0 = q_cur;
     q_cur = q_nxt;
@@ -940,6 +971,10 @@ int validate_bwd_args(const attn_tensor_t *q, const attn_tensor_t *k, const attn
   st = attn_fwd_validate(q, dk, dv, cu, causal, scale, nullptr, dq);
   if (st != ATTN_OK) return st;
   if (dk->heads != k->heads) return ATTN_ERR_INVALID_ARG;
+  // the dK/dV kernel addresses the rows of a Q or dO tile with 32-bit byte
+  // offsets from the tile's first row, as every kernel does for K and V
+  for (const attn_tensor_t *t : {q, dout})
+    if (t->stride_seq < 0 || t->stride_seq >= kMaxRowStride) return ATTN_ERR_UNSUPPORTED;
   const bool empty = q->batch == 0 || q->seqlen == 0;
   if (empty) return ATTN_OK;
   if (!lse) return ATTN_ERR_INVALID_ARG;

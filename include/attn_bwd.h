@@ -72,8 +72,9 @@ size_t attn_bwd_workspace_size(const attn_tensor_t *q);
  *                         workspace == NULL or workspace_bytes too small for
  *                         a non-empty problem; a bad mask descriptor
  *   ATTN_ERR_UNSUPPORTED  what attn_fwd does not support (head_dim 64, 128
- *                         and 256 are supported); with a mask, more than
- *                         16384 blocks of 128 per sequence
+ *                         and 256 are supported); a q or dout stride_seq
+ *                         outside [0, 2^24) elements (like k and v); with a
+ *                         mask, more than 16384 blocks of 128 per sequence
  *   ATTN_ERR_LAUNCH       a kernel launch failed
  * An empty problem returns ATTN_OK and launches nothing.
  */

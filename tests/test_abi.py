@@ -233,6 +233,19 @@ def test_bwd_head_dims_and_long_masked_sequences():
     assert bwd_validate(desc(b=1, s=s2, h=1), desc(b=1, s=s2, h=1), desc(b=1, s=s2, h=1), mask=m2) == 0
 
 
+def test_bwd_query_row_stride_limit():
+    """The dK/dV kernel addresses a Q or dO tile's rows with 32-bit byte offsets, as every
+    kernel does for K and V: their row strides are limited the same way."""
+    q = desc()
+    q.stride_seq = (1 << 24) - 8  # the largest accepted
+    assert bwd_validate(q, desc(h=2), desc(h=2), out=desc(), dq=desc()) == 0
+    q.stride_seq = 1 << 24
+    assert bwd_validate(q, desc(h=2), desc(h=2), out=desc(), dq=desc()) == -2
+    g = desc()
+    g.stride_seq = 1 << 24
+    assert bwd_validate(desc(), desc(h=2), desc(h=2), dout=g) == -2
+
+
 def test_bwd_empty_problem_needs_no_buffers():
     q, k = desc(b=0), desc(b=0, h=2)
     assert bwd_validate(q, k, desc(b=0, h=2), lse=None, ws=None, ws_bytes=0) == 0
