@@ -356,7 +356,11 @@ __global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void attn_entmax_kernel(En
     // two commutes with rounding); counted when bin >= topf - (kBins - 1).
     // Truncating t8 gives 256 floor(t8 / 256) plus 0..255, so masking it
     // with (kBins - 1) << 8 yields the byte offset of the bin's word (mod
-    // kBins) directly (t8 > 0 in the window; hl has no bits 8..12).
+    // kBins) directly (t8 > 0 in the window; hl has no bits 8..12).  A score
+    // below the window adds 0, so its word may be any of the lane's: the
+    // hardware conversion of any t8 serves (it saturates; -inf, for a masked
+    // score, gives INT_MIN), written as the instruction itself because the
+    // C++ conversion of an out-of-range value is undefined.
     const float lo_t8 = 256.f * (topf - (float)(kBins - 1));
     const float anchor8 = 256.f * anchor;
     const float c_h8 = 256.f * c_h;
@@ -368,8 +372,9 @@ __global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void attn_entmax_kernel(En
         // every lane adds, 0 for a score below the window (at the window's
         // lowest bin): no branch and exec-mask change per score
         const uint32_t inc = t8 >= lo_t8 ? 1u : 0u;
-        const float t8c = fmaxf(t8, lo_t8);
-        lds_add_u32(((uint32_t)(int)t8c & (uint32_t)((kBins - 1) << 8)) | hl, inc);
+        uint32_t t8i;
+        asm("v_cvt_i32_f32 %0, %1" : "=v"(t8i) : "v"(t8));
+        lds_add_u32((t8i & (uint32_t)((kBins - 1) << 8)) | hl, inc);
       }
   });
   const float m = m_raw * p.scale;  // (scale > 0)
