@@ -355,6 +355,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   static_assert(!OSK || kSub >= 2, "ordered skipping needs two or more tiles per list entry");
   int n_iter;
   int e0 = 0, n_ent = 0;
+  // this query block's list entries (col_idx + e0): one pointer kept instead of
+  // the list base and e0, which left the walk reloading spilled SGPRs from
+  // VGPR lanes at every entry (128K list: 2.8% faster)
+  const int32_t *crow = p.col_idx;
   const int n_kvblk = (len + kListBlock - 1) / kListBlock;
   // block mask: this query block's row of the (sequence, kv head) mask; under
   // causal masking only blocks up to the query block count
@@ -368,6 +372,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   if (MODE == kList || MODE == kOsk) {
     e0 = p.row_ptr[tile];
     n_ent = p.row_ptr[tile + 1] - e0;
+    crow = p.col_idx + e0;
     n_iter = n_ent * kSub;
   } else if (MODE == kMask) {
     mrow = p.mask + b * p.mask_ss + kvh * p.mask_sh + (int64_t)tile * p.mask_words;
@@ -402,7 +407,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
       }
       return m_blk * kListBlock + (it % kSub) * kBN;
     }
-    const int cb = ld_uniform(p.col_idx, e0 + it / kSub);
+    const int cb = ld_uniform(crow, it / kSub);
     if (cb < 0 || cb >= n_kvblk) return -1;
     if (CAUSAL && cb * kListBlock > q0 + kRows - 1) return -1;
     return cb * kListBlock + (it % kSub) * kBN;
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
   int w_ent = -1;       // list: current entry
   int w_blk = 0;        // current block
   bool w_ok = true;     // it lies in the sequence
-  int w_raw = (kPipe && (MODE == kList || OSK) && n_ent > 0) ? ld_uniform(p.col_idx, e0) : 0;  // id of entry w_ent + 1
+  int w_raw = (kPipe && (MODE == kList || OSK) && n_ent > 0) ? ld_uniform(crow, 0) : 0;  // id of entry w_ent + 1
   int mw_w = -1;        // mask: word being walked
   uint32_t mw_bits = 0u;  // its set bits not yet visited
   uint32_t mw_pf = (kPipe && MODE == kMask && m_words > 0) ? (ld_uniform(mrow, 0) & m_valid(0)) : 0u;  // word mw_w + 1
@@ -482,7 +487,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void attn_fwd_kernel(Pa
           ++w_ent;
           w_ok = w_raw >= 0 && w_raw < n_kvblk;
           w_blk = w_ok ? w_raw : 0;
-          if (w_ent + 1 < n_ent) w_raw = ld_uniform(p.col_idx, e0 + w_ent + 1);
+          if (w_ent + 1 < n_ent) w_raw = ld_uniform(crow, w_ent + 1);
         } else {
           while (mw_bits == 0u && mw_w + 1 < m_words) {
             ++mw_w;
